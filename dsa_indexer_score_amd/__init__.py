@@ -1,0 +1,174 @@
+"""MI355X-native lightning indexer (DSA / CSA): scores, streaming top-k and
+the adjacent-pair overlap diagnostic, all computed by HIP kernels for gfx950
+behind the C ABI of include/dsa_indexer.h.
+
+This module only marshals arguments: it checks tensor dtypes, shapes and
+devices, allocates outputs and the workspace through PyTorch, and passes raw
+pointers plus the current HIP stream to the library.  Nothing here computes
+any part of the indexer, and there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import IDX_BF16, IDX_EXPAND, IDX_F32, IDX_FP8_E4M3, IDX_TAIL  # noqa: F401
+
+__all__ = ["Indexer", "score_topk", "output_width", "pair_overlap", "overlap_summary",
+           "library_path"]
+
+_DTYPE_CODE = {torch.float32: IDX_F32, torch.bfloat16: IDX_BF16,
+               torch.float8_e4m3fn: IDX_FP8_E4M3}
+
+
+def library_path() -> str:
+    _lib.load()
+    return _lib.LIB_PATH
+
+
+def _flags(expand: bool, tail: bool) -> int:
+    return (IDX_EXPAND if expand else 0) | (IDX_TAIL if tail else 0)
+
+
+def output_width(topk: int, m: int = 1, expand: bool = False, tail: bool = False) -> int:
+    W = ctypes.c_int(0)
+    _lib.check(_lib.load().indexer_output_width(int(topk), int(m), _flags(expand, tail),
+                                                ctypes.byref(W)), "indexer_output_width")
+    return W.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Indexer:
+    """A library handle: element dtype, output mode and query chunk size."""
+
+    def __init__(self, dtype: torch.dtype, *, expand: bool = False, tail: bool = False,
+                 query_chunk: int = 0, device=None):
+        if dtype not in _DTYPE_CODE:
+            raise TypeError(f"unsupported dtype {dtype}")
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        self.dtype, self.expand, self.tail = dtype, bool(expand), bool(tail)
+        self.query_chunk = int(query_chunk or 0)
+        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail), self.query_chunk)
+        h = ctypes.c_void_p()
+        lib = _lib.load()
+        _lib.check(lib.indexer_create(ctypes.byref(cfg), self.device.index or 0, ctypes.byref(h)),
+                   "indexer_create")
+        self._h = h
+        self._lib = lib
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.indexer_destroy(h)
+            self._h = None
+
+    def workspace_bytes(self, S: int, T: int, H: int, d: int, m: int, topk: int) -> int:
+        n = ctypes.c_size_t(0)
+        _lib.check(self._lib.indexer_workspace_bytes(self._h, S, T, H, d, m, topk, ctypes.byref(n)),
+                   "indexer_workspace_bytes")
+        return n.value
+
+    def score_topk(self, q, w, k, *, m: int = 1, topk: int, causal: bool = True,
+                   q_scale=None, k_scale=None, q_pos0: int = 0, with_scores: bool = False,
+                   workspace: Optional[torch.Tensor] = None, out=None):
+        """q [S,H,d], w [S,H] or [H] (fp32), k [T,d] -> (idx [S,W] int32,
+        valid_len [S] int32[, sel_score [S,W] fp32]) on q's device."""
+        if q.dim() != 3 or k.dim() != 2:
+            raise ValueError("q must be [S, H, d] and k [T, d]")
+        S, H, d = q.shape
+        T = k.shape[0]
+        if q.dtype != self.dtype or k.dtype != self.dtype:
+            raise TypeError(f"q and k must be {self.dtype}")
+        if k.shape[1] != d:
+            raise ValueError("q and k disagree on d")
+        for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+            if t is not None and (t.device != self.device or not t.is_contiguous()):
+                raise ValueError(f"{name} must be contiguous on {self.device}")
+        if w.dtype != torch.float32:
+            raise TypeError("w must be float32")
+        if w.dim() == 1 and w.shape[0] == H:
+            w_stride = 0
+        elif w.dim() == 2 and tuple(w.shape) == (S, H):
+            w_stride = H
+        else:
+            raise ValueError("w must be [H] or [S, H]")
+        if self.dtype == torch.float8_e4m3fn:
+            if q_scale is None or k_scale is None:
+                raise ValueError("fp8 needs q_scale [S,H] and k_scale [T]")
+            if tuple(q_scale.shape) != (S, H) or tuple(k_scale.shape) != (T,) or \
+                    q_scale.dtype != torch.float32 or k_scale.dtype != torch.float32:
+                raise ValueError("q_scale must be float32 [S,H], k_scale float32 [T]")
+        W = output_width(topk, m, self.expand, self.tail)
+        if out is None:
+            idx = torch.empty((S, W), dtype=torch.int32, device=self.device)
+            valid_len = torch.empty((S,), dtype=torch.int32, device=self.device)
+            sel = torch.empty((S, W), dtype=torch.float32, device=self.device) \
+                if with_scores else None
+        else:
+            idx, valid_len, sel = out
+        nbytes = self.workspace_bytes(S, T, H, d, m, topk)
+        if workspace is None:
+            workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
+        rc = self._lib.indexer_score_topk(
+            self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
+            d, m, topk, int(bool(causal)), int(q_pos0), _ptr(idx), _ptr(valid_len), _ptr(sel),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(self.device))
+        _lib.check(rc, "indexer_score_topk")
+        return (idx, valid_len, sel) if with_scores else (idx, valid_len)
+
+
+_HANDLES = {}
+
+
+def _handle(dtype, expand, tail, query_chunk, device) -> Indexer:
+    key = (dtype, bool(expand), bool(tail), int(query_chunk or 0), str(device))
+    h = _HANDLES.get(key)
+    if h is None:
+        h = _HANDLES[key] = Indexer(dtype, expand=expand, tail=tail, query_chunk=query_chunk,
+                                    device=device)
+    return h
+
+
+def score_topk(q, w, k, *, m: int = 1, topk: int, causal: bool = True, expand: bool = False,
+               tail: bool = False, q_scale=None, k_scale=None, q_pos0: int = 0,
+               query_chunk: int = 0, with_scores: bool = False, workspace=None):
+    """One indexer step; see Indexer.score_topk."""
+    return _handle(q.dtype, expand, tail, query_chunk, q.device).score_topk(
+        q, w, k, m=m, topk=topk, causal=causal, q_scale=q_scale, k_scale=k_scale,
+        q_pos0=q_pos0, with_scores=with_scores, workspace=workspace)
+
+
+def pair_overlap(idx: torch.Tensor, valid_len: torch.Tensor) -> torch.Tensor:
+    """shared[i] = |row 2i ∩ row 2i+1| (device int32 [S//2])."""
+    if idx.dim() != 2 or idx.dtype != torch.int32 or valid_len.dtype != torch.int32:
+        raise TypeError("idx must be int32 [S, W] and valid_len int32 [S]")
+    if not (idx.is_cuda and idx.is_contiguous() and valid_len.is_cuda):
+        raise ValueError("idx / valid_len must be contiguous device tensors")
+    S, W = idx.shape
+    shared = torch.empty((S // 2,), dtype=torch.int32, device=idx.device)
+    lib = _lib.load()
+    _lib.check(lib.indexer_pair_overlap(_ptr(idx), _ptr(valid_len), S, W, _ptr(shared),
+                                        _stream(idx.device)), "indexer_pair_overlap")
+    return shared
+
+
+def overlap_summary(shared: torch.Tensor, valid_len: torch.Tensor) -> dict:
+    """Page-1 style statistics (host computation over host copies)."""
+    sh = shared.detach().to("cpu", torch.int32).contiguous()
+    vl = valid_len.detach().to("cpu", torch.int32).contiguous()
+    st = _lib.OverlapStats()
+    lib = _lib.load()
+    _lib.check(lib.indexer_overlap_summary(_ptr(sh), _ptr(vl), vl.numel(), ctypes.byref(st)),
+               "indexer_overlap_summary")
+    return {name: getattr(st, name) for name, _ in _lib.OverlapStats._fields_}

@@ -1,0 +1,290 @@
+// Host side of the C ABI declared in include/dsa_indexer.h: argument checks,
+// output-width and workspace arithmetic, the query-chunk loop and launches.
+// Nothing here computes scores or selections; every step of the indexer runs
+// in the HIP kernels (score_select.hip, pair_overlap.hip).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dsa_indexer.h"
+#include "kernels.h"
+
+struct indexer_s {
+    indexer_config cfg;
+    int device;
+};
+
+namespace {
+
+thread_local std::string g_hip_error;
+thread_local std::string g_msg;
+
+int fail_hip(hipError_t e)
+{
+    g_hip_error = hipGetErrorString(e);
+    return IDX_EHIP;
+}
+
+constexpr int64_t kMaxSel = 16000;  // 16-bit histogram counters bound the buffer at 65535
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool dtype_ok(int dt) { return dt == IDX_F32 || dt == IDX_BF16 || dt == IDX_FP8_E4M3; }
+
+bool shape_supported(int dtype, int H, int d)
+{
+    if (H < 1 || H > 64) return false;
+    switch (dtype) {
+    case IDX_F32: return d == 32 || d == 64;
+    case IDX_BF16: return d == 32 || d == 64 || d == 128;
+    case IDX_FP8_E4M3: return d == 32 || d == 64 || d == 128;
+    }
+    return false;
+}
+
+int64_t ksel_of(int topk, int m, int flags) { return (flags & IDX_EXPAND) ? topk / m : topk; }
+
+// Candidate slots per query: room for 4x the selection (so a compaction,
+// which keeps ~Ksel, frees most of the buffer), never more than every
+// visible key plus one tile.
+int64_t capacity(int64_t ksel, int64_t pmax)
+{
+    int64_t cap = round_up(std::max<int64_t>(4 * ksel, ksel + 4 * dsai::kKeysPerTile),
+                           dsai::kKeysPerTile);
+    int64_t all = round_up(std::max<int64_t>(pmax, 0), dsai::kKeysPerTile) + dsai::kKeysPerTile;
+    return std::min(cap, all);
+}
+
+int64_t rows_per_launch(const indexer_config &cfg, int64_t S)
+{
+    return (cfg.query_chunk > 0 && cfg.query_chunk < S) ? cfg.query_chunk : S;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev)
+    {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            changed = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int indexer_create(const indexer_config *cfg, int device, indexer_t *out)
+{
+    if (!cfg || !out || device < 0) return IDX_EINVAL;
+    if (!dtype_ok(cfg->dtype)) return IDX_EINVAL;
+    if (cfg->flags & ~(IDX_EXPAND | IDX_TAIL)) return IDX_EINVAL;
+    if ((cfg->flags & IDX_TAIL) && !(cfg->flags & IDX_EXPAND)) return IDX_EINVAL;
+    if (cfg->query_chunk < 0) return IDX_EINVAL;
+    indexer_s *h = new (std::nothrow) indexer_s;
+    if (!h) return IDX_EINVAL;
+    h->cfg = *cfg;
+    h->device = device;
+    *out = h;
+    return IDX_OK;
+}
+
+int indexer_destroy(indexer_t h)
+{
+    delete h;
+    return IDX_OK;
+}
+
+int indexer_output_width(int topk, int m, int flags, int *W)
+{
+    if (!W || topk < 1 || m < 1 || (flags & ~(IDX_EXPAND | IDX_TAIL))) return IDX_EINVAL;
+    if ((flags & IDX_TAIL) && !(flags & IDX_EXPAND)) return IDX_EINVAL;
+    if ((flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
+    int64_t w = (int64_t)topk + ((flags & IDX_TAIL) ? (m - 1) : 0);
+    if (w > INT32_MAX) return IDX_EINVAL;
+    *W = (int)w;
+    return IDX_OK;
+}
+
+int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int m, int topk,
+                            size_t *bytes)
+{
+    if (!h || !bytes || S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1) return IDX_EINVAL;
+    if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
+    const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
+    if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
+    const int64_t rows = rows_per_launch(h->cfg, S);
+    *bytes = (size_t)(rows * capacity(ksel, T) * (int64_t)sizeof(uint2));
+    return IDX_OK;
+}
+
+int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const float *w,
+                       int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
+                       int64_t T, int H, int d, int m, int topk, int causal, int64_t q_pos0,
+                       int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    if (!h) return IDX_EINVAL;
+    const indexer_config &cfg = h->cfg;
+    const int flags = cfg.flags;
+    const bool expand = flags & IDX_EXPAND, tail = flags & IDX_TAIL;
+    // ---- sizes and modes
+    if (S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1 || q_pos0 < 0) return IDX_EINVAL;
+    if (causal != 0 && causal != 1) return IDX_EINVAL;
+    if (w_stride_s != 0 && w_stride_s < H) return IDX_EINVAL;
+    if (expand && topk % m) return IDX_EINVAL;
+    if (tail && !causal) return IDX_EINVAL;
+    if (tail && T < (q_pos0 + S) / m) return IDX_EINVAL;
+    int W = 0;
+    if (indexer_output_width(topk, m, flags, &W) != IDX_OK) return IDX_EINVAL;
+    if (!shape_supported(cfg.dtype, H, d)) return IDX_EUNSUPPORTED;
+    const int64_t ksel = ksel_of(topk, m, flags);
+    if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
+    if (T >= INT32_MAX || (expand && T * (int64_t)m >= INT32_MAX) ||
+        (tail && q_pos0 + S >= INT32_MAX))
+        return IDX_EUNSUPPORTED;
+    if (S == 0) return IDX_OK;
+    // ---- pointers
+    const bool fp8 = cfg.dtype == IDX_FP8_E4M3;
+    if (!q || !w || !idx || !valid_len) return IDX_EINVAL;
+    if (T > 0 && !k) return IDX_EINVAL;
+    if (fp8 && (!q_scale || (T > 0 && !k_scale))) return IDX_EINVAL;
+    if (!fp8 && (q_scale || k_scale)) return IDX_EINVAL;
+    if (!aligned(q, 16) || (k && !aligned(k, 16)) || !aligned(w, 4)) return IDX_EINVAL;
+    // ---- workspace
+    const int64_t pmax = causal ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
+    const int64_t cap = capacity(ksel, pmax);
+    const int64_t rows = rows_per_launch(cfg, S);
+    const size_t need = (size_t)(rows * cap * (int64_t)sizeof(uint2));
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
+
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return fail_hip(guard.err);
+
+    dsai::ScoreSelectParams p{};
+    p.q = q;
+    p.q_scale = q_scale;
+    p.w = w;
+    p.w_stride = w_stride_s;
+    p.k = k;
+    p.k_scale = k_scale;
+    p.T = T;
+    p.H = H;
+    p.m = m;
+    p.ksel = (int)ksel;
+    p.causal = causal;
+    p.expand = expand;
+    p.tail = tail;
+    p.q_pos0 = q_pos0;
+    p.W = W;
+    p.idx = idx;
+    p.valid_len = valid_len;
+    p.sel_score = sel_score;
+    p.ws = static_cast<uint2 *>(workspace);
+    p.cap = (int)cap;
+    const int nb = (H + 31) / 32;
+    for (int64_t r0 = 0; r0 < S; r0 += rows) {
+        p.row0 = r0;
+        p.nrows = std::min(rows, S - r0);
+        bool supported = true;
+        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, p,
+                                                 static_cast<hipStream_t>(stream), &supported);
+        if (!supported) return IDX_EUNSUPPORTED;
+        if (e != hipSuccess) return fail_hip(e);
+    }
+    return IDX_OK;
+}
+
+int indexer_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,
+                         int32_t *shared, void *stream)
+{
+    if (S < 0 || W < 1) return IDX_EINVAL;
+    const int64_t npairs = S / 2;
+    if (npairs == 0) return IDX_OK;
+    if (!idx || !valid_len || !shared) return IDX_EINVAL;
+    hipError_t e = dsai::launch_pair_overlap(idx, valid_len, npairs, W, shared,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? IDX_OK : fail_hip(e);
+}
+
+int indexer_overlap_summary(const int32_t *shared, const int32_t *valid_len, int64_t S,
+                            indexer_overlap_stats *out)
+{
+    if (!out || S < 0) return IDX_EINVAL;
+    const int64_t npairs = S / 2;
+    if (npairs > 0 && (!shared || !valid_len)) return IDX_EINVAL;
+    std::memset(out, 0, sizeof(*out));
+    std::vector<double> ov;
+    ov.reserve((size_t)npairs);
+    double sum_ov = 0, sum_jac = 0, sum_sh = 0;
+    int64_t ge50 = 0, ge75 = 0, ge80 = 0;
+    for (int64_t i = 0; i < npairs; ++i) {
+        const double va = valid_len[2 * i], vb = valid_len[2 * i + 1], sh = shared[i];
+        if (std::min(va, vb) <= 0) {
+            ++out->excluded;
+            continue;
+        }
+        const double o = sh / std::min(va, vb);
+        ov.push_back(o);
+        sum_ov += o;
+        sum_jac += sh / (va + vb - sh);
+        sum_sh += sh;
+        ge50 += o >= 0.5;
+        ge75 += o >= 0.75;
+        ge80 += o >= 0.8;
+    }
+    const int64_t n = (int64_t)ov.size();
+    out->pairs = n;
+    if (n == 0) return IDX_OK;
+    std::sort(ov.begin(), ov.end());
+    auto quantile = [&](double qq) {
+        const double pos = qq * (double)(n - 1);
+        const int64_t lo = (int64_t)std::floor(pos);
+        const int64_t hi = std::min<int64_t>(lo + 1, n - 1);
+        return ov[lo] + (pos - (double)lo) * (ov[hi] - ov[lo]);
+    };
+    out->mean_overlap = sum_ov / n;
+    out->median_overlap = quantile(0.5);
+    out->p90_overlap = quantile(0.9);
+    out->mean_jaccard = sum_jac / n;
+    out->mean_shared = sum_sh / n;
+    out->frac_ge_50 = (double)ge50 / n;
+    out->frac_ge_75 = (double)ge75 / n;
+    out->frac_ge_80 = (double)ge80 / n;
+    return IDX_OK;
+}
+
+const char *indexer_strerror(int code)
+{
+    const char *base = "unknown status";
+    switch (code) {
+    case IDX_OK: base = "ok"; break;
+    case IDX_EINVAL: base = "invalid argument"; break;
+    case IDX_EUNSUPPORTED: base = "unsupported shape or dtype"; break;
+    case IDX_EWORKSPACE: base = "workspace missing or too small"; break;
+    case IDX_EHIP: base = "HIP error"; break;
+    }
+    if (code == IDX_EHIP && !g_hip_error.empty()) {
+        g_msg = std::string(base) + ": " + g_hip_error;
+        return g_msg.c_str();
+    }
+    return base;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Launch interface between the host C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsai {
+
+// One launch of score_select covers `nrows` consecutive query rows.
+struct ScoreSelectParams {
+    const void *q;          // [S, H, d] codes (row-major)
+    const float *q_scale;   // [S, H] or null
+    const float *w;         // head weights, row t at w + t * w_stride
+    int64_t w_stride;
+    const void *k;          // [T, d] codes
+    const float *k_scale;   // [T] or null
+    int64_t row0;           // first row of this launch (row index within the call)
+    int64_t nrows;          // rows in this launch
+    int64_t T;
+    int H;
+    int m;                  // tokens per key
+    int ksel;               // keys to select per query
+    int causal;
+    int expand;             // 1: key j -> positions j*m .. j*m+m-1
+    int tail;               // 1: append positions P*m .. p
+    int64_t q_pos0;
+    int W;                  // output row width
+    int32_t *idx;           // [S, W]
+    int32_t *valid_len;     // [S]
+    float *sel_score;       // [S, W] or null
+    uint2 *ws;              // candidate buffers, [nrows, cap] of (score bits, key)
+    int cap;                // candidate slots per query
+};
+
+constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
+constexpr int kKeysPerTile = 64;      // keys staged in LDS per step
+
+// dtype codes match enum idx_dtype
+hipError_t launch_score_select(int dtype, int nb, int d, const ScoreSelectParams &p,
+                               hipStream_t stream, bool *supported);
+
+hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t npairs,
+                               int W, int32_t *shared, hipStream_t stream);
+
+}  // namespace dsai

@@ -1,0 +1,573 @@
+// score_select: fused lightning-indexer scoring + streaming top-k for gfx950.
+//
+// Computes, for each query row t and each visible key j,
+//     s_tj = sum_h w[t,h] * ReLU(q[t,h,:] . k[j,:])
+// (DoSA: Dots Sparse Attention, summary page, "Prerequisites": signed-ReLU
+// multi-head indexer) and keeps the exact top-Ksel keys of each row under the
+// total order (higher score, then lower index), without ever writing a score
+// tensor: StreamIndex's point (abstract on the StreamIndex page) that the
+// [S, H, T] or [S, T] intermediate never exists.
+//
+// Work decomposition (one block = 8 consecutive queries, one per wave):
+//  * The block walks the keys visible to its last query in tiles of 64 keys.
+//    Each tile is staged once into LDS (XOR-swizzled 16-B chunks) and read by
+//    all 8 waves, so every key row is fetched from L2 once per 8 queries.
+//  * A wave holds its query's q[t, :, :] in registers as MFMA A operands:
+//    A rows = 32 heads per block (NB blocks cover H <= 32*NB heads; missing
+//    heads are zero rows with zero weight), B columns = 32 keys, the d axis
+//    is the contraction.  bf16: v_mfma_f32_32x32x16_bf16; fp8 (OCP e4m3):
+//    codes widened exactly to bf16 in registers / while staging to LDS, then
+//    the same bf16 MFMA (fp32 accumulation); fp32: v_mfma_f32_32x32x2_f32.  Accumulators hold 16 heads x 1 key per lane;
+//    the signed-ReLU head sum runs in registers (max + fma per element), one
+//    cross-half shuffle finishes it, and each lane ends with the score of one
+//    key of the 64-key tile.
+//  * fp8: per-row scales fold out of the ReLU because it is positively
+//    homogeneous (DoSA summary, "ReLU subadditivity, positive homogeneity"):
+//    w'[t,h] = w[t,h] * q_scale[t,h] multiplies the head sum, k_scale[j]
+//    multiplies the finished score.
+//
+// Streaming selection (per wave, per query; no block barrier involved):
+//  * Scores map to an order-preserving 32-bit code u (-0 folded into +0).
+//  * tau is a running lower bound on the final Ksel-th code: any visible key
+//    subset of size >= Ksel has a Ksel-th score no larger than the full set's
+//    (DoSA summary, "Top-K threshold and subset lower bound").  Keys scan in
+//    ascending index order, so a new key can only enter if u >= tau.
+//  * Survivors are appended, ballot-compacted, to the query's candidate buffer
+//    in global memory (ascending key order is preserved), and counted in a
+//    2048-bin LDS histogram of u's top 11 bits.
+//  * When the buffer could overflow on the next tile, the histogram gives the
+//    bin that holds the Ksel-th code; entries below it are dropped in one
+//    stable in-place pass and tau rises to that bin's edge.  If the bin holds
+//    too many entries (near-ties), two more radix levels (11 + 10 bits) find
+//    the exact Ksel-th code and equal codes are cut by buffer position, which
+//    is key order -- the tie rule.
+//  * After the last tile the same exact selection runs once more and writes
+//    the output row directly: survivors in buffer order are already sorted by
+//    KV index ("Adjacent-Query KV-Index Overlap in 256K DSA Training",
+//    section 3), pools expand to m positions and the incomplete tail follows
+//    (GLM-5.3-Flash Module 06 "DSA & KPool", section 2), then -1 padding.
+#include "kernels.h"
+
+namespace dsai {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = kQueriesPerBlock * 64;
+
+__device__ __forceinline__ uint32_t ord_code(uint32_t bits)
+{
+    if (bits == 0x80000000u) bits = 0;  // -0 -> +0
+    return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_rank(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Wait for this wave's outstanding LDS and global accesses.
+__device__ __forceinline__ void wave_sync_mem()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int64_t visible_keys(int64_t pos, int64_t T, int m, int causal)
+{
+    if (!causal) return T;
+    int64_t c = (pos + 1) / m;
+    return c < T ? c : T;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operand handling.  For every dtype, lane (hh = lane / 32, r = lane % 32)
+// supplies row r of A and column r of B; the contraction slots a lane owns
+// are the contiguous half d in [hh*D/2, hh*D/2 + D/2), split into KS steps.
+// A and B use the same slot -> d map, so the products pair up correctly.
+// ---------------------------------------------------------------------------
+template <int DT, int D> struct Op;
+
+template <int D> struct Op<1, D> {  // bf16
+    using A = bf16x8;
+    static constexpr int ES = 2, KS = D / 16, NCH = D * 2 / 16, GCH = NCH;
+    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
+    {
+        tile[r * NCH + (gch ^ swz)] = v;
+    }
+    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(row + hh * (D / 2) * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = __builtin_bit_cast(A, p[ks]);
+    }
+    __device__ static void load_b(const uint4 *tile, int r, int hh, int swz, A (&b)[KS])
+    {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            b[ks] = __builtin_bit_cast(A, tile[r * NCH + ((hh * KS + ks) ^ swz)]);
+    }
+    __device__ static f32x16 mma(A a, A b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static A zero() { return __builtin_bit_cast(A, make_uint4(0, 0, 0, 0)); }
+};
+
+// OCP e4m3 codes, widened exactly to bf16 (every e4m3 value is a bf16 value)
+// and contracted on the bf16 MFMA with fp32 accumulation.  The native
+// f8f6f4 MFMA is not used: its 64-product dot is accumulated at reduced
+// precision (measured on gfx950: error up to 2^-12 of the sum of |products|
+// on random codes, 2^-15 on normal-like data), against 2^-24 for bf16.
+template <int D> struct Op<2, D> : Op<1, D> {
+    using A = bf16x8;
+    static constexpr int ES = 1, KS = D / 16, NCH = D * 2 / 16, GCH = D / 16;
+    template <bool HI> __device__ static uint32_t widen2(uint32_t w)
+    {
+        auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    // 16 fp8 codes -> two 16-B chunks of 8 bf16
+    __device__ static void widen16(uint4 x, uint4 &lo, uint4 &hi)
+    {
+        lo = make_uint4(widen2<false>(x.x), widen2<true>(x.x), widen2<false>(x.y), widen2<true>(x.y));
+        hi = make_uint4(widen2<false>(x.z), widen2<true>(x.z), widen2<false>(x.w), widen2<true>(x.w));
+    }
+    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(row + hh * (D / 2));
+#pragma unroll
+        for (int c = 0; c < KS / 2; ++c) {
+            uint4 lo, hi;
+            widen16(p[c], lo, hi);
+            a[2 * c] = __builtin_bit_cast(A, lo);
+            a[2 * c + 1] = __builtin_bit_cast(A, hi);
+        }
+    }
+    // global chunk gch of a key row (16 codes) -> LDS chunks 2*gch, 2*gch+1
+    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
+    {
+        uint4 lo, hi;
+        widen16(v, lo, hi);
+        tile[r * NCH + ((2 * gch) ^ swz)] = lo;
+        tile[r * NCH + ((2 * gch + 1) ^ swz)] = hi;
+    }
+};
+
+template <int D> struct Op<0, D> {  // fp32
+    using A = float;
+    static constexpr int ES = 4, KS = D / 2, NCH = D * 4 / 16, GCH = NCH;
+    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
+    {
+        tile[r * NCH + (gch ^ swz)] = v;
+    }
+    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
+    {
+        const float4 *p = reinterpret_cast<const float4 *>(row + hh * (D / 2) * 4);
+#pragma unroll
+        for (int c = 0; c < KS / 4; ++c) {
+            float4 v = p[c];
+            a[4 * c] = v.x; a[4 * c + 1] = v.y; a[4 * c + 2] = v.z; a[4 * c + 3] = v.w;
+        }
+    }
+    __device__ static void load_b(const uint4 *tile, int r, int hh, int swz, A (&b)[KS])
+    {
+#pragma unroll
+        for (int c = 0; c < KS / 4; ++c) {
+            uint4 v = tile[r * NCH + ((hh * (KS / 4) + c) ^ swz)];
+            b[4 * c] = __uint_as_float(v.x); b[4 * c + 1] = __uint_as_float(v.y);
+            b[4 * c + 2] = __uint_as_float(v.z); b[4 * c + 3] = __uint_as_float(v.w);
+        }
+    }
+    __device__ static f32x16 mma(A a, A b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static A zero() { return 0.f; }
+};
+
+// ---------------------------------------------------------------------------
+// Selection helpers (one wave, one query).  `hist` is 1024 dwords of packed
+// 16-bit counters (2048 bins; the 10-bit level uses the first 512 dwords).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void hist_clear(uint32_t *hist, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 1024 / 64; ++i) hist[lane + 64 * i] = 0;
+}
+
+__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin)
+{
+    atomicAdd(&hist[bin >> 1], 1u << ((bin & 1u) * 16));
+}
+
+// Bin b with (count above b) < need <= (count above b) + h[b]; needs total >= need >= 1.
+__device__ void find_boundary(const uint32_t *hist, int nbins, int need, int lane, int &b_out,
+                              int &above_out, int &hb_out)
+{
+    const int per = nbins / 64, dpl = per / 2;
+    uint32_t sum = 0;
+    for (int i = 0; i < dpl; ++i) {
+        uint32_t x = hist[lane * dpl + i];
+        sum += (x & 0xFFFFu) + (x >> 16);
+    }
+    uint32_t suf = sum;  // inclusive suffix sum over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t v = __shfl_down(suf, off);
+        if (lane + off < 64) suf += v;
+    }
+    uint32_t nxt = __shfl_down(suf, 1);
+    if (lane == 63) nxt = 0;
+    const bool mine = suf >= (uint32_t)need && nxt < (uint32_t)need;
+    const uint64_t bm = __ballot(mine);
+    int owner = __ffsll((unsigned long long)bm) - 1;
+    if (owner < 0) owner = 0;  // unreachable while the histogram matches the buffer
+    int b = 0, above = 0, hb = 0;
+    if (lane == owner) {
+        uint32_t acc = nxt;
+        for (int i = per - 1; i >= 0; --i) {
+            uint32_t x = hist[lane * dpl + (i >> 1)];
+            uint32_t h = (i & 1) ? (x >> 16) : (x & 0xFFFFu);
+            if (acc + h >= (uint32_t)need) {
+                b = lane * per + i;
+                above = (int)acc;
+                hb = (int)h;
+                break;
+            }
+            acc += h;
+        }
+    }
+    b_out = __shfl(b, owner);
+    above_out = __shfl(above, owner);
+    hb_out = __shfl(hb, owner);
+}
+
+struct Cut {
+    uint32_t tc;  // keep u >= tc (exact == 0) or u > tc plus the first need_eq of u == tc
+    int exact;
+    int need_eq;
+};
+
+// Choose the cut that keeps at least `need` of the buffer's best entries.
+// With allow_approx, a histogram-bin edge is accepted when it keeps at most
+// `approx_limit` entries; otherwise the cut is exact (keeps exactly `need`).
+__device__ Cut choose_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, bool allow_approx,
+                          int approx_limit, int lane)
+{
+    Cut c;
+    int b1, a1, h1;
+    find_boundary(hist, 2048, need, lane, b1, a1, h1);
+    if ((allow_approx && a1 + h1 <= approx_limit) || a1 + h1 == need) {
+        c.tc = (uint32_t)b1 << 21;
+        c.exact = 0;
+        c.need_eq = 0;
+        return c;
+    }
+    // level 2: bits 20..10 of the entries in bin b1
+    wave_sync_mem();
+    hist_clear(hist, lane);
+    wave_sync_mem();
+    for (int e = lane; e < cnt; e += 64) {
+        uint32_t u = ord_code(buf[e].x);
+        if ((u >> 21) == (uint32_t)b1) hist_add(hist, (u >> 10) & 2047u);
+    }
+    wave_sync_mem();
+    int b2, a2, h2;
+    find_boundary(hist, 2048, need - a1, lane, b2, a2, h2);
+    const int above = a1 + a2;
+    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    if (above + h2 == need) {
+        c.tc = pre << 10;
+        c.exact = 0;
+        c.need_eq = 0;
+        return c;
+    }
+    // level 3: bits 9..0 of the entries sharing the top 22 bits
+    wave_sync_mem();
+    hist_clear(hist, lane);
+    wave_sync_mem();
+    for (int e = lane; e < cnt; e += 64) {
+        uint32_t u = ord_code(buf[e].x);
+        if ((u >> 10) == pre) hist_add(hist, u & 1023u);
+    }
+    wave_sync_mem();
+    int b3, a3, h3;
+    find_boundary(hist, 1024, need - above, lane, b3, a3, h3);
+    c.tc = (pre << 10) | (uint32_t)b3;
+    c.exact = 1;
+    c.need_eq = need - above - a3;
+    return c;
+}
+
+// Stable in-place compaction of buf[0, cnt) under `cut`; rebuilds the histogram.
+__device__ void compact(uint2 *buf, int &cnt, const Cut &cut, uint32_t *hist, int lane)
+{
+    wave_sync_mem();
+    hist_clear(hist, lane);
+    wave_sync_mem();
+    int wcnt = 0, eqseen = 0;
+    for (int base = 0; base < cnt; base += 64) {
+        const int e = base + lane;
+        const bool valid = e < cnt;
+        const uint2 v = valid ? buf[e] : make_uint2(0u, 0u);
+        const uint32_t u = ord_code(v.x);
+        bool keep;
+        if (cut.exact) {
+            const bool eq = valid && u == cut.tc;
+            const uint64_t em = __ballot(eq);
+            keep = valid && (u > cut.tc || (eq && eqseen + lane_rank(em) < cut.need_eq));
+            eqseen += __popcll(em);
+        } else {
+            keep = valid && u >= cut.tc;
+        }
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+            buf[wcnt + lane_rank(km)] = v;
+            hist_add(hist, u >> 21);
+        }
+        wcnt += __popcll(km);
+    }
+    cnt = wcnt;
+    wave_sync_mem();
+}
+
+template <int DT, int NB, int D>
+__global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectParams p)
+{
+    using O = Op<DT, D>;
+    using A = typename O::A;
+    constexpr int KS = O::KS, NCH = O::NCH, GCH = O::GCH, ES = O::ES;
+    constexpr int TILE_CH = kKeysPerTile * NCH;     // LDS 16-B chunks per tile
+    constexpr int GTILE_CH = kKeysPerTile * GCH;    // global 16-B chunks per tile
+    constexpr int CPT = (GTILE_CH + kThreads - 1) / kThreads;
+    constexpr int SWZ = (NCH < 16 ? NCH : 16) - 1;
+    constexpr int64_t ROWB = (int64_t)D * ES;
+
+    __shared__ uint4 ktile[2][TILE_CH];
+    __shared__ float kscale_tile[2][kKeysPerTile];
+    __shared__ uint32_t hist_all[kQueriesPerBlock][1024];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int64_t ngroups = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock;
+    const int64_t grp = ngroups - 1 - (int64_t)blockIdx.x;  // heaviest rows first
+    const int64_t qrow = grp * kQueriesPerBlock + wave;
+    const bool active = qrow < p.nrows;
+    const int64_t t = p.row0 + qrow;
+    const int64_t pos = p.q_pos0 + t;
+    const int64_t Pq = active ? visible_keys(pos, p.T, p.m, p.causal) : 0;
+    int64_t last = grp * kQueriesPerBlock + kQueriesPerBlock - 1;
+    if (last > p.nrows - 1) last = p.nrows - 1;
+    const int64_t Pblk = visible_keys(p.q_pos0 + p.row0 + last, p.T, p.m, p.causal);
+    const int ntiles = (int)((Pblk + kKeysPerTile - 1) / kKeysPerTile);
+
+    uint32_t *hist = hist_all[wave];
+    hist_clear(hist, lane);
+
+    // q fragments and folded head weights of this wave's query
+    A qa[NB][KS];
+    float wv[NB][16];
+    const char *qbytes = static_cast<const char *>(p.q);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int head = 32 * b + l32;
+        if (active && head < p.H) {
+            O::load_a(qbytes + ((t * p.H + head) * (int64_t)D) * ES, hh, qa[b]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[b][ks] = O::zero();
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int h2 = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
+            float wt = 0.f;
+            if (active && h2 < p.H) {
+                wt = p.w[t * p.w_stride + h2];
+                if (DT == 2) wt *= p.q_scale[t * p.H + h2];
+            }
+            wv[b][v] = wt;
+        }
+    }
+
+    uint2 *buf = p.ws + (active ? qrow : 0) * (int64_t)p.cap;
+    int cnt = 0;
+    uint32_t tau = 0;
+    const int approx_limit = (p.cap + p.ksel) / 2;
+
+    const char *kbytes = static_cast<const char *>(p.k);
+    uint4 stage[CPT];
+    float ksc = 0.f;
+    auto load_tile = [&](int it) {
+        const int64_t j0 = (int64_t)it * kKeysPerTile;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int id = threadIdx.x + c * kThreads;
+            stage[c] = make_uint4(0, 0, 0, 0);
+            if (id < GTILE_CH) {
+                const int64_t key = j0 + id / GCH;
+                if (key < p.T)
+                    stage[c] = reinterpret_cast<const uint4 *>(kbytes + key * ROWB)[id % GCH];
+            }
+        }
+        if (DT == 2 && threadIdx.x < kKeysPerTile) {
+            const int64_t key = j0 + threadIdx.x;
+            ksc = key < p.T ? p.k_scale[key] : 0.f;
+        }
+    };
+    auto store_tile = [&](int slot) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int id = threadIdx.x + c * kThreads;
+            if (id < GTILE_CH) {
+                const int r = id / GCH;
+                O::store_chunk(ktile[slot], r, id % GCH, stage[c], r & SWZ);
+            }
+        }
+        if (DT == 2 && threadIdx.x < kKeysPerTile) kscale_tile[slot][threadIdx.x] = ksc;
+    };
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int cur = it & 1;
+        const int64_t j0 = (int64_t)it * kKeysPerTile;
+        if (it + 1 < ntiles) load_tile(it + 1);
+
+        if (active && j0 < Pq) {
+            float part[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int r = cb * 32 + l32;
+                A bfr[KS];
+                O::load_b(ktile[cur], r, hh, r & SWZ, bfr);
+                f32x16 acc[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) acc[b] = O::mma(qa[b][ks], bfr[ks], acc[b]);
+                float s = 0.f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) s = fmaf(wv[b][v], fmaxf(acc[b][v], 0.f), s);
+                part[cb] = s;
+            }
+            // lanes < 32 finish keys 0..31 of the tile, lanes >= 32 keys 32..63
+            const float send = hh ? part[0] : part[1];
+            const float recv = __shfl_xor(send, 32);
+            float s = (hh ? part[1] : part[0]) + recv;
+            if (DT == 2) s *= kscale_tile[cur][lane];
+
+            const int64_t key = j0 + lane;
+            const uint32_t bits = __float_as_uint(s);
+            const uint32_t u = ord_code(bits);
+            const bool pass = key < Pq && u >= tau;
+            const uint64_t mask = __ballot(pass);
+            if (mask) {
+                if (pass) {
+                    buf[cnt + lane_rank(mask)] = make_uint2(bits, (uint32_t)key);
+                    hist_add(hist, u >> 21);
+                }
+                cnt += __popcll(mask);
+                if (cnt > p.cap - kKeysPerTile) {
+                    wave_sync_mem();
+                    const Cut cut = choose_cut(buf, cnt, p.ksel, hist, true, approx_limit, lane);
+                    compact(buf, cnt, cut, hist, lane);
+                    tau = cut.tc + 1;
+                }
+            }
+        }
+        if (it + 1 < ntiles) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    if (!active) return;
+
+    // ---- exact final selection, written straight into the output row ----
+    wave_sync_mem();
+    Cut cut;
+    cut.tc = 0;
+    cut.exact = 0;
+    cut.need_eq = 0;
+    if (cnt > p.ksel) cut = choose_cut(buf, cnt, p.ksel, hist, false, 0, lane);
+    wave_sync_mem();
+
+    const int mexp = p.expand ? p.m : 1;
+    int32_t *orow = p.idx + t * (int64_t)p.W;
+    float *srow = p.sel_score ? p.sel_score + t * (int64_t)p.W : nullptr;
+    int wcnt = 0, eqseen = 0;
+    for (int base = 0; base < cnt; base += 64) {
+        const int e = base + lane;
+        const bool valid = e < cnt;
+        const uint2 v = valid ? buf[e] : make_uint2(0u, 0u);
+        const uint32_t u = ord_code(v.x);
+        bool keep;
+        if (cut.exact) {
+            const bool eq = valid && u == cut.tc;
+            const uint64_t em = __ballot(eq);
+            keep = valid && (u > cut.tc || (eq && eqseen + lane_rank(em) < cut.need_eq));
+            eqseen += __popcll(em);
+        } else {
+            keep = valid && u >= cut.tc;
+        }
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+            const int o = (wcnt + lane_rank(km)) * mexp;
+            for (int x = 0; x < mexp; ++x) {
+                orow[o + x] = (int32_t)(v.y * (uint32_t)mexp + (uint32_t)x);
+                if (srow) srow[o + x] = __uint_as_float(v.x);
+            }
+        }
+        wcnt += __popcll(km);
+    }
+    const int body = wcnt * mexp;
+    const int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - Pq * p.m) : 0;
+    for (int s = body + lane; s < p.W; s += 64) {
+        const bool in_tail = s < body + tl;
+        orow[s] = in_tail ? (int32_t)(Pq * p.m + (s - body)) : -1;
+        if (srow) srow[s] = 0.f;
+    }
+    if (lane == 0) p.valid_len[t] = body + tl;
+}
+
+template <int DT, int NB, int D>
+hipError_t launch_one(const ScoreSelectParams &p, hipStream_t stream)
+{
+    const int64_t blocks = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((score_select_kernel<DT, NB, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_select(int dtype, int nb, int d, const ScoreSelectParams &p,
+                               hipStream_t stream, bool *supported)
+{
+    *supported = true;
+#define DSAI_CASE(DT, NB, D) \
+    if (dtype == DT && nb == NB && d == D) return launch_one<DT, NB, D>(p, stream);
+    DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
+    DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
+    DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)
+    DSAI_CASE(2, 2, 32) DSAI_CASE(2, 2, 64) DSAI_CASE(2, 2, 128)
+    DSAI_CASE(0, 1, 32) DSAI_CASE(0, 1, 64)
+    DSAI_CASE(0, 2, 32) DSAI_CASE(0, 2, 64)
+#undef DSAI_CASE
+    *supported = false;
+    return hipSuccess;
+}
+
+}  // namespace dsai

@@ -1,0 +1,169 @@
+/*
+ * dsa_indexer.h -- C ABI of the MI355X (gfx950) lightning-indexer library.
+ *
+ * The operation (DoSA: Dots Sparse Attention, summary page, "Prerequisites:
+ * DSA and the multi-head indexer"): for every query t and every key j that
+ * t may see,
+ *
+ *     s_tj = sum_{h < H} w[t,h] * ReLU( q[t,h,:] . k[j,:] )
+ *
+ * with signed head weights w; then keep the top-k keys per query under one
+ * total order -- higher score first, equal scores to the lower key index --
+ * and hand them over sorted by KV index ("Adjacent-Query KV-Index Overlap in
+ * 256K DSA Training", section 3: consumers read the canonical top-k indices
+ * sorted by KV index).
+ *
+ * Keys may be tokens (m = 1) or m-token pools / compressed blocks (GLM-5.3-
+ * Flash Module 06 "DSA & KPool"; the CSA abstract on the StreamIndex page).
+ * Causality (Module 06, section 3): the query at absolute position p sees key
+ * j iff (j+1)*m - 1 <= p, i.e. a pool becomes selectable once its last token
+ * is visible.  Expansion and tail (Module 06, section 2): in expand mode each
+ * selected pool becomes its m positions and the incomplete pool at the
+ * query's own position (p+1 mod m positions, at most m-1) is appended as a
+ * visible tail; rows are topk + m - 1 slots wide and padded.
+ *
+ * Memory: every pointer below is a caller-owned buffer.  Pointers documented
+ * as "device" must point to device memory of the device the handle was
+ * created for; "host" pointers to host memory.  The library never allocates
+ * device memory: scratch space comes from the caller's workspace buffer.
+ * Work is enqueued on the caller's HIP stream (hipStream_t passed as void*,
+ * NULL = the default stream); no call synchronises with the host.
+ *
+ * Errors: every entry point returns IDX_OK (0) or a negative IDX_E* code.
+ * Arguments are validated on the host before anything is enqueued, so a
+ * failed validation leaves every output untouched.  A failed launch returns
+ * IDX_EHIP; indexer_strerror() then also reports the HIP error text of the
+ * calling thread's last failure.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct indexer_s *indexer_t;
+
+/* Element type of q and k.  FP8 is OCP e4m3 (e4m3fn: max 448, no inf). */
+enum idx_dtype { IDX_F32 = 0, IDX_BF16 = 1, IDX_FP8_E4M3 = 2 };
+
+/* Output mode flags. */
+enum {
+    IDX_EXPAND = 1, /* selected pools expand to their m token positions   */
+    IDX_TAIL = 2    /* append the incomplete pool (needs EXPAND, causal)  */
+};
+
+enum {
+    IDX_OK = 0,
+    IDX_EINVAL = -1,       /* bad argument (null pointer, size, flag mix) */
+    IDX_EUNSUPPORTED = -2, /* valid but not built (H, d, dtype combination) */
+    IDX_EWORKSPACE = -3,   /* workspace missing or smaller than required  */
+    IDX_EHIP = -4          /* a HIP runtime call or launch failed         */
+};
+
+typedef struct {
+    int dtype;           /* enum idx_dtype                                     */
+    int flags;           /* IDX_EXPAND | IDX_TAIL                              */
+    int64_t query_chunk; /* queries per launch (bounds the workspace); 0 = all */
+} indexer_config;
+
+/* Limits of this build (IDX_EUNSUPPORTED outside them):
+ *   1 <= H <= 64; d in {32, 64} (fp32), {32, 64, 128} (bf16, fp8);
+ *   1 <= topk, selected keys per query (topk, or topk/m in expand mode)
+ *   <= 16000; T < 2^31 keys; output positions < 2^31. */
+
+/* Create a handle.  Host-only: records the configuration and device number;
+ * makes no HIP call.  *out receives the handle (caller frees it with
+ * indexer_destroy).  IDX_EINVAL on a null pointer or unknown dtype/flags. */
+int indexer_create(const indexer_config *cfg, int device, indexer_t *out);
+
+/* Release a handle (NULL is accepted). */
+int indexer_destroy(indexer_t h);
+
+/* Row width of idx / sel_score: topk + (m-1 if IDX_TAIL) -- 2,051 for
+ * topk 2048, m 4 with the tail (Module 06, section 2).  Host-only. */
+int indexer_output_width(int topk, int m, int flags, int *W);
+
+/* Device workspace bytes that indexer_score_topk needs for this problem
+ * with this handle (per-query candidate buffers for one query chunk).
+ * Host-only; depends on min(S, query_chunk), T, m, topk and the flags. */
+int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int m, int topk,
+                            size_t *bytes);
+
+/*
+ * Score every visible key for S queries and write each query's top-k.
+ *
+ *   q          device, [S, H, d] of cfg.dtype, row-major.
+ *   q_scale    device, [S, H] fp32 per-row dequantisation scale (fp8 only;
+ *              must be NULL for f32/bf16).  Dequantised q = code * scale.
+ *   w          device, fp32; row t's head weights are w[t*w_stride_s + h]
+ *              (w_stride_s = H for an [S, H] array, 0 to broadcast one [H]).
+ *   k          device, [T, d] of cfg.dtype, row-major.
+ *   k_scale    device, [T] fp32 (fp8 only, else NULL).
+ *   S, T, H, d sizes (S = 0 or T = 0 are valid).
+ *   m          tokens per key (1 = token keys).
+ *   topk       output units per query: token positions in expand mode (must
+ *              be a multiple of m; topk/m pools are selected), keys otherwise.
+ *   causal     1: row t sits at absolute position p = q_pos0 + t and sees
+ *              key j iff (j+1)*m - 1 <= p; 0: every key is visible.
+ *   q_pos0     absolute position of row 0 (external chunking, decode).
+ *   idx        device, [S, W] int32 out (W from indexer_output_width):
+ *              ascending indices, then -1 padding.  Expand mode: token
+ *              positions (tail positions last); otherwise key indices.
+ *   valid_len  device, [S] int32 out: number of valid entries of each row =
+ *              min(Ksel, P_t) * (m if expand) + tail, P_t visible keys.
+ *   sel_score  device, [S, W] fp32 out or NULL: the fp32 score of the key
+ *              behind each entry; 0 for tail and padding slots.
+ *   workspace  device, >= indexer_workspace_bytes(...) bytes, 16-B aligned;
+ *              contents on entry are ignored, on return undefined.
+ *   stream     hipStream_t (void*), NULL = default stream.
+ *
+ * IDX_TAIL requires IDX_EXPAND, causal = 1 and T >= (q_pos0 + S) / m (every
+ * complete pool present), else IDX_EINVAL.  q and k must be 16-B aligned
+ * (IDX_EINVAL).  Preconditions not checked on
+ * the device: finite inputs, scales > 0, q/k/w/scale buffers as described.
+ * Calls sharing one workspace must be ordered on one stream.
+ */
+int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const float *w,
+                       int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
+                       int64_t T, int H, int d, int m, int topk, int causal, int64_t q_pos0,
+                       int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * Adjacent-pair overlap diagnostic ("Adjacent-Query KV-Index Overlap in
+ * 256K DSA Training", sections 1 and 3): for each non-overlapping pair
+ * (rows 2i, 2i+1), i < S/2, shared[i] = |A_2i ∩ A_2i+1| where A_t is
+ * idx[t, 0:valid_len[t]] (ascending, as indexer_score_topk writes it);
+ * exact intersection by binary search, no all-pairs comparison.
+ *   idx [S, W] int32, valid_len [S] int32: device, in.
+ *   shared [S/2] int32: device, out.  An odd last row is unpaired.
+ */
+int indexer_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,
+                         int32_t *shared, void *stream);
+
+/* Summary of the adjacent-pair statistic over host copies of shared[S/2]
+ * and valid_len[S].  Overlap of a pair = shared / min(vA, vB) (normalised by
+ * the rows' valid top-k lengths); Jaccard = shared / (vA + vB - shared).
+ * Pairs with an empty row are counted in `excluded` and left out.  Median
+ * and P90 interpolate linearly between order statistics.  Host-only. */
+typedef struct {
+    int64_t pairs, excluded;
+    double mean_overlap, median_overlap, p90_overlap, mean_jaccard, mean_shared;
+    double frac_ge_50, frac_ge_75, frac_ge_80;
+} indexer_overlap_stats;
+
+int indexer_overlap_summary(const int32_t *shared, const int32_t *valid_len, int64_t S,
+                            indexer_overlap_stats *out);
+
+/* Static text for a status code, followed (for IDX_EHIP) by the calling
+ * thread's last HIP error.  Never NULL. */
+const char *indexer_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_INDEXER_H */

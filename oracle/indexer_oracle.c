@@ -275,6 +275,45 @@ int oracle_pair_scores(const void *q, const float *q_scale, const float *w, int6
     return 0;
 }
 
+/* Condition sums B(row, key) = sum_h |w_h| * sum_i |q_hi * k_i| of arbitrary
+ * pairs: the standard error bound of evaluating a score in floating point
+ * with unit roundoff u over n sequential operations is gamma_n * B, with
+ * gamma_n = n u / (1 - n u).  Used to derive the fp32 tolerance. */
+int oracle_pair_bounds(const void *q, const float *q_scale, const float *w, int64_t w_stride,
+                       const void *k, const float *k_scale, int dtype, int64_t T, int H, int d,
+                       int64_t n, const int64_t *row, const int64_t *key, double *out,
+                       int nthreads)
+{
+    if (n < 0 || H < 1 || d < 1) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double *Q = (double *)malloc(sizeof(double) * (size_t)H * d);
+        double *Wt = (double *)malloc(sizeof(double) * (size_t)H);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t e = 0; e < n; ++e) {
+            int64_t j = key[e];
+            if (!Q || !Wt || j < 0 || j >= T) { out[e] = NAN; continue; }
+            dequant_query(q, q_scale, w, w_stride, dtype, row[e], H, d, Q, Wt);
+            double sc = k_scale ? (double)k_scale[j] : 1.0, b = 0.0;
+            for (int h = 0; h < H; ++h) {
+                double a = 0.0;
+                for (int i = 0; i < d; ++i)
+                    a += fabs(Q[h * d + i] * elem(k, dtype, j * d + i) * sc);
+                b += fabs(Wt[h]) * a;
+            }
+            out[e] = b;
+        }
+        free(Q);
+        free(Wt);
+    }
+    return 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

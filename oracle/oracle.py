@@ -58,6 +58,8 @@ def _load():
         lib.oracle_pair_scores.restype = I32
         lib.oracle_pair_scores.argtypes = [P, P, P, I64, P, P, I32, I64, I32, I32, I64, P, P,
                                            P, I32]
+        lib.oracle_pair_bounds.restype = I32
+        lib.oracle_pair_bounds.argtypes = lib.oracle_pair_scores.argtypes
         lib.oracle_decode_bf16.restype = D
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_e4m3.restype = D
@@ -170,8 +172,9 @@ def select_rows(inp, rows, nthreads: int = 0):
     return out
 
 
-def pair_scores(inp, rows, keys, nthreads: int = 0):
-    """fp64 scores s*(rows[e], keys[e]) (rows index inp.q; keys index inp.k)."""
+def pair_scores(inp, rows, keys, nthreads: int = 0, bounds: bool = False):
+    """fp64 scores s*(rows[e], keys[e]) (rows index inp.q; keys index inp.k).
+    With bounds=True, the condition sums sum_h |w_h| sum_i |q_hi k_i| instead."""
     lib = _load()
     rows = np.asarray(rows, dtype=np.int64)
     keys = np.ascontiguousarray(np.asarray(keys, dtype=np.int64))
@@ -181,7 +184,8 @@ def pair_scores(inp, rows, keys, nthreads: int = 0):
     ks = None if inp.k_scale is None else _host(inp.k_scale).astype(np.float32)
     out = np.empty(rows.shape[0], np.float64)
     inv = np.ascontiguousarray(inv.astype(np.int64))
-    rc = lib.oracle_pair_scores(_ptr(q), _ptr(qs), _ptr(w), wst, _ptr(k), _ptr(ks),
+    fn = lib.oracle_pair_bounds if bounds else lib.oracle_pair_scores
+    rc = fn(_ptr(q), _ptr(qs), _ptr(w), wst, _ptr(k), _ptr(ks),
                                 DTYPE_CODE[inp.dtype], inp.T, inp.H, inp.d, rows.shape[0],
                                 _ptr(inv), _ptr(keys), _ptr(out), int(nthreads))
     if rc != 0:

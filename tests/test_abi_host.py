@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dsa_indexer.h declares, and its host-side arithmetic and argument
+validation behave as documented (nothing here reaches a device call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dsa_indexer_score_amd import _lib
+from oracle import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*\**\s*(indexer_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.load()._name)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_output_width_matches_oracle_arithmetic():
+    lib = _lib.load()
+    W = ctypes.c_int()
+    for topk in (1, 4, 64, 512, 2048, 4096):
+        for m in (1, 2, 4, 8):
+            for flags in (0, _lib.IDX_EXPAND, _lib.IDX_EXPAND | _lib.IDX_TAIL):
+                rc = lib.indexer_output_width(topk, m, flags, ctypes.byref(W))
+                if (flags & _lib.IDX_EXPAND) and topk % m:
+                    assert rc == _lib.IDX_EINVAL
+                    continue
+                assert rc == 0
+                assert W.value == orc.output_width(topk, m, bool(flags & 1), bool(flags & 2))
+    assert lib.indexer_output_width(2048, 4, 3, ctypes.byref(W)) == 0 and W.value == 2051
+    assert lib.indexer_output_width(8, 4, _lib.IDX_TAIL, ctypes.byref(W)) == _lib.IDX_EINVAL
+    assert lib.indexer_output_width(0, 4, 0, ctypes.byref(W)) == _lib.IDX_EINVAL
+
+
+def _handle(dtype=_lib.IDX_BF16, flags=0, chunk=0):
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    cfg = _lib.IndexerConfig(dtype, flags, chunk)
+    assert lib.indexer_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == 0
+    return lib, h
+
+
+def test_create_rejects_bad_configs():
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    for dtype, flags, chunk, dev in ((7, 0, 0, 0), (1, 4, 0, 0), (1, _lib.IDX_TAIL, 0, 0),
+                                     (1, 0, -1, 0), (1, 0, 0, -1)):
+        cfg = _lib.IndexerConfig(dtype, flags, chunk)
+        assert lib.indexer_create(ctypes.byref(cfg), dev, ctypes.byref(h)) == _lib.IDX_EINVAL
+    assert lib.indexer_create(None, 0, ctypes.byref(h)) == _lib.IDX_EINVAL
+    assert lib.indexer_destroy(None) == 0
+
+
+def test_workspace_bytes_scale_with_chunk_and_selection():
+    lib, h = _handle(chunk=16384)
+    n = ctypes.c_size_t()
+    assert lib.indexer_workspace_bytes(h, 262144, 65536, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 16384 * 8192 * 8          # 4 x 2048 candidate slots of 8 bytes per query
+    assert lib.indexer_workspace_bytes(h, 100, 65536, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 100 * 8192 * 8            # chunk clipped to S
+    assert lib.indexer_workspace_bytes(h, 100, 100, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 100 * 192 * 8             # never more than all keys plus one tile
+    assert lib.indexer_workspace_bytes(h, 100, 10 ** 6, 64, 128, 1, 20000,
+                                       ctypes.byref(n)) == _lib.IDX_EUNSUPPORTED
+    lib.indexer_destroy(h)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def _call(lib, h, **kw):
+    a = dict(q=FAKE, q_scale=None, w=FAKE, w_stride=0, k=FAKE, k_scale=None, S=16, T=16, H=64,
+             d=128, m=1, topk=4, causal=1, q_pos0=0, idx=FAKE, vl=FAKE, sel=None, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.indexer_score_topk(h, a["q"], a["q_scale"], a["w"], a["w_stride"], a["k"],
+                                  a["k_scale"], a["S"], a["T"], a["H"], a["d"], a["m"], a["topk"],
+                                  a["causal"], a["q_pos0"], a["idx"], a["vl"], a["sel"], a["ws"],
+                                  a["ws_bytes"], a["stream"])
+
+
+def test_score_topk_validation_paths():
+    lib, h = _handle()
+    E, U, WS = _lib.IDX_EINVAL, _lib.IDX_EUNSUPPORTED, _lib.IDX_EWORKSPACE
+    assert _call(lib, h, S=0) == 0                        # empty problem: nothing to do
+    assert _call(lib, h, topk=0) == E
+    assert _call(lib, h, m=0) == E
+    assert _call(lib, h, causal=2) == E
+    assert _call(lib, h, S=-1) == E
+    assert _call(lib, h, q_pos0=-1) == E
+    assert _call(lib, h, w_stride=3) == E                 # rows of w would overlap
+    assert _call(lib, h, q=None) == E
+    assert _call(lib, h, idx=None) == E
+    assert _call(lib, h, q_scale=FAKE) == E              # scales only for fp8
+    assert _call(lib, h, q=ctypes.c_void_p(0x10008)) == E  # misaligned q
+    assert _call(lib, h, H=65) == U
+    assert _call(lib, h, d=96) == U
+    assert _call(lib, h, topk=16001) == U
+    assert _call(lib, h, ws=None) == WS
+    assert _call(lib, h, ws_bytes=64) == WS
+    assert _call(lib, None) == E
+    lib.indexer_destroy(h)
+    lib, h = _handle(dtype=_lib.IDX_FP8_E4M3)
+    assert _call(lib, h) == E                             # fp8 needs scales
+    assert _call(lib, h, q_scale=FAKE, k_scale=FAKE, d=96) == U
+    lib.indexer_destroy(h)
+    lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL)
+    assert _call(lib, h, m=4, topk=6) == E               # topk not a multiple of m
+    assert _call(lib, h, m=4, topk=8, causal=0) == E      # tail needs causal
+    assert _call(lib, h, m=4, topk=8, S=64, T=15) == E    # tail needs every complete pool
+    lib.indexer_destroy(h)
+
+
+def test_pair_overlap_host_paths():
+    lib = _lib.load()
+    assert lib.indexer_pair_overlap(None, None, 1, 4, None, None) == 0   # no pair
+    assert lib.indexer_pair_overlap(None, None, 4, 4, None, None) == _lib.IDX_EINVAL
+    assert lib.indexer_pair_overlap(FAKE, FAKE, 4, 0, FAKE, None) == _lib.IDX_EINVAL
+
+
+def test_overlap_summary_matches_oracle_statistics():
+    rng = np.random.default_rng(11)
+    lib = _lib.load()
+    for S in (2, 7, 1000):
+        vl = rng.integers(0, 60, S).astype(np.int32)
+        npairs = S // 2
+        sh = np.array([rng.integers(0, min(vl[2 * i], vl[2 * i + 1]) + 1) for i in range(npairs)],
+                      np.int32)
+        st = _lib.OverlapStats()
+        assert lib.indexer_overlap_summary(sh.ctypes.data_as(ctypes.c_void_p),
+                                           vl.ctypes.data_as(ctypes.c_void_p), S,
+                                           ctypes.byref(st)) == 0
+        want = orc.overlap_stats(sh, vl)
+        assert st.pairs == want["pairs"] and st.excluded == want["excluded"]
+        if want["pairs"]:
+            for key in ("mean_overlap", "median_overlap", "p90_overlap", "mean_jaccard",
+                        "mean_shared", "frac_ge_50", "frac_ge_75", "frac_ge_80"):
+                assert getattr(st, key) == pytest.approx(want[key], rel=1e-12, abs=1e-12), key
+
+
+def test_strerror_is_never_null():
+    lib = _lib.load()
+    for code in (0, -1, -2, -3, -4, -99):
+        assert lib.indexer_strerror(code)

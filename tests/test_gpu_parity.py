@@ -1,0 +1,290 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Integer-exact problems must match bit for bit; float problems follow the
+tolerance rule in oracle/check.py.  Scaled-down problems are compared on
+every row (several key tiles, compactions and a ragged last tile); the five
+full-size workloads run in the launch configuration the benchmark times and
+are compared on sampled rows, with the all-row invariants checked on the
+device.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import device_invariants, log, rows_to_host, run
+from oracle import check
+from oracle import oracle as orc
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _compare_all(inp, out, exact=None):
+    idx, vl, sc = out
+    rows = np.arange(inp.S)
+    rep = check.compare(inp, rows, idx.cpu().numpy(), vl.cpu().numpy(),
+                        None if sc is None else sc.cpu().numpy(), exact=exact)
+    assert rep["ok"], rep["failures"]
+    return rep
+
+
+def test_c1_integer_exact_all_rows():
+    inp = gen.generate("c1_tiny_int").to(DEV)
+    log(f"c1 full S={inp.S}")
+    out = run(inp)
+    rep = _compare_all(inp, out, exact=True)
+    assert rep["exact"]
+    device_invariants(inp, out[0], out[1])
+
+
+SCALED = [
+    ("c1_tiny_int", 3001, 64),     # ragged: S, T not multiples of the tile sizes
+    ("c2_glm_pooled", 4096, 512),  # 128 pools of 1024 visible: compactions + tail
+    ("c2_glm_pooled", 1000, 64),
+    ("c3_dsa_token", 4096, 256),   # fp8 with scales, AR(1) queries
+    ("c4_csa_256k", 8192, 256),    # bf16 compressed keys
+    ("c5_csa_1m", 6000, 128),      # fp8 compressed keys, ragged
+]
+
+
+@pytest.mark.parametrize("name,S,topk", SCALED)
+def test_scaled_configs_all_rows(name, S, topk):
+    inp = gen.generate(name, S=S, topk=topk).to(DEV)
+    log(f"{name} S={S} T={inp.T} topk={topk}")
+    out = run(inp, query_chunk=0)
+    rep = _compare_all(inp, out)
+    log(f"  index-mismatch rows {rep['index_mismatch_rows']}, max score rel err "
+        f"{rep['max_score_rel_err']:.2e}")
+    device_invariants(inp, out[0], out[1])
+
+
+FULL = ["c2_glm_pooled", "c3_dsa_token", "c4_csa_256k", "c5_csa_1m"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    inp = gen.generate(name, device=DEV)
+    log(f"{name} full S={inp.S} T={inp.T} H={inp.H} d={inp.d} dtype={inp.dtype} "
+        f"chunk={inp.query_chunk}")
+    idx, vl, sc = run(inp)
+    device_invariants(inp, idx, vl)
+    ksel = inp.topk // inp.m if inp.expand else inp.topk
+    n_uniform = 96 if inp.S >= 1 << 20 else 160
+    rows = check.sample_rows(inp.S, m=inp.m, ksel=ksel, chunk=inp.query_chunk, seed=inp.seed,
+                             n_uniform=n_uniform)
+    hi, hv, hs = rows_to_host(rows, idx, vl, sc)
+    rep = check.compare(inp, rows, hi, hv, hs)
+    log(f"  rows {rep['rows']}, index-mismatch rows {rep['index_mismatch_rows']}, "
+        f"max score rel err {rep['max_score_rel_err']:.2e}")
+    assert rep["ok"], rep["failures"]
+
+
+# ---------------------------------------------------------------- edge cases
+def _exact_rows(inp, out):
+    ref = orc.select_rows(inp, np.arange(inp.S))
+    assert np.array_equal(out[1].cpu().numpy(), ref["valid_len"])
+    assert np.array_equal(out[0].cpu().numpy(), ref["idx"])
+    return ref
+
+
+def test_worked_examples_on_gpu():
+    # WE1 / WE2: signed weights, an all-ReLU-zero key, and the tie rule (d padded to 32)
+    q = torch.zeros(5, 2, 32)
+    q[:, 0, 0] = 1
+    q[:, 1, 1] = 1
+    k = torch.zeros(5, 32)
+    k[:, :2] = torch.tensor([[2., 1.], [1., 3.], [-1., -1.], [3., -2.], [1., 1.]])
+    w = torch.tensor([1.0, -1.0])
+    for topk in (2, 3):
+        inp = gen.custom(q=q, k=k, w=w, topk=topk).to(DEV)
+        out = run(inp)
+        _exact_rows(inp, out)
+    assert out[0][4].tolist() == [0, 2, 3]
+    # WE4: pool [4..7] is never visible to query 5
+    q = torch.ones(9, 1, 32)
+    k = torch.zeros(2, 32)
+    k[0, 0], k[1, 0] = 1.0, 2.0
+    inp = gen.custom(q=q, k=k, w=torch.ones(1), m=4, topk=4, expand=True, tail=True).to(DEV)
+    out = run(inp)
+    _exact_rows(inp, out)
+    assert out[0][5].tolist() == [0, 1, 2, 3, 4, 5, -1]
+    assert out[0][7].tolist() == [4, 5, 6, 7, -1, -1, -1]
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 7, 8, 9, 63, 64, 65])
+def test_watch_lengths_pooled_tail(S):
+    inp = gen.generate("c2_glm_pooled", S=max(S, 4), topk=8)
+    inp = gen.custom(q=inp.q[:S], k=inp.k[:max(1, S // 4)], w=inp.w, m=4, topk=8, expand=True,
+                     tail=True).to(DEV)
+    out = run(inp)
+    _compare_all(inp, out)
+    device_invariants(inp, out[0], out[1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_all_scores_tie(dtype):
+    """q = 0: every score is 0; the tie rule keeps the lowest indices, through
+    many compactions whose cut falls inside one run of equal codes."""
+    S = T = 3000
+    H, d = 64, 64
+    g = torch.Generator().manual_seed(5)
+    k = torch.randn(T, d, generator=g)
+    q = torch.zeros(S, H, d)
+    w = torch.randn(H, generator=g)
+    q_scale = k_scale = None
+    if dtype == "bf16":
+        q, k = q.bfloat16(), k.bfloat16()
+    elif dtype == "fp8":
+        q, q_scale = gen.quant_e4m3_rows(q)
+        k, k_scale = gen.quant_e4m3_rows(k)
+    inp = gen.custom(q=q, k=k, w=w, topk=100, q_scale=q_scale, k_scale=k_scale).to(DEV)
+    idx, vl, sc = run(inp)
+    want = np.full((S, 100), -1, np.int32)
+    for t in range(S):
+        n = min(100, t + 1)
+        want[t, :n] = np.arange(n)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert bool((sc == 0).all())
+
+
+def test_all_relu_zero_rows():
+    """Every q.k negative: every ReLU is 0, every score 0."""
+    S = T = 700
+    q = -torch.ones(S, 4, 32)
+    k = torch.rand(T, 32, generator=torch.Generator().manual_seed(2)) + 0.1
+    inp = gen.custom(q=q, k=k, w=torch.tensor([1.0, -0.5, 2.0, -1.0]), topk=50).to(DEV)
+    out = run(inp)
+    _exact_rows(inp, out)
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_monotone_scores(order):
+    """Ascending scores make every key beat the running threshold (maximal
+    compaction work); descending ones make the threshold reject everything
+    after the first fill."""
+    S = T = 5000
+    q = torch.zeros(S, 1, 32)
+    q[:, 0, 0] = 1.0
+    k = torch.zeros(T, 32)
+    k[:, 0] = torch.arange(T, dtype=torch.float32) * (1 if order == "ascending" else -1)
+    inp = gen.custom(q=q, k=k, w=torch.ones(1), topk=300).to(DEV)
+    out = run(inp)
+    ref = _exact_rows(inp, out)
+    t = S - 1
+    want = np.arange(T - 300, T) if order == "ascending" else np.arange(300)
+    assert np.array_equal(ref["idx"][t], want)
+
+
+def test_topk_larger_than_visible_and_topk_one():
+    base = gen.generate("c4_csa_256k", S=2048).to(DEV)
+    for topk in (1, 4096):
+        inp = gen.custom(q=base.q, k=base.k, w=base.w, m=4, topk=topk).to(DEV)
+        out = run(inp)
+        _compare_all(inp, out)
+        device_invariants(inp, out[0], out[1])
+
+
+def test_non_causal_and_ragged():
+    base = gen.generate("c4_csa_256k", S=1001, T=777, topk=100)
+    inp = gen.custom(q=base.q, k=base.k, w=base.w, m=4, topk=100, causal=False).to(DEV)
+    out = run(inp)
+    _compare_all(inp, out)
+    assert bool((out[1] == 100).all())
+
+
+def test_empty_inputs():
+    base = gen.generate("c4_csa_256k", S=64).to(DEV)
+    inp = gen.custom(q=base.q[:0], k=base.k, w=base.w, m=4, topk=16).to(DEV)
+    idx, vl, _ = run(inp)
+    assert idx.shape == (0, 16) and vl.shape == (0,)
+    inp = gen.custom(q=base.q, k=base.k[:0], w=base.w, m=4, topk=16).to(DEV)
+    idx, vl, _ = run(inp)
+    assert bool((vl == 0).all()) and bool((idx == -1).all())
+    # tail only: no complete pool for the first three positions
+    inp = gen.custom(q=base.q[:3], k=base.k[:0], w=base.w, m=4, topk=16, expand=True,
+                     tail=True).to(DEV)
+    idx, vl, _ = run(inp)
+    assert vl.tolist() == [1, 2, 3]
+    assert idx[2, :4].tolist() == [0, 1, 2, -1]
+
+
+@pytest.mark.parametrize("dtype,H,d", [("bf16", 4, 64), ("bf16", 16, 128), ("bf16", 33, 32),
+                                       ("bf16", 64, 64), ("fp8", 32, 64), ("fp8", 48, 128),
+                                       ("f32", 48, 64), ("f32", 64, 32)])
+def test_head_and_dim_variants(dtype, H, d):
+    S, T = 1500, 1500
+    g = torch.Generator().manual_seed(H * 1000 + d)
+    q = torch.randn(S, H, d, generator=g) / d ** 0.5
+    k = torch.randn(T, d, generator=g) / d ** 0.5
+    w = torch.randn(S, H, generator=g)                # per-row weights
+    q_scale = k_scale = None
+    if dtype == "bf16":
+        q, k = q.bfloat16(), k.bfloat16()
+    elif dtype == "fp8":
+        q, q_scale = gen.quant_e4m3_rows(q)
+        k, k_scale = gen.quant_e4m3_rows(k)
+    inp = gen.custom(q=q, k=k, w=w, topk=96, q_scale=q_scale, k_scale=k_scale).to(DEV)
+    out = run(inp)
+    _compare_all(inp, out)
+
+
+def test_chunking_q_pos0_and_determinism_are_bit_identical():
+    inp = gen.generate("c4_csa_256k", S=12000, topk=256).to(DEV)
+    ref = run(inp, query_chunk=0)
+    for chunk in (1000, 4096, 7777):
+        out = run(inp, query_chunk=chunk)
+        for a, b in zip(ref, out):
+            assert torch.equal(a, b), f"chunk {chunk}"
+    again = run(inp, query_chunk=0)
+    for a, b in zip(ref, again):
+        assert torch.equal(a, b)
+    # external chunking: rows [a, S) called alone at q_pos0 = a
+    a = 5000
+    sub = gen.custom(q=inp.q[a:], k=inp.k, w=inp.w, m=4, topk=256, q_pos0=a)
+    out = run(sub, query_chunk=0)
+    for x, y in zip(ref, out):
+        assert torch.equal(x[a:], y)
+
+
+def test_pair_overlap_matches_oracle():
+    inp = gen.generate("c3_dsa_token", S=6001, topk=256).to(DEV)
+    import dsa_indexer_score_amd as dsai
+    idx, vl, _ = run(inp)
+    shared = dsai.pair_overlap(idx, vl)
+    torch.cuda.synchronize()
+    hi, hv = idx.cpu().numpy(), vl.cpu().numpy()
+    want = orc.pair_overlap(hi, hv)
+    assert np.array_equal(shared.cpu().numpy(), want)
+    st = dsai.overlap_summary(shared, vl)
+    ref = orc.overlap_stats(want, hv)
+    assert st["pairs"] == ref["pairs"]
+    assert st["mean_overlap"] == pytest.approx(ref["mean_overlap"], rel=1e-12)
+    assert st["p90_overlap"] == pytest.approx(ref["p90_overlap"], rel=1e-12)
+    log(f"  AR(1) fp8 adjacent-pair overlap: mean {st['mean_overlap']:.3f}, "
+        f"median {st['median_overlap']:.3f}")
+    # causal prefix pairs (rows 2i, 2i+1 with t < topk) overlap completely
+    assert (want[:100] == hv[0:200:2]).all()
+
+
+def test_fp8_every_code_is_widened_exactly():
+    """Each of the 254 finite e4m3 codes, read through the kernel's widening
+    and contraction, reproduces the oracle's hand-decoded value exactly:
+    with heads (q, -q), weights (+1, -1) and one-hot keys, score_j = q_j."""
+    codes = torch.arange(256, dtype=torch.int32)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    codes = codes.to(torch.uint8)
+    q8 = torch.zeros(2, 2, 128, dtype=torch.uint8)
+    for t in range(2):
+        q8[t, 0] = codes[128 * t:128 * (t + 1)]
+        q8[t, 1] = codes[128 * t:128 * (t + 1)] ^ 0x80
+    k8 = torch.zeros(128, 128, dtype=torch.uint8)
+    k8[torch.arange(128), torch.arange(128)] = 0x38          # 1.0
+    inp = gen.custom(q=q8.view(torch.float8_e4m3fn), k=k8.view(torch.float8_e4m3fn),
+                     w=torch.tensor([1.0, -1.0]), topk=128, causal=False,
+                     q_scale=torch.ones(2, 2), k_scale=torch.ones(128)).to(DEV)
+    out = run(inp)
+    rep = _compare_all(inp, out, exact=True)
+    assert rep["exact"]
+    want = np.array([orc.decode_e4m3(int(c)) for c in codes], np.float64).reshape(2, 128)
+    assert np.array_equal(out[2].cpu().numpy().astype(np.float64), want + 0.0)

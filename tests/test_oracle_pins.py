@@ -323,3 +323,23 @@ def test_invariant_checker_catches_planted_mistakes():
     badv[63] -= 1                                               # wrong length
     with pytest.raises(AssertionError):
         check_rows(out["idx"], badv, range(64), **kw)
+
+
+def test_pair_bounds_closed_forms():
+    """B = sum_h |w_h| sum_i |q_hi k_i|: hand value on WE1, equal to the score
+    when every term is non-negative, and never below |s| (triangle inequality)."""
+    rec = load("we1_signed_relu.txt")
+    inp = _we_inputs(rec, S=4)
+    b = orc.pair_scores(inp, [3] * 4, [0, 1, 2, 3], bounds=True)
+    assert list(b) == [3.0, 4.0, 2.0, 5.0]   # k0=(2,1): 2+1, k1: 1+3, k2: 1+1, k3: 3+2
+    g = torch.Generator().manual_seed(9)
+    pos = gen.custom(q=torch.rand(8, 3, 16, generator=g), k=torch.rand(40, 16, generator=g),
+                     w=torch.rand(3, generator=g), topk=4, causal=False)
+    rows, keys = np.repeat(np.arange(8), 40), np.tile(np.arange(40), 8)
+    np.testing.assert_allclose(orc.pair_scores(pos, rows, keys, bounds=True),
+                               orc.pair_scores(pos, rows, keys), rtol=1e-14)
+    mix = gen.generate("c3_dsa_token", S=32, topk=8)
+    rows, keys = np.repeat(np.arange(32), 32), np.tile(np.arange(32), 32)
+    s = orc.pair_scores(mix, rows, keys)
+    bb = orc.pair_scores(mix, rows, keys, bounds=True)
+    assert np.all(bb >= np.abs(s)) and np.any(bb > 1.5 * np.abs(s))
