@@ -1,0 +1,221 @@
+"""Benchmark of the lightning-indexer step on one MI355X.
+
+One step = one pass of the whole hot path over the resident synthetic input:
+indexer_score_topk (scoring, streaming top-k, canonical rows, all query
+chunks) followed by the adjacent-pair overlap diagnostic.  Inputs are
+generated on the device before timing; W warm-up steps run untimed, then
+exactly K steps are timed between device synchronisations.
+
+Prints ONE JSON line: whole-job (query, key, head) triples per second, with
+queries/s, the MFMA roofline of the scoring kernel (HIP events on the stream
+the library launches on), HBM traffic from the committed rocprofv3 counter
+summary when it matches the current kernel source, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer (q,k,head) triples/s + queries/s at S=256K,H=64; % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}  # fp8 codes run on the bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", "score_select.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_select_c4_csa_256k_pmc.md")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(S, T, m, causal, q_pos0=0):
+    """sum_t P_t, P_t = min(T, (q_pos0 + t + 1) // m) (causal) or T."""
+    if not causal:
+        return S * T
+    total = 0
+    # closed form per block of positions sharing floor((p+1)/m)
+    p0, p1 = q_pos0, q_pos0 + S  # positions [p0, p1)
+    cap_pos = T * m - 1          # from this position on, P = T
+    def tri(a, b):  # sum_{p=a}^{b-1} floor((p+1)/m), 0 <= a <= b
+        def F(n):   # sum_{x=1}^{n} floor(x/m)
+            qn, r = divmod(n, m)
+            return m * qn * (qn - 1) // 2 + qn * (r + 1)
+        return F(b) - F(a)
+    lo = min(p1, max(p0, cap_pos))
+    total += tri(p0, lo)
+    total += (p1 - lo) * T
+    return total
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per score_select launch from the committed counter summary,
+    if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sha():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(inp, budget_s, seed):
+    """The oracle on seeded uniform rows of the same workload, for about
+    budget_s seconds of host time; a rate, so no extrapolation is needed."""
+    from oracle import oracle as orc
+    rng = np.random.default_rng(seed)
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, 16)
+    done_rows, done_triples, spent = 0, 0, 0.0
+    while spent < budget_s:
+        rows = np.sort(rng.integers(0, inp.S, size=4 * threads))
+        t0 = time.perf_counter()
+        orc.select_rows(inp, rows, nthreads=threads)
+        spent += time.perf_counter() - t0
+        done_rows += rows.size
+        done_triples += sum(min(inp.T, (int(r) + 1) // inp.m) for r in rows) * inp.H
+    return dict(value=done_triples / spent, unit="triples/s", cores=threads, kind="oracle",
+                sample=f"{done_rows} seeded uniform rows of the {inp.name} workload "
+                       f"({done_triples} triples, {spent:.1f} s, fp64, {threads} threads)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c4_csa_256k")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see the sharding note in the design document).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dsa_indexer_score_amd as dsai
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: library {dsai.library_path()}")
+    t0 = time.perf_counter()
+    inp = gen.generate(args.workload, device=dev)
+    torch.cuda.synchronize()
+    log(f"bench: generated {args.workload} S={inp.S} T={inp.T} H={inp.H} d={inp.d} m={inp.m} "
+        f"topk={inp.topk} dtype={inp.dtype} chunk={inp.query_chunk} in "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
+                      query_chunk=inp.query_chunk or 0, device=dev)
+    W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
+    idx = torch.empty((inp.S, W), dtype=torch.int32, device=dev)
+    vl = torch.empty((inp.S,), dtype=torch.int32, device=dev)
+    ws = torch.empty((ix.workspace_bytes(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk),),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
+                      q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
+                      workspace=ws, out=(idx, vl, None))
+        if ev:
+            ev[1].record(stream)
+        shared = dsai.pair_overlap(idx, vl)
+        if ev:
+            ev[2].record(stream)
+        return shared
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        shared = step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    score_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    ovl_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
+
+    ms_per_step = wall * 1e3 / args.steps
+    pairs = visible_pairs(inp.S, inp.T, inp.m, inp.causal, inp.q_pos0)
+    triples = pairs * inp.H
+    flops = 2 * inp.d * triples
+    n_launch = math.ceil(inp.S / (inp.query_chunk or inp.S))
+    score_s = float(np.mean(score_ms)) / 1e3
+    achieved_tflops = flops / score_s / 1e12
+    peak = PEAK_TFLOPS[inp.dtype]
+    traffic = stored_traffic()
+
+    st = dsai.overlap_summary(shared, vl)
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.int32, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("bench: copy calibration: 1 GiB read + 1 GiB written")
+
+    result = {
+        "metric": METRIC,
+        "value": triples / (ms_per_step / 1e3),
+        "unit": "triples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic (seeded, generated on device; no datasets or weights)",
+        "config": {"workload": inp.name, "S": inp.S, "T": inp.T, "H": inp.H, "d": inp.d,
+                   "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
+                   inp.query_chunk, "launches_per_step": n_launch, "parallelism": "none (1 GPU)"},
+        "queries_per_s": inp.S / (ms_per_step / 1e3),
+        "mfma_frac": achieved_tflops / peak,
+        "score_select_ms": float(np.mean(score_ms)),
+        "pair_overlap_ms": float(np.mean(ovl_ms)),
+        "peak_hbm_bytes_allocated": int(peak_bytes),
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / peak,
+                     "traffic": None if traffic is None else traffic,
+                     "kernel": "score_select", "flops_per_launch": flops / n_launch,
+                     "avg_launch_ms": score_s * 1e3 / n_launch},
+        "overlap": {k: st[k] for k in ("mean_overlap", "median_overlap", "mean_jaccard")},
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the CPU oracle for ~{args.cpu_budget:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, inp.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
 SOURCES = ["score_select.hip", "pair_overlap.hip", "indexer_api.cpp"]
 
+# Per-file extra flags.  The scoring kernel assumes finite inputs (a documented
+# precondition), so IEEE NaN quieting is switched off there: ReLU then lowers
+# to a single v_max_f32 instead of a canonicalising max followed by the max.
+FILE_FLAGS = {"score_select.hip": ["-fno-honor-nans", "-Xclang", "-mno-amdgpu-ieee"]}
+
 # Packed fp32 VALU ops are kept out of the generated code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,7 +39,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         res = subprocess.run(cmd, capture_output=True, text=True)

@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/dsa_indexer.h"
+#include "dsa_indexer.h"
 #include "kernels.h"
 
 struct indexer_s {
@@ -50,14 +50,16 @@ bool shape_supported(int dtype, int H, int d)
 
 int64_t ksel_of(int topk, int m, int flags) { return (flags & IDX_EXPAND) ? topk / m : topk; }
 
-// Candidate slots per query: room for 4x the selection (so a compaction,
-// which keeps ~Ksel, frees most of the buffer), never more than every
-// visible key plus one tile.
+// Candidate slots per query.  With the running threshold a query appends
+// about Ksel * (1 + ln(visible / Ksel)) candidates (plus histogram-bin slack),
+// so 10 * Ksel slots hold every append for visible / Ksel up to several
+// thousand and the compaction fallback stays rare; never more than every
+// visible key plus one group, and at most 65472 (16-bit histogram counters).
 int64_t capacity(int64_t ksel, int64_t pmax)
 {
-    int64_t cap = round_up(std::max<int64_t>(4 * ksel, ksel + 4 * dsai::kKeysPerTile),
-                           dsai::kKeysPerTile);
-    int64_t all = round_up(std::max<int64_t>(pmax, 0), dsai::kKeysPerTile) + dsai::kKeysPerTile;
+    const int64_t g = dsai::kSelGroup;
+    int64_t cap = std::min<int64_t>(round_up(10 * ksel + 4 * g, g), 65472);
+    int64_t all = round_up(std::max<int64_t>(pmax, 0), g) + g;
     return std::min(cap, all);
 }
 

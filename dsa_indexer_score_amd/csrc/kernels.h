@@ -32,7 +32,8 @@ struct ScoreSelectParams {
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
-constexpr int kKeysPerTile = 64;      // keys staged in LDS per step
+constexpr int kKeysPerTile = 128;     // keys staged in LDS per step
+constexpr int kSelGroup = 64;         // keys appended per selection step (one per lane)
 
 // dtype codes match enum idx_dtype
 hipError_t launch_score_select(int dtype, int nb, int d, const ScoreSelectParams &p,

@@ -189,13 +189,20 @@ template <int D> struct Op<0, D> {  // fp32
 };
 
 // ---------------------------------------------------------------------------
-// Selection helpers (one wave, one query).  `hist` is 1024 dwords of packed
-// 16-bit counters (2048 bins; the 10-bit level uses the first 512 dwords).
+// Selection helpers (one wave, one query).  Codes are cut in three radix
+// levels: the top kB1 = 12 bits (the running histogram), then 10 and 10.
+// `hist` holds kHistWords dwords of packed 16-bit counters (4096 bins); the
+// 10-bit levels use the first 512 dwords.
 // ---------------------------------------------------------------------------
+constexpr int kB1 = 12;                         // bits of the running histogram
+constexpr int kBins1 = 1 << kB1;
+constexpr int kShift1 = 32 - kB1;               // bin of a code: u >> kShift1
+constexpr int kHistWords = kBins1 / 2;
+
 __device__ __forceinline__ void hist_clear(uint32_t *hist, int lane)
 {
 #pragma unroll
-    for (int i = 0; i < 1024 / 64; ++i) hist[lane + 64 * i] = 0;
+    for (int i = 0; i < kHistWords / 64; ++i) hist[lane + 64 * i] = 0;
 }
 
 __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin)
@@ -203,7 +210,15 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin)
     atomicAdd(&hist[bin >> 1], 1u << ((bin & 1u) * 16));
 }
 
+__device__ __forceinline__ int hist_get(const uint32_t *hist, int bin)
+{
+    const uint32_t x = hist[bin >> 1];
+    return (int)((bin & 1) ? (x >> 16) : (x & 0xFFFFu));
+}
+
 // Bin b with (count above b) < need <= (count above b) + h[b]; needs total >= need >= 1.
+// Two lane-parallel levels: per-lane sums of nbins/64 bins with a suffix scan
+// across lanes give the owning range, then one bin per lane inside it.
 __device__ void find_boundary(const uint32_t *hist, int nbins, int need, int lane, int &b_out,
                               int &above_out, int &hb_out)
 {
@@ -221,28 +236,73 @@ __device__ void find_boundary(const uint32_t *hist, int nbins, int need, int lan
     }
     uint32_t nxt = __shfl_down(suf, 1);
     if (lane == 63) nxt = 0;
-    const bool mine = suf >= (uint32_t)need && nxt < (uint32_t)need;
-    const uint64_t bm = __ballot(mine);
+    const uint64_t bm = __ballot(suf >= (uint32_t)need && nxt < (uint32_t)need);
     int owner = __ffsll((unsigned long long)bm) - 1;
     if (owner < 0) owner = 0;  // unreachable while the histogram matches the buffer
-    int b = 0, above = 0, hb = 0;
-    if (lane == owner) {
-        uint32_t acc = nxt;
-        for (int i = per - 1; i >= 0; --i) {
-            uint32_t x = hist[lane * dpl + (i >> 1)];
-            uint32_t h = (i & 1) ? (x >> 16) : (x & 0xFFFFu);
-            if (acc + h >= (uint32_t)need) {
-                b = lane * per + i;
-                above = (int)acc;
-                hb = (int)h;
-                break;
-            }
-            acc += h;
-        }
+    const uint32_t base = __shfl(nxt, owner);  // count above the owner's range
+    // lane i < per takes bin owner*per + per-1-i (descending); inclusive prefix
+    const int bin = owner * per + per - 1 - lane;
+    uint32_t h = lane < per ? (uint32_t)hist_get(hist, bin) : 0u;
+    uint32_t incl = h;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
     }
-    b_out = __shfl(b, owner);
-    above_out = __shfl(above, owner);
-    hb_out = __shfl(hb, owner);
+    const uint64_t hit = __ballot(lane < per && base + incl >= (uint32_t)need);
+    int L = __ffsll((unsigned long long)hit) - 1;
+    if (L < 0) L = 0;
+    b_out = owner * per + per - 1 - L;
+    hb_out = (int)__shfl(h, L);
+    above_out = (int)(base + __shfl(incl, L) - (uint32_t)hb_out);
+}
+
+// Raise the running boundary bin tb (above = count in bins > tb) until
+// above < need, 64 bins per step: lane i looks at bin tb + 1 + i, and the
+// first lane whose inclusive prefix brings `above` below `need` is the new tb.
+// Long runs of empty bins (e.g. all tiny magnitudes between -eps and +eps)
+// cost one step per 64 bins.
+__device__ void advance_boundary(const uint32_t *hist, int need, int lane, int &tb, int &above)
+{
+    while (above >= need) {
+        const int b = tb + 1 + lane;
+        int incl = b < kBins1 ? hist_get(hist, b) : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        const uint64_t ok = __ballot(above - incl < need);
+        if (ok) {
+            const int L = __ffsll((unsigned long long)ok) - 1;
+            tb += 1 + L;
+            above -= __shfl(incl, L);
+            return;
+        }
+        tb += 64;
+        above -= __shfl(incl, 63);
+    }
+}
+
+// Visit buf[0, cnt) in buffer order, kBatch chunks of 64 entries at a time:
+// all loads of a batch are issued before any of them is consumed, so a pass
+// costs a few memory round trips per 512 entries instead of one per 64.  The
+// callback may store into buf at or below the entry it was given (in-place
+// compaction): later batches are read before those positions are reached.
+constexpr int kBatch = 8;
+template <class F>
+__device__ __forceinline__ void for_each_entry(const uint2 *buf, int cnt, int lane, F &&f)
+{
+    for (int base = 0; base < cnt; base += 64 * kBatch) {
+        uint2 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int e = base + i * 64 + lane;
+            v[i] = e < cnt ? buf[e] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) f(base + i * 64 + lane < cnt, v[i]);
+    }
 }
 
 struct Cut {
@@ -251,48 +311,34 @@ struct Cut {
     int need_eq;
 };
 
-// Choose the cut that keeps at least `need` of the buffer's best entries.
-// With allow_approx, a histogram-bin edge is accepted when it keeps at most
-// `approx_limit` entries; otherwise the cut is exact (keeps exactly `need`).
-__device__ Cut choose_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, bool allow_approx,
-                          int approx_limit, int lane)
+// Levels 2 and 3 of the radix cut: `src(f)` feeds every candidate code of the
+// level-1 boundary bin b1 to f (from the buffer or from an LDS gather), a1 is
+// the count above b1.  Returns the cut that keeps exactly `need` entries.
+template <class Src>
+__device__ Cut refine_cut(Src &&src, int need, int b1, int a1, uint32_t *hist, int lane)
 {
     Cut c;
-    int b1, a1, h1;
-    find_boundary(hist, 2048, need, lane, b1, a1, h1);
-    if ((allow_approx && a1 + h1 <= approx_limit) || a1 + h1 == need) {
-        c.tc = (uint32_t)b1 << 21;
-        c.exact = 0;
-        c.need_eq = 0;
-        return c;
-    }
-    // level 2: bits 20..10 of the entries in bin b1
     wave_sync_mem();
     hist_clear(hist, lane);
     wave_sync_mem();
-    for (int e = lane; e < cnt; e += 64) {
-        uint32_t u = ord_code(buf[e].x);
-        if ((u >> 21) == (uint32_t)b1) hist_add(hist, (u >> 10) & 2047u);
-    }
+    src([&](uint32_t u) { hist_add(hist, (u >> 10) & 1023u); });
     wave_sync_mem();
     int b2, a2, h2;
-    find_boundary(hist, 2048, need - a1, lane, b2, a2, h2);
+    find_boundary(hist, 1024, need - a1, lane, b2, a2, h2);
     const int above = a1 + a2;
-    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
+    const uint32_t pre = ((uint32_t)b1 << 10) | (uint32_t)b2;  // top 22 bits
     if (above + h2 == need) {
         c.tc = pre << 10;
         c.exact = 0;
         c.need_eq = 0;
         return c;
     }
-    // level 3: bits 9..0 of the entries sharing the top 22 bits
     wave_sync_mem();
     hist_clear(hist, lane);
     wave_sync_mem();
-    for (int e = lane; e < cnt; e += 64) {
-        uint32_t u = ord_code(buf[e].x);
+    src([&](uint32_t u) {
         if ((u >> 10) == pre) hist_add(hist, u & 1023u);
-    }
+    });
     wave_sync_mem();
     int b3, a3, h3;
     find_boundary(hist, 1024, need - above, lane, b3, a3, h3);
@@ -302,6 +348,53 @@ __device__ Cut choose_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, b
     return c;
 }
 
+// Cut that keeps at least `need` of the buffer's best entries.  With
+// allow_approx, a level-1 bin edge is accepted when it keeps at most
+// `approx_limit` entries; otherwise the cut is exact (keeps exactly `need`).
+__device__ Cut choose_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, bool allow_approx,
+                          int approx_limit, int lane)
+{
+    int b1, a1, h1;
+    find_boundary(hist, kBins1, need, lane, b1, a1, h1);
+    if ((allow_approx && a1 + h1 <= approx_limit) || a1 + h1 == need) {
+        Cut c;
+        c.tc = (uint32_t)b1 << kShift1;
+        c.exact = 0;
+        c.need_eq = 0;
+        return c;
+    }
+    auto src = [&](auto &&f) {
+        for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
+            const uint32_t u = ord_code(v.x);
+            if (valid && (u >> kShift1) == (uint32_t)b1) f(u);
+        });
+    };
+    return refine_cut(src, need, b1, a1, hist, lane);
+}
+
+// Exact cut for the final selection: the codes of the level-1 boundary bin
+// are gathered (one batched pass, buffer order) into `gather` (LDS, gcap
+// entries) and refined there; a bin larger than gcap refines from the buffer.
+__device__ Cut final_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, uint32_t *gather,
+                         int gcap, int lane)
+{
+    int b1, a1, h1;
+    find_boundary(hist, kBins1, need, lane, b1, a1, h1);
+    if (a1 + h1 == need || h1 > gcap) return choose_cut(buf, cnt, need, hist, false, 0, lane);
+    int gcnt = 0;
+    for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
+        const uint32_t u = ord_code(v.x);
+        const bool in = valid && (u >> kShift1) == (uint32_t)b1;
+        const uint64_t m = __ballot(in);
+        if (in) gather[gcnt + lane_rank(m)] = u;
+        gcnt += __popcll(m);
+    });
+    auto src = [&](auto &&f) {
+        for (int i = lane; i < gcnt; i += 64) f(gather[i]);
+    };
+    return refine_cut(src, need, b1, a1, hist, lane);
+}
+
 // Stable in-place compaction of buf[0, cnt) under `cut`; rebuilds the histogram.
 __device__ void compact(uint2 *buf, int &cnt, const Cut &cut, uint32_t *hist, int lane)
 {
@@ -309,10 +402,7 @@ __device__ void compact(uint2 *buf, int &cnt, const Cut &cut, uint32_t *hist, in
     hist_clear(hist, lane);
     wave_sync_mem();
     int wcnt = 0, eqseen = 0;
-    for (int base = 0; base < cnt; base += 64) {
-        const int e = base + lane;
-        const bool valid = e < cnt;
-        const uint2 v = valid ? buf[e] : make_uint2(0u, 0u);
+    for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
         const uint32_t u = ord_code(v.x);
         bool keep;
         if (cut.exact) {
@@ -326,10 +416,10 @@ __device__ void compact(uint2 *buf, int &cnt, const Cut &cut, uint32_t *hist, in
         const uint64_t km = __ballot(keep);
         if (keep) {
             buf[wcnt + lane_rank(km)] = v;
-            hist_add(hist, u >> 21);
+            hist_add(hist, u >> kShift1);
         }
         wcnt += __popcll(km);
-    }
+    });
     cnt = wcnt;
     wave_sync_mem();
 }
@@ -348,7 +438,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
 
     __shared__ uint4 ktile[2][TILE_CH];
     __shared__ float kscale_tile[2][kKeysPerTile];
-    __shared__ uint32_t hist_all[kQueriesPerBlock][1024];
+    __shared__ uint32_t hist_all[kQueriesPerBlock][kHistWords];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = lane >> 5, l32 = lane & 31;
@@ -394,8 +484,10 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
 
     uint2 *buf = p.ws + (active ? qrow : 0) * (int64_t)p.cap;
     int cnt = 0;
-    uint32_t tau = 0;
-    const int approx_limit = (p.cap + p.ksel) / 2;
+    uint32_t tau = 0;        // pass iff code >= tau
+    bool tracking = false;   // cnt has reached ksel: tb / above are maintained
+    int tb = 0, above = 0;   // boundary bin of the running histogram, count above it
+    const int approx_limit = (p.cap + p.ksel) / 2;  // <= cap - kSelGroup: cap >= ksel + 4 groups
 
     const char *kbytes = static_cast<const char *>(p.k);
     uint4 stage[CPT];
@@ -435,15 +527,72 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     }
     __syncthreads();
 
+    // Selection of one tile's scores (NG groups of 64 keys, one key per lane).
+    constexpr int NCB = kKeysPerTile / 32;  // 32-key column blocks per tile
+    constexpr int NG = NCB / 2;             // 64-key selection groups per tile
+    auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int64_t key = j0 + g * kSelGroup + lane;
+            const uint32_t bits = __float_as_uint(sg[g]);
+            const uint32_t u = ord_code(bits);
+            const bool pass = key < Pq && u >= tau;
+            const uint64_t mask = __ballot(pass);
+            if (mask) {
+                if (pass) {
+                    buf[cnt + lane_rank(mask)] = make_uint2(bits, (uint32_t)key);
+                    hist_add(hist, u >> kShift1);
+                }
+                cnt += __popcll(mask);
+                if (tracking) {
+                    // keep tau near the edge of the bin holding the Ksel-th best;
+                    // the boundary may lag by up to one group of entries
+                    above += __popcll(__ballot(pass && (int)(u >> kShift1) > tb));
+                    if (above >= p.ksel + kSelGroup) {
+                        advance_boundary(hist, p.ksel, lane, tb, above);
+                        const uint32_t edge = (uint32_t)tb << kShift1;
+                        tau = edge > tau ? edge : tau;
+                    }
+                } else if (cnt >= p.ksel) {
+                    tracking = true;
+                    int hb;
+                    find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
+                    const uint32_t edge = (uint32_t)tb << kShift1;
+                    tau = edge > tau ? edge : tau;
+                }
+                if (cnt > p.cap - kSelGroup) {  // overflow fallback
+                    wave_sync_mem();
+                    const Cut cut = choose_cut(buf, cnt, p.ksel, hist, true, approx_limit, lane);
+                    compact(buf, cnt, cut, hist, lane);
+                    tau = cut.tc + 1;
+                    int hb;
+                    find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
+                }
+            }
+        }
+    };
+
+    // The two waves sharing a SIMD (w and w + 4) run their selection at
+    // opposite ends of a tile: waves 0-3 right after their MFMA/epilogue work,
+    // waves 4-7 one tile later, before their MFMAs -- so one wave's branchy
+    // selection code always has the other wave's MFMAs to overlap with.
+    const bool lagged = wave >= kQueriesPerBlock / 2;
+    float pend[NG];
+    int64_t pend_j0 = -1;
+
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
         const int64_t j0 = (int64_t)it * kKeysPerTile;
         if (it + 1 < ntiles) load_tile(it + 1);
 
+        if (lagged && pend_j0 >= 0) {
+            select_tile(pend, pend_j0);
+            pend_j0 = -1;
+        }
         if (active && j0 < Pq) {
-            float part[2];
+            float part[NCB];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb) {
                 const int r = cb * 32 + l32;
                 A bfr[KS];
                 O::load_b(ktile[cur], r, hh, r & SWZ, bfr);
@@ -463,54 +612,48 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                     for (int v = 0; v < 16; ++v) s = fmaf(wv[b][v], fmaxf(acc[b][v], 0.f), s);
                 part[cb] = s;
             }
-            // lanes < 32 finish keys 0..31 of the tile, lanes >= 32 keys 32..63
-            const float send = hh ? part[0] : part[1];
-            const float recv = __shfl_xor(send, 32);
-            float s = (hh ? part[1] : part[0]) + recv;
-            if (DT == 2) s *= kscale_tile[cur][lane];
-
-            const int64_t key = j0 + lane;
-            const uint32_t bits = __float_as_uint(s);
-            const uint32_t u = ord_code(bits);
-            const bool pass = key < Pq && u >= tau;
-            const uint64_t mask = __ballot(pass);
-            if (mask) {
-                if (pass) {
-                    buf[cnt + lane_rank(mask)] = make_uint2(bits, (uint32_t)key);
-                    hist_add(hist, u >> 21);
-                }
-                cnt += __popcll(mask);
-                if (cnt > p.cap - kKeysPerTile) {
-                    wave_sync_mem();
-                    const Cut cut = choose_cut(buf, cnt, p.ksel, hist, true, approx_limit, lane);
-                    compact(buf, cnt, cut, hist, lane);
-                    tau = cut.tc + 1;
-                }
+            float sg[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                // lanes < 32 finish keys 0..31 of this 64-key group, lanes >= 32 keys 32..63
+                const float send = hh ? part[2 * g] : part[2 * g + 1];
+                const float recv = __shfl_xor(send, 32);
+                sg[g] = (hh ? part[2 * g + 1] : part[2 * g]) + recv;
+                if (DT == 2) sg[g] *= kscale_tile[cur][g * kSelGroup + lane];
+            }
+            if (lagged) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g) pend[g] = sg[g];
+                pend_j0 = j0;
+            } else {
+                select_tile(sg, j0);
             }
         }
         if (it + 1 < ntiles) store_tile(cur ^ 1);
         __syncthreads();
     }
+    if (pend_j0 >= 0) select_tile(pend, pend_j0);
 
     if (!active) return;
 
     // ---- exact final selection, written straight into the output row ----
+    // The K tiles are idle after the last barrier: each wave borrows a slice
+    // of them to gather the codes of its boundary histogram bin.
+    constexpr int kGatherCap = (int)(sizeof(ktile) / kQueriesPerBlock / sizeof(uint32_t));
+    uint32_t *gather = reinterpret_cast<uint32_t *>(&ktile[0][0]) + wave * kGatherCap;
     wave_sync_mem();
     Cut cut;
     cut.tc = 0;
     cut.exact = 0;
     cut.need_eq = 0;
-    if (cnt > p.ksel) cut = choose_cut(buf, cnt, p.ksel, hist, false, 0, lane);
+    if (cnt > p.ksel) cut = final_cut(buf, cnt, p.ksel, hist, gather, kGatherCap, lane);
     wave_sync_mem();
 
     const int mexp = p.expand ? p.m : 1;
     int32_t *orow = p.idx + t * (int64_t)p.W;
     float *srow = p.sel_score ? p.sel_score + t * (int64_t)p.W : nullptr;
     int wcnt = 0, eqseen = 0;
-    for (int base = 0; base < cnt; base += 64) {
-        const int e = base + lane;
-        const bool valid = e < cnt;
-        const uint2 v = valid ? buf[e] : make_uint2(0u, 0u);
+    for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
         const uint32_t u = ord_code(v.x);
         bool keep;
         if (cut.exact) {
@@ -530,7 +673,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             }
         }
         wcnt += __popcll(km);
-    }
+    });
     const int body = wcnt * mexp;
     const int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - Pq * p.m) : 0;
     for (int s = body + lane; s < p.W; s += 64) {

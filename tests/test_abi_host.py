@@ -72,9 +72,9 @@ def test_workspace_bytes_scale_with_chunk_and_selection():
     lib, h = _handle(chunk=16384)
     n = ctypes.c_size_t()
     assert lib.indexer_workspace_bytes(h, 262144, 65536, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == 16384 * 8192 * 8          # 4 x 2048 candidate slots of 8 bytes per query
+    assert n.value == 16384 * 20736 * 8         # 10 x 2048 + 256 candidate slots of 8 bytes
     assert lib.indexer_workspace_bytes(h, 100, 65536, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == 100 * 8192 * 8            # chunk clipped to S
+    assert n.value == 100 * 20736 * 8           # chunk clipped to S
     assert lib.indexer_workspace_bytes(h, 100, 100, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 100 * 192 * 8             # never more than all keys plus one tile
     assert lib.indexer_workspace_bytes(h, 100, 10 ** 6, 64, 128, 1, 20000,
