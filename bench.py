@@ -177,11 +177,14 @@ def main():
 
     st = dsai.overlap_summary(shared, vl)
     if args.copy_calibration:
-        a = torch.empty(256 << 20, dtype=torch.int32, device=dev)  # 1 GiB
+        # One elementwise kernel of known size (reads 1 GiB, writes 1 GiB): the
+        # scale for the FETCH_SIZE / WRITE_SIZE counters of the same run.
+        a = torch.ones(256 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
         torch.cuda.synchronize()
-        log("bench: copy calibration: 1 GiB read + 1 GiB written")
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        log("bench: copy calibration: 1 GiB read + 1 GiB written (neg kernel)")
 
     result = {
         "metric": METRIC,

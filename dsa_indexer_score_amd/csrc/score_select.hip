@@ -9,22 +9,33 @@
 // [S, H, T] or [S, T] intermediate never exists.
 //
 // Work decomposition (one block = 8 consecutive queries, one per wave):
-//  * The block walks the keys visible to its last query in tiles of 64 keys.
-//    Each tile is staged once into LDS (XOR-swizzled 16-B chunks) and read by
-//    all 8 waves, so every key row is fetched from L2 once per 8 queries.
+//  * The block walks the keys visible to its last query in tiles of 128 keys.
+//    Each tile is staged once into LDS (XOR-swizzled 16-B chunks, double
+//    buffered: tile i+1 is fetched into registers while tile i is scored) and
+//    read by all 8 waves, so every key row is fetched from L2 once per 8
+//    queries.  Blocks are issued heaviest-first (last query group first) so
+//    the causal triangle's long rows start early.
 //  * A wave holds its query's q[t, :, :] in registers as MFMA A operands:
 //    A rows = 32 heads per block (NB blocks cover H <= 32*NB heads; missing
 //    heads are zero rows with zero weight), B columns = 32 keys, the d axis
 //    is the contraction.  bf16: v_mfma_f32_32x32x16_bf16; fp8 (OCP e4m3):
 //    codes widened exactly to bf16 in registers / while staging to LDS, then
-//    the same bf16 MFMA (fp32 accumulation); fp32: v_mfma_f32_32x32x2_f32.  Accumulators hold 16 heads x 1 key per lane;
-//    the signed-ReLU head sum runs in registers (max + fma per element), one
-//    cross-half shuffle finishes it, and each lane ends with the score of one
-//    key of the 64-key tile.
+//    the same bf16 MFMA (fp32 accumulation); fp32: v_mfma_f32_32x32x2_f32.
+//    Accumulators hold 16 heads x 1 key per lane; the signed-ReLU head sum
+//    runs in registers (max + fma per element), and a swap of register
+//    halves between the two 16-head partial sums (v_permlane32_swap)
+//    finishes it: each lane ends with the score of one key of a 64-key
+//    selection group.
+//  * The MFMAs of one (32-key column block, 32-head block) step are issued
+//    interleaved with the epilogue of the previous step and with the LDS
+//    reads of the next column block's B operands, so the VALU work runs in
+//    the shadow of the matrix pipe instead of after it.
 //  * fp8: per-row scales fold out of the ReLU because it is positively
 //    homogeneous (DoSA summary, "ReLU subadditivity, positive homogeneity"):
 //    w'[t,h] = w[t,h] * q_scale[t,h] multiplies the head sum, k_scale[j]
 //    multiplies the finished score.
+//  * The two waves that share a SIMD (w and w + 4) select at opposite ends of
+//    a tile, so one wave's branchy selection overlaps the other's MFMAs.
 //
 // Streaming selection (per wave, per query; no block barrier involved):
 //  * Scores map to an order-preserving 32-bit code u (-0 folded into +0).
@@ -32,19 +43,24 @@
 //    subset of size >= Ksel has a Ksel-th score no larger than the full set's
 //    (DoSA summary, "Top-K threshold and subset lower bound").  Keys scan in
 //    ascending index order, so a new key can only enter if u >= tau.
+//    The pass test runs on the float score against the threshold's decoded
+//    value, which is exactly equivalent to comparing codes.
 //  * Survivors are appended, ballot-compacted, to the query's candidate buffer
 //    in global memory (ascending key order is preserved), and counted in a
-//    2048-bin LDS histogram of u's top 11 bits.
-//  * When the buffer could overflow on the next tile, the histogram gives the
-//    bin that holds the Ksel-th code; entries below it are dropped in one
-//    stable in-place pass and tau rises to that bin's edge.  If the bin holds
-//    too many entries (near-ties), two more radix levels (11 + 10 bits) find
-//    the exact Ksel-th code and equal codes are cut by buffer position, which
-//    is key order -- the tie rule.
-//  * After the last tile the same exact selection runs once more and writes
-//    the output row directly: survivors in buffer order are already sorted by
-//    KV index ("Adjacent-Query KV-Index Overlap in 256K DSA Training",
-//    section 3), pools expand to m positions and the incomplete tail follows
+//    4096-bin LDS histogram of u's top 12 bits (16-bit packed counters).
+//  * Once Ksel entries exist, the wave tracks the histogram bin tb holding
+//    the Ksel-th best code and the count above it; when that count runs a
+//    group past Ksel, tb advances (64 bins per lane-parallel step) and tau
+//    rises to tb's lower edge.  Entries below tau are never appended.
+//  * If the buffer could still overflow, the histogram gives a cut; entries
+//    below it are dropped in one stable in-place pass.  Near-ties in one bin
+//    are resolved by two more radix levels (10 + 10 bits), and equal codes
+//    are cut by buffer position, which is key order -- the tie rule.
+//  * After the last tile the exact selection runs once more (boundary-bin
+//    codes gathered into the idle K tiles in LDS) and writes the output row
+//    directly: survivors in buffer order are already sorted by KV index
+//    ("Adjacent-Query KV-Index Overlap in 256K DSA Training", section 3),
+//    pools expand to m positions and the incomplete tail follows
 //    (GLM-5.3-Flash Module 06 "DSA & KPool", section 2), then -1 padding.
 #include "kernels.h"
 
@@ -66,6 +82,33 @@ __device__ __forceinline__ int lane_rank(uint64_t mask)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Inclusive prefix sum over the 64 lanes (lane 0 first), in registers:
+// Hillis-Steele steps within each 16-lane row, then the row totals.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+
+// Smallest float value whose order code is >= c: s >= code_floor_value(c)
+// holds exactly when ord_code(s) >= c, for every finite s.
+__device__ __forceinline__ float code_floor_value(uint32_t c)
+{
+    if (c >= 0x80000000u) return __uint_as_float(c & 0x7FFFFFFFu);
+    if (c >= 0x007FFFFFu) return __uint_as_float(~c);
+    return -__builtin_inff();
 }
 
 // Wait for this wave's outstanding LDS and global accesses.
@@ -108,6 +151,10 @@ template <int D> struct Op<1, D> {  // bf16
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             b[ks] = __builtin_bit_cast(A, tile[r * NCH + ((hh * KS + ks) ^ swz)]);
+    }
+    __device__ static void load_b_one(const uint4 *tile, int r, int hh, int swz, int ks, A &b)
+    {
+        b = __builtin_bit_cast(A, tile[r * NCH + ((hh * KS + ks) ^ swz)]);
     }
     __device__ static f32x16 mma(A a, A b, f32x16 c)
     {
@@ -181,6 +228,12 @@ template <int D> struct Op<0, D> {  // fp32
             b[4 * c + 2] = __uint_as_float(v.z); b[4 * c + 3] = __uint_as_float(v.w);
         }
     }
+    __device__ static void load_b_one(const uint4 *tile, int r, int hh, int swz, int ks, A &b)
+    {
+        const uint4 v = tile[r * NCH + ((hh * (KS / 4) + ks / 4) ^ swz)];
+        const uint32_t w = ks % 4 == 0 ? v.x : ks % 4 == 1 ? v.y : ks % 4 == 2 ? v.z : v.w;
+        b = __uint_as_float(w);
+    }
     __device__ static f32x16 mma(A a, A b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -223,38 +276,31 @@ __device__ void find_boundary(const uint32_t *hist, int nbins, int need, int lan
                               int &above_out, int &hb_out)
 {
     const int per = nbins / 64, dpl = per / 2;
+    // lane i sums range 63 - i of the bins, so a prefix over lanes is a
+    // suffix over ranges (counted from the top bins down)
+    const int ri = 63 - lane;
     uint32_t sum = 0;
     for (int i = 0; i < dpl; ++i) {
-        uint32_t x = hist[lane * dpl + i];
+        uint32_t x = hist[ri * dpl + i];
         sum += (x & 0xFFFFu) + (x >> 16);
     }
-    uint32_t suf = sum;  // inclusive suffix sum over lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t v = __shfl_down(suf, off);
-        if (lane + off < 64) suf += v;
-    }
-    uint32_t nxt = __shfl_down(suf, 1);
-    if (lane == 63) nxt = 0;
-    const uint64_t bm = __ballot(suf >= (uint32_t)need && nxt < (uint32_t)need);
-    int owner = __ffsll((unsigned long long)bm) - 1;
-    if (owner < 0) owner = 0;  // unreachable while the histogram matches the buffer
-    const uint32_t base = __shfl(nxt, owner);  // count above the owner's range
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t excl = incl - sum;
+    const uint64_t bm = __ballot(incl >= (uint32_t)need && excl < (uint32_t)need);
+    int L0 = __ffsll((unsigned long long)bm) - 1;
+    if (L0 < 0) L0 = 0;  // unreachable while the histogram matches the buffer
+    const int owner = 63 - L0;
+    const uint32_t base = lane_value(excl, L0);  // count above the owner's range
     // lane i < per takes bin owner*per + per-1-i (descending); inclusive prefix
     const int bin = owner * per + per - 1 - lane;
-    uint32_t h = lane < per ? (uint32_t)hist_get(hist, bin) : 0u;
-    uint32_t incl = h;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-    }
-    const uint64_t hit = __ballot(lane < per && base + incl >= (uint32_t)need);
+    const uint32_t h = lane < per ? (uint32_t)hist_get(hist, bin) : 0u;
+    const uint32_t incl2 = wave_incl_scan(h);
+    const uint64_t hit = __ballot(lane < per && base + incl2 >= (uint32_t)need);
     int L = __ffsll((unsigned long long)hit) - 1;
     if (L < 0) L = 0;
     b_out = owner * per + per - 1 - L;
-    hb_out = (int)__shfl(h, L);
-    above_out = (int)(base + __shfl(incl, L) - (uint32_t)hb_out);
+    hb_out = (int)lane_value(h, L);
+    above_out = (int)(base + lane_value(incl2, L) - (uint32_t)hb_out);
 }
 
 // Raise the running boundary bin tb (above = count in bins > tb) until
@@ -266,21 +312,16 @@ __device__ void advance_boundary(const uint32_t *hist, int need, int lane, int &
 {
     while (above >= need) {
         const int b = tb + 1 + lane;
-        int incl = b < kBins1 ? hist_get(hist, b) : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
-        }
+        const int incl = (int)wave_incl_scan(b < kBins1 ? (uint32_t)hist_get(hist, b) : 0u);
         const uint64_t ok = __ballot(above - incl < need);
         if (ok) {
             const int L = __ffsll((unsigned long long)ok) - 1;
             tb += 1 + L;
-            above -= __shfl(incl, L);
+            above -= (int)lane_value((uint32_t)incl, L);
             return;
         }
         tb += 64;
-        above -= __shfl(incl, 63);
+        above -= (int)lane_value((uint32_t)incl, 63);
     }
 }
 
@@ -485,6 +526,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     uint2 *buf = p.ws + (active ? qrow : 0) * (int64_t)p.cap;
     int cnt = 0;
     uint32_t tau = 0;        // pass iff code >= tau
+    float tau_f = -__builtin_inff();  // the same test on the float score
     bool tracking = false;   // cnt has reached ksel: tb / above are maintained
     int tb = 0, above = 0;   // boundary bin of the running histogram, count above it
     const int approx_limit = (p.cap + p.ksel) / 2;  // <= cap - kSelGroup: cap >= ksel + 4 groups
@@ -531,14 +573,15 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     constexpr int NCB = kKeysPerTile / 32;  // 32-key column blocks per tile
     constexpr int NG = NCB / 2;             // 64-key selection groups per tile
     auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
+        const bool full = j0 + kKeysPerTile <= Pq;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const int64_t key = j0 + g * kSelGroup + lane;
             const uint32_t bits = __float_as_uint(sg[g]);
-            const uint32_t u = ord_code(bits);
-            const bool pass = key < Pq && u >= tau;
+            const bool pass = sg[g] >= tau_f && (full || key < Pq);
             const uint64_t mask = __ballot(pass);
             if (mask) {
+                const uint32_t u = ord_code(bits);
                 if (pass) {
                     buf[cnt + lane_rank(mask)] = make_uint2(bits, (uint32_t)key);
                     hist_add(hist, u >> kShift1);
@@ -552,6 +595,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                         advance_boundary(hist, p.ksel, lane, tb, above);
                         const uint32_t edge = (uint32_t)tb << kShift1;
                         tau = edge > tau ? edge : tau;
+                        tau_f = code_floor_value(tau);
                     }
                 } else if (cnt >= p.ksel) {
                     tracking = true;
@@ -559,12 +603,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                     find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
                     const uint32_t edge = (uint32_t)tb << kShift1;
                     tau = edge > tau ? edge : tau;
+                    tau_f = code_floor_value(tau);
                 }
                 if (cnt > p.cap - kSelGroup) {  // overflow fallback
                     wave_sync_mem();
                     const Cut cut = choose_cut(buf, cnt, p.ksel, hist, true, approx_limit, lane);
                     compact(buf, cnt, cut, hist, lane);
                     tau = cut.tc + 1;
+                    tau_f = code_floor_value(tau);
                     int hb;
                     find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
                 }
@@ -590,35 +636,56 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             pend_j0 = -1;
         }
         if (active && j0 < Pq) {
+            // Software pipeline over steps (cb, b): the MFMAs of step s run
+            // while the signed-ReLU epilogue of step s-1 is issued between
+            // them; B of the next column block is fetched during the last
+            // step that reads the current one.
+            constexpr int NS = NCB * NB;
             float part[NCB];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const int r = cb * 32 + l32;
-                A bfr[KS];
-                O::load_b(ktile[cur], r, hh, r & SWZ, bfr);
-                f32x16 acc[NB];
+            for (int cb = 0; cb < NCB; ++cb) part[cb] = 0.f;
+            A bfr[KS];
+            O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
+            f32x16 accp;
+            constexpr int EPK = (16 + KS - 1) / KS;  // epilogue elements per MFMA slot
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+            for (int s = 0; s <= NS; ++s) {
+                const int cb = s / NB, b = s % NB;
+                const int pcb = (s - 1) / NB, pb = (s - 1) % NB;
+                const bool loads = s < NS && b == NB - 1 && cb + 1 < NCB;
+                f32x16 acc;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+                for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+                float e = s > 0 ? part[pcb] : 0.f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (s < NS) acc = O::mma(qa[b][ks], bfr[ks], acc);
+                    if (loads) {
+                        const int r = (cb + 1) * 32 + l32;
+                        O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
+                    }
+                    if (s > 0) {
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) acc[b] = O::mma(qa[b][ks], bfr[ks], acc[b]);
-                float s = 0.f;
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) s = fmaf(wv[b][v], fmaxf(acc[b][v], 0.f), s);
-                part[cb] = s;
+                        for (int x = 0; x < EPK; ++x) {
+                            const int v = ks * EPK + x;
+                            if (v < 16) e = fmaf(wv[pb][v], fmaxf(accp[v], 0.f), e);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (s > 0) part[pcb] = e;
+                if (s < NS) accp = acc;
             }
             float sg[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                // lanes < 32 finish keys 0..31 of this 64-key group, lanes >= 32 keys 32..63
-                const float send = hh ? part[2 * g] : part[2 * g + 1];
-                const float recv = __shfl_xor(send, 32);
-                sg[g] = (hh ? part[2 * g + 1] : part[2 * g]) + recv;
+                // lanes < 32 finish keys 0..31 of this 64-key group, lanes >= 32
+                // keys 32..63: swap the upper half of part[2g] with the lower
+                // half of part[2g+1] and add
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[2 * g]),
+                                                                 __float_as_uint(part[2 * g + 1]),
+                                                                 false, false);
+                sg[g] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                 if (DT == 2) sg[g] *= kscale_tile[cur][g * kSelGroup + lane];
             }
             if (lagged) {
