@@ -267,6 +267,42 @@ def test_pair_overlap_matches_oracle():
     assert (want[:100] == hv[0:200:2]).all()
 
 
+@pytest.mark.parametrize("W", [2051, 5000])
+def test_pair_overlap_wide_ranges_and_ragged_rows(W):
+    """Rows whose index range spans several bitmap windows (up to 400,000),
+    ragged and empty valid lengths, an odd row count, shared and disjoint
+    entries, rows short enough to sit in registers and rows longer than that
+    -- against the oracle's exact set intersection."""
+    import dsa_indexer_score_amd as dsai
+    rng = np.random.default_rng(11 + W)
+    S = 301
+    idx = np.full((S, W), -1, np.int32)
+    vl = np.zeros(S, np.int32)
+    for t in range(S):
+        span = int(rng.choice([50, 5000, 140000, 400000]))
+        n = int(rng.choice([0, 1, 63, 64, 65, 1000, 2400, W])) if t % 7 else 0
+        n = min(n, span, W)
+        if t % 2 == 1 and vl[t - 1] > 0 and rng.random() < 0.7:
+            prev = idx[t - 1, :vl[t - 1]]            # overlap with the partner row
+            keep = prev[rng.random(prev.size) < 0.5]
+            extra = rng.choice(span, size=n, replace=False)
+            row = np.unique(np.concatenate([keep, extra]))[:W]
+        else:
+            row = np.sort(rng.choice(span, size=n, replace=False))
+        idx[t, :row.size] = row
+        vl[t] = row.size
+    d_idx = torch.from_numpy(idx).to(DEV)
+    d_vl = torch.from_numpy(vl).to(DEV)
+    shared = dsai.pair_overlap(d_idx, d_vl)
+    torch.cuda.synchronize()
+    want = orc.pair_overlap(idx, vl)
+    assert shared.shape[0] == S // 2
+    assert np.array_equal(shared.cpu().numpy(), want)
+    assert want.max() > 0 and (want == 0).any()
+    if W > 2304:
+        assert (vl > 2304).any()
+
+
 def test_fp8_every_code_is_widened_exactly():
     """Each of the 254 finite e4m3 codes, read through the kernel's widening
     and contraction, reproduces the oracle's hand-decoded value exactly:
