@@ -90,7 +90,8 @@ def cpu_baseline(inp, budget_s, seed):
         orc.select_rows(inp, rows, nthreads=threads)
         spent += time.perf_counter() - t0
         done_rows += rows.size
-        done_triples += sum(min(inp.T, (int(r) + 1) // inp.m) for r in rows) * inp.H
+        done_triples += sum(min(inp.T, (int(r) + inp.q_pos0 + 1) // inp.m) if inp.causal
+                            else inp.T for r in rows) * inp.H
     return dict(value=done_triples / spent, unit="triples/s", cores=threads, kind="oracle",
                 sample=f"{done_rows} seeded uniform rows of the {inp.name} workload "
                        f"({done_triples} triples, {spent:.1f} s, fp64, {threads} threads)")
@@ -106,6 +107,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="few-query shape: N query rows at the end of the workload's full "
+                         "context (every key visible), timed through the few-query path")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,14 +126,21 @@ def main():
     torch.cuda.set_device(dev)
     log(f"bench: library {dsai.library_path()}")
     t0 = time.perf_counter()
-    inp = gen.generate(args.workload, device=dev)
+    if args.decode:
+        from dataclasses import replace
+        full_T = gen.CONFIGS[args.workload]["T"]
+        inp = gen.generate(args.workload, S=args.decode, T=full_T, device=dev)
+        inp = replace(inp, q_pos0=full_T * inp.m - args.decode, query_chunk=None)
+    else:
+        inp = gen.generate(args.workload, device=dev)
     torch.cuda.synchronize()
     log(f"bench: generated {args.workload} S={inp.S} T={inp.T} H={inp.H} d={inp.d} m={inp.m} "
         f"topk={inp.topk} dtype={inp.dtype} chunk={inp.query_chunk} in "
         f"{time.perf_counter() - t0:.1f} s")
 
     ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
-                      query_chunk=inp.query_chunk or 0, device=dev)
+                      query_chunk=inp.query_chunk or 0,
+                      few_query_rows=max(64, args.decode) if args.decode else 0, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
     idx = torch.empty((inp.S, W), dtype=torch.int32, device=dev)
     vl = torch.empty((inp.S,), dtype=torch.int32, device=dev)
@@ -186,6 +197,27 @@ def main():
         torch.cuda.synchronize()
         log("bench: copy calibration: 1 GiB read + 1 GiB written (neg kernel)")
 
+    workload_name = inp.name if not args.decode else \
+        f"{inp.name} decode: {inp.S} rows at positions {inp.q_pos0}..{inp.q_pos0 + inp.S - 1}"
+    roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": peak,
+                "unit": "TFLOP/s", "frac": achieved_tflops / peak,
+                "traffic": None if traffic is None else traffic,
+                "kernel": "score_select", "flops_per_launch": flops / n_launch,
+                "avg_launch_ms": score_s * 1e3 / n_launch}
+    if args.decode:
+        # Few-query step (dense scoring + one selection block per row): bound
+        # by reading the key set once from HBM.
+        esz = {"bf16": 2, "fp8": 1, "f32": 4}[inp.dtype]
+        W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
+        alg_bytes = (inp.T * inp.d * esz + inp.S * inp.H * inp.d * esz + inp.w.numel() * 4 +
+                     (inp.T * 4 + inp.S * inp.H * 4 if inp.dtype == "fp8" else 0) +
+                     inp.S * (W + 1) * 4)
+        gbs = alg_bytes / score_s / 1e9
+        roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                    "kernel": "few-query step (dense scoring + block select)",
+                    "bytes_per_launch": alg_bytes, "avg_launch_ms": score_s * 1e3,
+                    "mfma_frac": achieved_tflops / peak}
     result = {
         "metric": METRIC,
         "value": triples / (ms_per_step / 1e3),
@@ -199,7 +231,7 @@ def main():
         "vs_baseline": None,
         "dtype": inp.dtype,
         "data": "synthetic (seeded, generated on device; no datasets or weights)",
-        "config": {"workload": inp.name, "S": inp.S, "T": inp.T, "H": inp.H, "d": inp.d,
+        "config": {"workload": workload_name, "S": inp.S, "T": inp.T, "H": inp.H, "d": inp.d,
                    "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
                    inp.query_chunk, "launches_per_step": n_launch, "parallelism": "none (1 GPU)"},
         "queries_per_s": inp.S / (ms_per_step / 1e3),
@@ -207,11 +239,7 @@ def main():
         "score_select_ms": float(np.mean(score_ms)),
         "pair_overlap_ms": float(np.mean(ovl_ms)),
         "peak_hbm_bytes_allocated": int(peak_bytes),
-        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / peak,
-                     "traffic": None if traffic is None else traffic,
-                     "kernel": "score_select", "flops_per_launch": flops / n_launch,
-                     "avg_launch_ms": score_s * 1e3 / n_launch},
+        "roofline": roofline,
         "overlap": {k: st[k] for k in ("mean_overlap", "median_overlap", "mean_jaccard")},
     }
     if not args.no_cpu_baseline:

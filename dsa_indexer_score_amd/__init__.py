@@ -49,17 +49,21 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 class Indexer:
-    """A library handle: element dtype, output mode and query chunk size."""
+    """A library handle: element dtype, output mode, query chunk size and the
+    row count at or below which the few-query path runs (0: the library's
+    default, negative: never)."""
 
     def __init__(self, dtype: torch.dtype, *, expand: bool = False, tail: bool = False,
-                 query_chunk: int = 0, device=None):
+                 query_chunk: int = 0, few_query_rows: int = 0, device=None):
         if dtype not in _DTYPE_CODE:
             raise TypeError(f"unsupported dtype {dtype}")
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
         self.dtype, self.expand, self.tail = dtype, bool(expand), bool(tail)
         self.query_chunk = int(query_chunk or 0)
-        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail), self.query_chunk)
+        self.few_query_rows = int(few_query_rows or 0)
+        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail), self.query_chunk,
+                                 self.few_query_rows)
         h = ctypes.c_void_p()
         lib = _lib.load()
         _lib.check(lib.indexer_create(ctypes.byref(cfg), self.device.index or 0, ctypes.byref(h)),
@@ -131,20 +135,22 @@ class Indexer:
 _HANDLES = {}
 
 
-def _handle(dtype, expand, tail, query_chunk, device) -> Indexer:
-    key = (dtype, bool(expand), bool(tail), int(query_chunk or 0), str(device))
+def _handle(dtype, expand, tail, query_chunk, few_query_rows, device) -> Indexer:
+    key = (dtype, bool(expand), bool(tail), int(query_chunk or 0), int(few_query_rows or 0),
+           str(device))
     h = _HANDLES.get(key)
     if h is None:
         h = _HANDLES[key] = Indexer(dtype, expand=expand, tail=tail, query_chunk=query_chunk,
-                                    device=device)
+                                    few_query_rows=few_query_rows, device=device)
     return h
 
 
 def score_topk(q, w, k, *, m: int = 1, topk: int, causal: bool = True, expand: bool = False,
                tail: bool = False, q_scale=None, k_scale=None, q_pos0: int = 0,
-               query_chunk: int = 0, with_scores: bool = False, workspace=None):
+               query_chunk: int = 0, few_query_rows: int = 0, with_scores: bool = False,
+               workspace=None):
     """One indexer step; see Indexer.score_topk."""
-    return _handle(q.dtype, expand, tail, query_chunk, q.device).score_topk(
+    return _handle(q.dtype, expand, tail, query_chunk, few_query_rows, q.device).score_topk(
         q, w, k, m=m, topk=topk, causal=causal, q_scale=q_scale, k_scale=k_scale,
         q_pos0=q_pos0, with_scores=with_scores, workspace=workspace)
 

@@ -14,7 +14,8 @@ IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EWORKSPACE, IDX_EHIP = 0, -1, -2, -3, 
 
 
 class IndexerConfig(ctypes.Structure):
-    _fields_ = [("dtype", ctypes.c_int), ("flags", ctypes.c_int), ("query_chunk", ctypes.c_int64)]
+    _fields_ = [("dtype", ctypes.c_int), ("flags", ctypes.c_int), ("query_chunk", ctypes.c_int64),
+                ("few_query_rows", ctypes.c_int64)]
 
 
 class OverlapStats(ctypes.Structure):

@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/dsa_indexer.h: argument checks,
 // output-width and workspace arithmetic, the query-chunk loop and launches.
 // Nothing here computes scores or selections; every step of the indexer runs
-// in the HIP kernels (score_select.hip, pair_overlap.hip).
+// in the HIP kernels (score_select.hip, select_dense.hip, pair_overlap.hip).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -68,6 +68,26 @@ int64_t rows_per_launch(const indexer_config &cfg, int64_t S)
     return (cfg.query_chunk > 0 && cfg.query_chunk < S) ? cfg.query_chunk : S;
 }
 
+constexpr int64_t kFewRowsDefault = 64;
+constexpr int64_t kDenseMaxBytes = int64_t(1) << 32;
+constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
+
+int64_t dense_stride(int64_t T) { return round_up(std::max<int64_t>(T, 1), 4); }
+
+// Few-query path: the S rows' visible scores fit a dense workspace.
+bool use_dense(const indexer_config &cfg, int64_t S, int64_t T)
+{
+    const int64_t lim = cfg.few_query_rows == 0 ? kFewRowsDefault : cfg.few_query_rows;
+    return lim > 0 && S <= lim && S * dense_stride(T) * 4 <= kDenseMaxBytes;
+}
+
+int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int64_t ksel,
+                       int64_t pmax)
+{
+    if (use_dense(cfg, S, T)) return S * dense_stride(T) * 4;
+    return rows_per_launch(cfg, S) * capacity(ksel, pmax) * (int64_t)sizeof(uint2);
+}
+
 struct DeviceGuard {
     int prev = -1;
     bool changed = false;
@@ -131,8 +151,7 @@ int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
-    const int64_t rows = rows_per_launch(h->cfg, S);
-    *bytes = (size_t)(rows * capacity(ksel, T) * (int64_t)sizeof(uint2));
+    *bytes = (size_t)workspace_need(h->cfg, S, T, ksel, T);
     return IDX_OK;
 }
 
@@ -173,7 +192,8 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     const int64_t pmax = causal ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
     const int64_t rows = rows_per_launch(cfg, S);
-    const size_t need = (size_t)(rows * cap * (int64_t)sizeof(uint2));
+    const bool dense = use_dense(cfg, S, T);
+    const size_t need = (size_t)workspace_need(cfg, S, T, ksel, pmax);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
 
     DeviceGuard guard(h->device);
@@ -200,13 +220,38 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     p.sel_score = sel_score;
     p.ws = static_cast<uint2 *>(workspace);
     p.cap = (int)cap;
+    p.nsplit = 1;
+    p.split_keys = round_up(std::max<int64_t>(T, 1), dsai::kKeysPerTile);
     const int nb = (H + 31) / 32;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dense) {
+        // Few-query path: all CUs score the rows' key ranges into the dense
+        // workspace, then one block per row selects.
+        p.ws = nullptr;
+        p.scores = static_cast<float *>(workspace);
+        p.sstride = dense_stride(T);
+        p.row0 = 0;
+        p.nrows = S;
+        const int64_t groups = (S + dsai::kQueriesPerBlock - 1) / dsai::kQueriesPerBlock;
+        const int64_t tiles = (std::max<int64_t>(pmax, 1) + dsai::kKeysPerTile - 1) /
+                              dsai::kKeysPerTile;
+        const int64_t want = std::max<int64_t>(1, (kFillBlocks + groups - 1) / groups);
+        const int64_t tiles_per = (tiles + std::min(want, tiles) - 1) / std::min(want, tiles);
+        p.split_keys = tiles_per * dsai::kKeysPerTile;
+        p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
+        bool supported = true;
+        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, true, p, st, &supported);
+        if (!supported) return IDX_EUNSUPPORTED;
+        if (e != hipSuccess) return fail_hip(e);
+        e = dsai::launch_select_dense(p, st);
+        if (e != hipSuccess) return fail_hip(e);
+        return IDX_OK;
+    }
     for (int64_t r0 = 0; r0 < S; r0 += rows) {
         p.row0 = r0;
         p.nrows = std::min(rows, S - r0);
         bool supported = true;
-        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, p,
-                                                 static_cast<hipStream_t>(stream), &supported);
+        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, false, p, st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
     }

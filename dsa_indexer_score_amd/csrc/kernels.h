@@ -29,15 +29,26 @@ struct ScoreSelectParams {
     float *sel_score;       // [S, W] or null
     uint2 *ws;              // candidate buffers, [nrows, cap] of (score bits, key)
     int cap;                // candidate slots per query
+    // Dense mode (few queries): scores of each row's visible keys are written
+    // to scores[row * sstride + key] instead of being selected in the kernel.
+    float *scores;
+    int64_t sstride;
+    int nsplit;             // key ranges per query group; grid = groups * nsplit
+    int64_t split_keys;     // keys per range, a multiple of kKeysPerTile
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
 constexpr int kKeysPerTile = 128;     // keys staged in LDS per step
 constexpr int kSelGroup = 64;         // keys appended per selection step (one per lane)
 
-// dtype codes match enum idx_dtype
-hipError_t launch_score_select(int dtype, int nb, int d, const ScoreSelectParams &p,
+// dtype codes match enum idx_dtype; dense = write scores (p.scores) instead
+// of selecting
+hipError_t launch_score_select(int dtype, int nb, int d, bool dense, const ScoreSelectParams &p,
                                hipStream_t stream, bool *supported);
+
+// Exact top-k of each row's dense scores (one block per row) and its
+// canonical output row.
+hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream);
 
 hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t npairs,
                                int W, int32_t *shared, hipStream_t stream);

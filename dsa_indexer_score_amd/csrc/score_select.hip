@@ -63,6 +63,7 @@
 //    pools expand to m positions and the incomplete tail follows
 //    (GLM-5.3-Flash Module 06 "DSA & KPool", section 2), then -1 padding.
 #include "kernels.h"
+#include "select_common.h"
 
 namespace dsai {
 namespace {
@@ -71,59 +72,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = kQueriesPerBlock * 64;
-
-__device__ __forceinline__ uint32_t ord_code(uint32_t bits)
-{
-    if (bits == 0x80000000u) bits = 0;  // -0 -> +0
-    return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-}
-
-__device__ __forceinline__ int lane_rank(uint64_t mask)
-{
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// Inclusive prefix sum over the 64 lanes (lane 0 first), in registers:
-// Hillis-Steele steps within each 16-lane row, then the row totals.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
-{
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return x;
-}
-
-__device__ __forceinline__ uint32_t lane_value(uint32_t x, int l)
-{
-    return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
-}
-
-// Smallest float value whose order code is >= c: s >= code_floor_value(c)
-// holds exactly when ord_code(s) >= c, for every finite s.
-__device__ __forceinline__ float code_floor_value(uint32_t c)
-{
-    if (c >= 0x80000000u) return __uint_as_float(c & 0x7FFFFFFFu);
-    if (c >= 0x007FFFFFu) return __uint_as_float(~c);
-    return -__builtin_inff();
-}
-
-// Wait for this wave's outstanding LDS and global accesses.
-__device__ __forceinline__ void wave_sync_mem()
-{
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ int64_t visible_keys(int64_t pos, int64_t T, int m, int causal)
-{
-    if (!causal) return T;
-    int64_t c = (pos + 1) / m;
-    return c < T ? c : T;
-}
 
 // ---------------------------------------------------------------------------
 // MFMA operand handling.  For every dtype, lane (hh = lane / 32, r = lane % 32)
@@ -241,231 +189,7 @@ template <int D> struct Op<0, D> {  // fp32
     __device__ static A zero() { return 0.f; }
 };
 
-// ---------------------------------------------------------------------------
-// Selection helpers (one wave, one query).  Codes are cut in three radix
-// levels: the top kB1 = 12 bits (the running histogram), then 10 and 10.
-// `hist` holds kHistWords dwords of packed 16-bit counters (4096 bins); the
-// 10-bit levels use the first 512 dwords.
-// ---------------------------------------------------------------------------
-constexpr int kB1 = 12;                         // bits of the running histogram
-constexpr int kBins1 = 1 << kB1;
-constexpr int kShift1 = 32 - kB1;               // bin of a code: u >> kShift1
-constexpr int kHistWords = kBins1 / 2;
-
-__device__ __forceinline__ void hist_clear(uint32_t *hist, int lane)
-{
-#pragma unroll
-    for (int i = 0; i < kHistWords / 64; ++i) hist[lane + 64 * i] = 0;
-}
-
-__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t bin)
-{
-    atomicAdd(&hist[bin >> 1], 1u << ((bin & 1u) * 16));
-}
-
-__device__ __forceinline__ int hist_get(const uint32_t *hist, int bin)
-{
-    const uint32_t x = hist[bin >> 1];
-    return (int)((bin & 1) ? (x >> 16) : (x & 0xFFFFu));
-}
-
-// Bin b with (count above b) < need <= (count above b) + h[b]; needs total >= need >= 1.
-// Two lane-parallel levels: per-lane sums of nbins/64 bins with a suffix scan
-// across lanes give the owning range, then one bin per lane inside it.
-__device__ void find_boundary(const uint32_t *hist, int nbins, int need, int lane, int &b_out,
-                              int &above_out, int &hb_out)
-{
-    const int per = nbins / 64, dpl = per / 2;
-    // lane i sums range 63 - i of the bins, so a prefix over lanes is a
-    // suffix over ranges (counted from the top bins down)
-    const int ri = 63 - lane;
-    uint32_t sum = 0;
-    for (int i = 0; i < dpl; ++i) {
-        uint32_t x = hist[ri * dpl + i];
-        sum += (x & 0xFFFFu) + (x >> 16);
-    }
-    const uint32_t incl = wave_incl_scan(sum);
-    const uint32_t excl = incl - sum;
-    const uint64_t bm = __ballot(incl >= (uint32_t)need && excl < (uint32_t)need);
-    int L0 = __ffsll((unsigned long long)bm) - 1;
-    if (L0 < 0) L0 = 0;  // unreachable while the histogram matches the buffer
-    const int owner = 63 - L0;
-    const uint32_t base = lane_value(excl, L0);  // count above the owner's range
-    // lane i < per takes bin owner*per + per-1-i (descending); inclusive prefix
-    const int bin = owner * per + per - 1 - lane;
-    const uint32_t h = lane < per ? (uint32_t)hist_get(hist, bin) : 0u;
-    const uint32_t incl2 = wave_incl_scan(h);
-    const uint64_t hit = __ballot(lane < per && base + incl2 >= (uint32_t)need);
-    int L = __ffsll((unsigned long long)hit) - 1;
-    if (L < 0) L = 0;
-    b_out = owner * per + per - 1 - L;
-    hb_out = (int)lane_value(h, L);
-    above_out = (int)(base + lane_value(incl2, L) - (uint32_t)hb_out);
-}
-
-// Raise the running boundary bin tb (above = count in bins > tb) until
-// above < need, 64 bins per step: lane i looks at bin tb + 1 + i, and the
-// first lane whose inclusive prefix brings `above` below `need` is the new tb.
-// Long runs of empty bins (e.g. all tiny magnitudes between -eps and +eps)
-// cost one step per 64 bins.
-__device__ void advance_boundary(const uint32_t *hist, int need, int lane, int &tb, int &above)
-{
-    while (above >= need) {
-        const int b = tb + 1 + lane;
-        const int incl = (int)wave_incl_scan(b < kBins1 ? (uint32_t)hist_get(hist, b) : 0u);
-        const uint64_t ok = __ballot(above - incl < need);
-        if (ok) {
-            const int L = __ffsll((unsigned long long)ok) - 1;
-            tb += 1 + L;
-            above -= (int)lane_value((uint32_t)incl, L);
-            return;
-        }
-        tb += 64;
-        above -= (int)lane_value((uint32_t)incl, 63);
-    }
-}
-
-// Visit buf[0, cnt) in buffer order, kBatch chunks of 64 entries at a time:
-// all loads of a batch are issued before any of them is consumed, so a pass
-// costs a few memory round trips per 512 entries instead of one per 64.  The
-// callback may store into buf at or below the entry it was given (in-place
-// compaction): later batches are read before those positions are reached.
-constexpr int kBatch = 8;
-template <class F>
-__device__ __forceinline__ void for_each_entry(const uint2 *buf, int cnt, int lane, F &&f)
-{
-    for (int base = 0; base < cnt; base += 64 * kBatch) {
-        uint2 v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int e = base + i * 64 + lane;
-            v[i] = e < cnt ? buf[e] : make_uint2(0u, 0u);
-        }
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) f(base + i * 64 + lane < cnt, v[i]);
-    }
-}
-
-struct Cut {
-    uint32_t tc;  // keep u >= tc (exact == 0) or u > tc plus the first need_eq of u == tc
-    int exact;
-    int need_eq;
-};
-
-// Levels 2 and 3 of the radix cut: `src(f)` feeds every candidate code of the
-// level-1 boundary bin b1 to f (from the buffer or from an LDS gather), a1 is
-// the count above b1.  Returns the cut that keeps exactly `need` entries.
-template <class Src>
-__device__ Cut refine_cut(Src &&src, int need, int b1, int a1, uint32_t *hist, int lane)
-{
-    Cut c;
-    wave_sync_mem();
-    hist_clear(hist, lane);
-    wave_sync_mem();
-    src([&](uint32_t u) { hist_add(hist, (u >> 10) & 1023u); });
-    wave_sync_mem();
-    int b2, a2, h2;
-    find_boundary(hist, 1024, need - a1, lane, b2, a2, h2);
-    const int above = a1 + a2;
-    const uint32_t pre = ((uint32_t)b1 << 10) | (uint32_t)b2;  // top 22 bits
-    if (above + h2 == need) {
-        c.tc = pre << 10;
-        c.exact = 0;
-        c.need_eq = 0;
-        return c;
-    }
-    wave_sync_mem();
-    hist_clear(hist, lane);
-    wave_sync_mem();
-    src([&](uint32_t u) {
-        if ((u >> 10) == pre) hist_add(hist, u & 1023u);
-    });
-    wave_sync_mem();
-    int b3, a3, h3;
-    find_boundary(hist, 1024, need - above, lane, b3, a3, h3);
-    c.tc = (pre << 10) | (uint32_t)b3;
-    c.exact = 1;
-    c.need_eq = need - above - a3;
-    return c;
-}
-
-// Cut that keeps at least `need` of the buffer's best entries.  With
-// allow_approx, a level-1 bin edge is accepted when it keeps at most
-// `approx_limit` entries; otherwise the cut is exact (keeps exactly `need`).
-__device__ Cut choose_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, bool allow_approx,
-                          int approx_limit, int lane)
-{
-    int b1, a1, h1;
-    find_boundary(hist, kBins1, need, lane, b1, a1, h1);
-    if ((allow_approx && a1 + h1 <= approx_limit) || a1 + h1 == need) {
-        Cut c;
-        c.tc = (uint32_t)b1 << kShift1;
-        c.exact = 0;
-        c.need_eq = 0;
-        return c;
-    }
-    auto src = [&](auto &&f) {
-        for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
-            const uint32_t u = ord_code(v.x);
-            if (valid && (u >> kShift1) == (uint32_t)b1) f(u);
-        });
-    };
-    return refine_cut(src, need, b1, a1, hist, lane);
-}
-
-// Exact cut for the final selection: the codes of the level-1 boundary bin
-// are gathered (one batched pass, buffer order) into `gather` (LDS, gcap
-// entries) and refined there; a bin larger than gcap refines from the buffer.
-__device__ Cut final_cut(const uint2 *buf, int cnt, int need, uint32_t *hist, uint32_t *gather,
-                         int gcap, int lane)
-{
-    int b1, a1, h1;
-    find_boundary(hist, kBins1, need, lane, b1, a1, h1);
-    if (a1 + h1 == need || h1 > gcap) return choose_cut(buf, cnt, need, hist, false, 0, lane);
-    int gcnt = 0;
-    for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
-        const uint32_t u = ord_code(v.x);
-        const bool in = valid && (u >> kShift1) == (uint32_t)b1;
-        const uint64_t m = __ballot(in);
-        if (in) gather[gcnt + lane_rank(m)] = u;
-        gcnt += __popcll(m);
-    });
-    auto src = [&](auto &&f) {
-        for (int i = lane; i < gcnt; i += 64) f(gather[i]);
-    };
-    return refine_cut(src, need, b1, a1, hist, lane);
-}
-
-// Stable in-place compaction of buf[0, cnt) under `cut`; rebuilds the histogram.
-__device__ void compact(uint2 *buf, int &cnt, const Cut &cut, uint32_t *hist, int lane)
-{
-    wave_sync_mem();
-    hist_clear(hist, lane);
-    wave_sync_mem();
-    int wcnt = 0, eqseen = 0;
-    for_each_entry(buf, cnt, lane, [&](bool valid, uint2 v) {
-        const uint32_t u = ord_code(v.x);
-        bool keep;
-        if (cut.exact) {
-            const bool eq = valid && u == cut.tc;
-            const uint64_t em = __ballot(eq);
-            keep = valid && (u > cut.tc || (eq && eqseen + lane_rank(em) < cut.need_eq));
-            eqseen += __popcll(em);
-        } else {
-            keep = valid && u >= cut.tc;
-        }
-        const uint64_t km = __ballot(keep);
-        if (keep) {
-            buf[wcnt + lane_rank(km)] = v;
-            hist_add(hist, u >> kShift1);
-        }
-        wcnt += __popcll(km);
-    });
-    cnt = wcnt;
-    wave_sync_mem();
-}
-
-template <int DT, int NB, int D>
+template <int DT, int NB, int D, bool DENSE>
 __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectParams p)
 {
     using O = Op<DT, D>;
@@ -484,7 +208,10 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = lane >> 5, l32 = lane & 31;
     const int64_t ngroups = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock;
-    const int64_t grp = ngroups - 1 - (int64_t)blockIdx.x;  // heaviest rows first
+    // dense mode: block = (query group, key range); streaming: one range
+    const int64_t gi = DENSE ? (int64_t)blockIdx.x / p.nsplit : (int64_t)blockIdx.x;
+    const int sp = DENSE ? (int)((int64_t)blockIdx.x - gi * p.nsplit) : 0;
+    const int64_t grp = ngroups - 1 - gi;  // heaviest rows first
     const int64_t qrow = grp * kQueriesPerBlock + wave;
     const bool active = qrow < p.nrows;
     const int64_t t = p.row0 + qrow;
@@ -493,10 +220,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     int64_t last = grp * kQueriesPerBlock + kQueriesPerBlock - 1;
     if (last > p.nrows - 1) last = p.nrows - 1;
     const int64_t Pblk = visible_keys(p.q_pos0 + p.row0 + last, p.T, p.m, p.causal);
-    const int ntiles = (int)((Pblk + kKeysPerTile - 1) / kKeysPerTile);
+    const int64_t kbeg = DENSE ? (int64_t)sp * p.split_keys : 0;
+    const int64_t kend = DENSE && kbeg + p.split_keys < Pblk ? kbeg + p.split_keys : Pblk;
+    const int ntiles = kend > kbeg ? (int)((kend - kbeg + kKeysPerTile - 1) / kKeysPerTile) : 0;
 
     uint32_t *hist = hist_all[wave];
-    hist_clear(hist, lane);
+    if (!DENSE) hist_clear(hist, lane);
 
     // q fragments and folded head weights of this wave's query
     A qa[NB][KS];
@@ -523,7 +252,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         }
     }
 
-    uint2 *buf = p.ws + (active ? qrow : 0) * (int64_t)p.cap;
+    uint2 *buf = p.ws + (active && !DENSE ? qrow : 0) * (int64_t)p.cap;
     int cnt = 0;
     uint32_t tau = 0;        // pass iff code >= tau
     float tau_f = -__builtin_inff();  // the same test on the float score
@@ -535,7 +264,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     uint4 stage[CPT];
     float ksc = 0.f;
     auto load_tile = [&](int it) {
-        const int64_t j0 = (int64_t)it * kKeysPerTile;
+        const int64_t j0 = kbeg + (int64_t)it * kKeysPerTile;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int id = threadIdx.x + c * kThreads;
@@ -573,6 +302,15 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     constexpr int NCB = kKeysPerTile / 32;  // 32-key column blocks per tile
     constexpr int NG = NCB / 2;             // 64-key selection groups per tile
     auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
+        if constexpr (DENSE) {
+            float *srow = p.scores + qrow * p.sstride;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int64_t key = j0 + g * kSelGroup + lane;
+                if (key < Pq) srow[key] = sg[g];
+            }
+            return;
+        }
         const bool full = j0 + kKeysPerTile <= Pq;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -622,13 +360,13 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // opposite ends of a tile: waves 0-3 right after their MFMA/epilogue work,
     // waves 4-7 one tile later, before their MFMAs -- so one wave's branchy
     // selection code always has the other wave's MFMAs to overlap with.
-    const bool lagged = wave >= kQueriesPerBlock / 2;
+    const bool lagged = !DENSE && wave >= kQueriesPerBlock / 2;
     float pend[NG];
     int64_t pend_j0 = -1;
 
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
-        const int64_t j0 = (int64_t)it * kKeysPerTile;
+        const int64_t j0 = kbeg + (int64_t)it * kKeysPerTile;
         if (it + 1 < ntiles) load_tile(it + 1);
 
         if (lagged && pend_j0 >= 0) {
@@ -701,7 +439,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     }
     if (pend_j0 >= 0) select_tile(pend, pend_j0);
 
-    if (!active) return;
+    if (!active || DENSE) return;
 
     // ---- exact final selection, written straight into the output row ----
     // The K tiles are idle after the last barrier: each wave borrows a slice
@@ -751,24 +489,34 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     if (lane == 0) p.valid_len[t] = body + tl;
 }
 
-template <int DT, int NB, int D>
+template <int DT, int NB, int D, bool DENSE>
 hipError_t launch_one(const ScoreSelectParams &p, hipStream_t stream)
 {
-    const int64_t blocks = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock;
+    const int64_t blocks = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock * p.nsplit;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((score_select_kernel<DT, NB, D>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, DENSE>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int DT, int NB, int D>
+hipError_t launch_mode(bool dense, const ScoreSelectParams &p, hipStream_t stream)
+{
+    return dense ? launch_one<DT, NB, D, true>(p, stream) : launch_one<DT, NB, D, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_select(int dtype, int nb, int d, const ScoreSelectParams &p,
+hipError_t launch_score_select(int dtype, int nb, int d, bool dense, const ScoreSelectParams &p,
                                hipStream_t stream, bool *supported)
 {
     *supported = true;
+    if (p.nsplit < 1 || p.split_keys < kKeysPerTile || p.split_keys % kKeysPerTile) {
+        *supported = false;
+        return hipSuccess;
+    }
 #define DSAI_CASE(DT, NB, D) \
-    if (dtype == DT && nb == NB && d == D) return launch_one<DT, NB, D>(p, stream);
+    if (dtype == DT && nb == NB && d == D) return launch_mode<DT, NB, D>(dense, p, stream);
     DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
     DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
     DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)

@@ -1,0 +1,377 @@
+// select_dense: exact top-k of a few queries' materialised scores.
+//
+// For a handful of query rows (decode, small batches against a long key
+// set) the scoring kernel runs in its dense mode and writes each row's
+// visible scores to the workspace (a [rows, T] array: kilobytes to tens of
+// megabytes here, never the prefill-sized tensor).  This kernel then gives
+// every row one 1024-thread block and finds the same exact result as the
+// streaming selection -- the Ksel best keys under the total order (higher
+// score first, equal scores to the lower key index, DoSA summary,
+// "Prerequisites") written in ascending key order ("Adjacent-Query KV-Index
+// Overlap in 256K DSA Training", section 3), expanded and followed by the
+// tail (GLM-5.3-Flash Module 06 "DSA & KPool", section 2):
+//  1. candidates: a sample of the row (128 blocks of 64 keys) gives an
+//     estimated threshold a little below the expected Ksel-th score; one
+//     pass keeps every key at or above it, in key order, in an LDS list.  The
+//     true selection is contained in that list whenever the list holds at
+//     least Ksel keys (all of them are >= the estimate, so the Ksel-th best
+//     is too); otherwise -- or if the list overflows, e.g. under massive
+//     ties -- the steps below run over the full row instead;
+//  2. exact cut: a 4096-bin histogram of the order codes' top 12 bits gives
+//     the bin holding the Ksel-th code; if that bin does not end the
+//     selection exactly, two more 10-bit histograms over the codes of that
+//     bin give the exact Ksel-th code c and how many entries equal to c are
+//     kept;
+//  3. ordered output: a block-wide prefix count of entries above c and of
+//     entries equal to c (packed into one 32-bit scan) gives each kept key
+//     its output slot, so ties go to the lowest keys.
+// Passes over the row read chunks of 16K keys, 16 consecutive keys per
+// thread loaded as four 16-byte vectors, so each thread has its loads in
+// flight together; no pass over the row uses atomics.
+#include "kernels.h"
+#include "select_common.h"
+
+namespace dsai {
+namespace {
+
+constexpr int kDenseThreads = 1024;
+constexpr int kDenseWaves = kDenseThreads / 64;
+constexpr int kPer = 16;                        // consecutive keys per thread per chunk
+constexpr int kChunk = kDenseThreads * kPer;    // keys per chunk
+
+// The KP consecutive scores of this thread's slice of chunk `base` (raw
+// bits); all loads are issued before any is used.
+template <int KP>
+struct SliceT {
+    uint32_t bits[KP];
+    __device__ void load(const uint32_t *sc, int base, int n)
+    {
+        const int j0 = base + (int)threadIdx.x * KP;
+        if (j0 + KP <= n) {
+            const uint4 *v = reinterpret_cast<const uint4 *>(sc + j0);
+#pragma unroll
+            for (int i = 0; i < KP / 4; ++i) {
+                const uint4 x = v[i];
+                bits[4 * i] = x.x;
+                bits[4 * i + 1] = x.y;
+                bits[4 * i + 2] = x.z;
+                bits[4 * i + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < KP; ++i) bits[i] = j0 + i < n ? sc[j0 + i] : 0u;
+        }
+    }
+};
+using Slice = SliceT<kPer>;
+
+// Exclusive prefix sum over the block's threads (thread order) and its total.
+__device__ uint32_t block_excl_scan(uint32_t x, uint32_t *red, uint32_t &total)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t incl = wave_incl_scan(x);
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kDenseWaves; ++i) {
+        const uint32_t v = red[i];
+        off += i < wave ? v : 0u;
+        tot += v;
+    }
+    __syncthreads();
+    total = tot;
+    return off + incl - x;
+}
+
+// Bin b of hist[0, nbins) with (count above b) < need <= (count above b) +
+// hist[b], for 1 <= need <= total.  Thread i owns nbins/1024 consecutive bins
+// counted down from the top, so a prefix over threads is a suffix over bins.
+__device__ void block_boundary(const uint32_t *hist, int nbins, uint32_t need, uint32_t *red,
+                               uint32_t *res, int &b, uint32_t &above, uint32_t &hb)
+{
+    const int per = nbins / kDenseThreads;
+    const int top = nbins - 1 - (int)threadIdx.x * per;
+    uint32_t s = 0;
+    for (int i = 0; i < per; ++i) s += hist[top - i];
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(s, red, tot);
+    if (ex < need && ex + s >= need) {  // exactly one thread
+        uint32_t acc = ex;
+        for (int i = 0; i < per; ++i) {
+            const uint32_t h = hist[top - i];
+            if (acc + h >= need) {
+                res[0] = (uint32_t)(top - i);
+                res[1] = acc;
+                res[2] = h;
+                break;
+            }
+            acc += h;
+        }
+    }
+    __syncthreads();
+    b = (int)res[0];
+    above = res[1];
+    hb = res[2];
+    __syncthreads();
+}
+
+// Exact cut keeping `need` of the codes that src(f) feeds to f (each thread
+// feeds its own share): keep codes > tc plus the first need_eq codes equal
+// to tc in key order (exact), or every code >= tc.  1 <= need <= count.
+template <class Src>
+__device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32_t *red,
+                                uint32_t *res, uint32_t &tc, bool &exact, uint32_t &need_eq)
+{
+    exact = false;
+    need_eq = 0;
+    for (int i = threadIdx.x; i < kBins1; i += kDenseThreads) hist[i] = 0;
+    __syncthreads();
+    src([&](uint32_t u) { atomicAdd(&hist[u >> kShift1], 1u); });
+    __syncthreads();
+    int b1;
+    uint32_t a1, h1;
+    block_boundary(hist, kBins1, need, red, res, b1, a1, h1);
+    if (a1 + h1 == need) {
+        tc = (uint32_t)b1 << kShift1;
+        return;
+    }
+    for (int i = threadIdx.x; i < 1024; i += kDenseThreads) hist[i] = 0;
+    __syncthreads();
+    src([&](uint32_t u) {
+        if ((u >> kShift1) == (uint32_t)b1) atomicAdd(&hist[(u >> 10) & 1023u], 1u);
+    });
+    __syncthreads();
+    int b2;
+    uint32_t a2, h2;
+    block_boundary(hist, 1024, need - a1, red, res, b2, a2, h2);
+    const uint32_t pre = ((uint32_t)b1 << 10) | (uint32_t)b2;  // top 22 bits
+    const uint32_t above = a1 + a2;
+    if (above + h2 == need) {
+        tc = pre << 10;
+        return;
+    }
+    for (int i = threadIdx.x; i < 1024; i += kDenseThreads) hist[i] = 0;
+    __syncthreads();
+    src([&](uint32_t u) {
+        if ((u >> 10) == pre) atomicAdd(&hist[u & 1023u], 1u);
+    });
+    __syncthreads();
+    int b3;
+    uint32_t a3, h3;
+    block_boundary(hist, 1024, need - above, red, res, b3, a3, h3);
+    tc = (pre << 10) | (uint32_t)b3;
+    exact = true;
+    need_eq = need - above - a3;
+}
+
+// Output slots of one thread's consecutive entries under a cut: counts of
+// entries above / equal to the cut before this thread (block-wide, plus the
+// running totals of earlier rounds), then each kept entry's slot in order.
+struct CutCounter {
+    uint32_t tc, need_eq;
+    bool exact;
+    uint32_t gt_run = 0, eq_run = 0;
+    __device__ bool gt(bool valid, uint32_t u) const { return valid && (exact ? u > tc : u >= tc); }
+    __device__ bool eq(bool valid, uint32_t u) const { return valid && exact && u == tc; }
+    __device__ uint32_t kept() const { return gt_run + (eq_run < need_eq ? eq_run : need_eq); }
+};
+
+__global__ void __launch_bounds__(kDenseThreads) select_dense_kernel(ScoreSelectParams p)
+{
+    constexpr int kCap = 8192;           // candidate list (LDS), also the sample size
+    constexpr int kSampleBlock = 64;     // consecutive keys per sample block
+    __shared__ uint32_t hist[kBins1];
+    __shared__ uint32_t ccode[kCap];
+    __shared__ int32_t ckey[kCap];
+    __shared__ uint32_t red[kDenseWaves];
+    __shared__ uint32_t res[3];
+
+    const int64_t qrow = blockIdx.x;
+    const int64_t t = p.row0 + qrow;
+    const int64_t pos = p.q_pos0 + t;
+    const int64_t P = visible_keys(pos, p.T, p.m, p.causal);
+    const int n = (int)P;
+    const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scores + qrow * p.sstride);
+    const uint32_t need = (uint32_t)(n < p.ksel ? n : p.ksel);
+    const int mexp = p.expand ? p.m : 1;
+    int32_t *orow = p.idx + t * (int64_t)p.W;
+    float *srow = p.sel_score ? p.sel_score + t * (int64_t)p.W : nullptr;
+
+    auto row_src = [&](auto &&f) {  // every visible score of the row, from memory
+        for (int base = 0; base < n; base += kChunk) {
+            Slice sl;
+            sl.load(sc, base, n);
+            const int j0 = base + (int)threadIdx.x * kPer;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+                if (j0 + i < n) f(ord_code(sl.bits[i]));
+        }
+    };
+
+    // ---- candidate list: every visible key whose code is >= an estimated
+    // threshold, in key order.  The estimate is the c-th best code of a
+    // sample of 128 blocks of 64 keys spread over the row, with c about 1.5x
+    // the sample's expected share of the selection plus a margin, so the
+    // list almost always holds the whole selection and fits in LDS.  When
+    // the row itself fits, every key is a candidate.
+    int ncand = -1;  // -1: the list is not usable, select from the full row
+    if (n <= kCap) {
+        for (int i = threadIdx.x; i < n; i += kDenseThreads) {
+            ccode[i] = ord_code(sc[i]);
+            ckey[i] = i;
+        }
+        ncand = n;
+        __syncthreads();
+    } else {
+        const uint32_t c = (uint32_t)((3ull * need * kCap) / (2ull * (uint64_t)n)) + 8u;
+        if (c <= (uint32_t)kCap) {
+            const int spacing = (n - kSampleBlock) / (kCap / kSampleBlock - 1);
+            for (int s = threadIdx.x; s < kCap; s += kDenseThreads) {
+                const int key = (s / kSampleBlock) * spacing + s % kSampleBlock;
+                ccode[s] = ord_code(sc[key]);
+            }
+            __syncthreads();
+            uint32_t est, est_eq;
+            bool est_exact;
+            block_exact_cut(
+                [&](auto &&f) {
+                    for (int i = threadIdx.x; i < kCap; i += kDenseThreads) f(ccode[i]);
+                },
+                c, hist, red, res, est, est_exact, est_eq);
+            __syncthreads();  // the sample is dead from here on
+            // one pass over the row; the next chunk's loads are issued before
+            // this chunk is compacted
+            uint32_t total = 0;
+            Slice nxt;
+            nxt.load(sc, 0, n);
+            for (int base = 0; base < n; base += kChunk) {
+                const Slice sl = nxt;
+                if (base + kChunk < n) nxt.load(sc, base + kChunk, n);
+                const int j0 = base + (int)threadIdx.x * kPer;
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i)
+                    cnt += (j0 + i < n && ord_code(sl.bits[i]) >= est) ? 1u : 0u;
+                uint32_t tot;
+                uint32_t o = total + block_excl_scan(cnt, red, tot);
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const uint32_t u = ord_code(sl.bits[i]);
+                    if (j0 + i < n && u >= est) {
+                        if (o < (uint32_t)kCap) {
+                            ccode[o] = u;
+                            ckey[o] = j0 + i;
+                        }
+                        ++o;
+                    }
+                }
+                total += tot;
+            }
+            __syncthreads();
+            if (total >= need && total <= (uint32_t)kCap) ncand = (int)total;
+        }
+    }
+
+    CutCounter cc;
+    cc.tc = 0;
+    cc.exact = false;
+    cc.need_eq = 0;
+    if (ncand >= 0) {
+        // ---- exact selection within the list, then its ordered output
+        if ((uint32_t)ncand > need)
+            block_exact_cut(
+                [&](auto &&f) {
+                    for (int i = threadIdx.x; i < ncand; i += kDenseThreads) f(ccode[i]);
+                },
+                need, hist, red, res, cc.tc, cc.exact, cc.need_eq);
+        constexpr int kPerC = kCap / kDenseThreads;
+        const int i0 = (int)threadIdx.x * kPerC;
+        uint32_t ngt = 0, neq = 0;
+#pragma unroll
+        for (int i = 0; i < kPerC; ++i) {
+            const bool valid = i0 + i < ncand;
+            const uint32_t u = valid ? ccode[i0 + i] : 0u;
+            ngt += cc.gt(valid, u) ? 1u : 0u;
+            neq += cc.eq(valid, u) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(ngt | (neq << 16), red, tot);
+        uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
+#pragma unroll
+        for (int i = 0; i < kPerC; ++i) {
+            const bool valid = i0 + i < ncand;
+            const uint32_t u = valid ? ccode[i0 + i] : 0u;
+            const bool gt = cc.gt(valid, u), eq = cc.eq(valid, u);
+            if (gt || (eq && eq_before < cc.need_eq)) {
+                const uint32_t kb = gt_before + (eq_before < cc.need_eq ? eq_before : cc.need_eq);
+                const int key = ckey[i0 + i];
+                for (int x = 0; x < mexp; ++x) {
+                    orow[(int)kb * mexp + x] = key * mexp + x;
+                    if (srow) srow[(int)kb * mexp + x] = __uint_as_float(sc[key]);
+                }
+            }
+            gt_before += gt ? 1u : 0u;
+            eq_before += eq ? 1u : 0u;
+        }
+        cc.gt_run = tot & 0xFFFFu;
+        cc.eq_run = tot >> 16;
+    } else {
+        // ---- fallback: radix passes and the ordered output over the full row
+        if ((uint32_t)n > need) block_exact_cut(row_src, need, hist, red, res, cc.tc, cc.exact,
+                                                cc.need_eq);
+        for (int base = 0; base < n; base += kChunk) {
+            Slice sl;
+            sl.load(sc, base, n);
+            const int j0 = base + (int)threadIdx.x * kPer;
+            uint32_t ngt = 0, neq = 0;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint32_t u = ord_code(sl.bits[i]);
+                ngt += cc.gt(j0 + i < n, u) ? 1u : 0u;
+                neq += cc.eq(j0 + i < n, u) ? 1u : 0u;
+            }
+            uint32_t tot;
+            const uint32_t ex = block_excl_scan(ngt | (neq << 16), red, tot);
+            uint32_t gt_before = cc.gt_run + (ex & 0xFFFFu);
+            uint32_t eq_before = cc.eq_run + (ex >> 16);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint32_t u = ord_code(sl.bits[i]);
+                const bool gt = cc.gt(j0 + i < n, u), eq = cc.eq(j0 + i < n, u);
+                if (gt || (eq && eq_before < cc.need_eq)) {
+                    const uint32_t kb =
+                        gt_before + (eq_before < cc.need_eq ? eq_before : cc.need_eq);
+                    for (int x = 0; x < mexp; ++x) {
+                        orow[(int)kb * mexp + x] = (j0 + i) * mexp + x;
+                        if (srow) srow[(int)kb * mexp + x] = __uint_as_float(sl.bits[i]);
+                    }
+                }
+                gt_before += gt ? 1u : 0u;
+                eq_before += eq ? 1u : 0u;
+            }
+            cc.gt_run += tot & 0xFFFFu;
+            cc.eq_run += tot >> 16;
+        }
+    }
+
+    const int body = (int)cc.kept() * mexp;
+    const int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - P * p.m) : 0;
+    for (int s = body + (int)threadIdx.x; s < p.W; s += kDenseThreads) {
+        orow[s] = s < body + tl ? (int32_t)(P * p.m + (s - body)) : -1;
+        if (srow) srow[s] = 0.f;
+    }
+    if (threadIdx.x == 0) p.valid_len[t] = body + tl;
+}
+
+}  // namespace
+
+hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream)
+{
+    if (p.nrows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(select_dense_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+}  // namespace dsai

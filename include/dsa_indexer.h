@@ -68,6 +68,14 @@ typedef struct {
     int dtype;           /* enum idx_dtype                                     */
     int flags;           /* IDX_EXPAND | IDX_TAIL                              */
     int64_t query_chunk; /* queries per launch (bounds the workspace); 0 = all */
+    /* Few-query path (decode, small batches against a long key set): when
+     * S <= few_query_rows, every visible score of the S rows is written to
+     * the workspace by all CUs and each row is then selected by one block;
+     * otherwise rows are scored and selected in one streaming pass per query
+     * chunk.  0 = default (64); negative = never.  Both paths give identical
+     * results.  The dense workspace (S * T * 4 bytes, T rounded up to 4) is
+     * used only while it stays within 4 GiB. */
+    int64_t few_query_rows;
 } indexer_config;
 
 /* Limits of this build (IDX_EUNSUPPORTED outside them):
@@ -88,8 +96,9 @@ int indexer_destroy(indexer_t h);
 int indexer_output_width(int topk, int m, int flags, int *W);
 
 /* Device workspace bytes that indexer_score_topk needs for this problem
- * with this handle (per-query candidate buffers for one query chunk).
- * Host-only; depends on min(S, query_chunk), T, m, topk and the flags. */
+ * with this handle: per-query candidate buffers for one query chunk, or the
+ * dense score rows of the few-query path.  Host-only; depends on S,
+ * query_chunk, few_query_rows, T, m, topk and the flags. */
 int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int m, int topk,
                             size_t *bytes);
 

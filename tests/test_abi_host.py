@@ -49,10 +49,10 @@ def test_output_width_matches_oracle_arithmetic():
     assert lib.indexer_output_width(0, 4, 0, ctypes.byref(W)) == _lib.IDX_EINVAL
 
 
-def _handle(dtype=_lib.IDX_BF16, flags=0, chunk=0):
+def _handle(dtype=_lib.IDX_BF16, flags=0, chunk=0, few=0):
     lib = _lib.load()
     h = ctypes.c_void_p()
-    cfg = _lib.IndexerConfig(dtype, flags, chunk)
+    cfg = _lib.IndexerConfig(dtype, flags, chunk, few)
     assert lib.indexer_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == 0
     return lib, h
 
@@ -79,6 +79,31 @@ def test_workspace_bytes_scale_with_chunk_and_selection():
     assert n.value == 100 * 192 * 8             # never more than all keys plus one tile
     assert lib.indexer_workspace_bytes(h, 100, 10 ** 6, 64, 128, 1, 20000,
                                        ctypes.byref(n)) == _lib.IDX_EUNSUPPORTED
+    lib.indexer_destroy(h)
+
+
+def test_workspace_bytes_of_the_few_query_path():
+    """At or below few_query_rows (default 64) the workspace holds the rows'
+    dense scores: S x T (T rounded up to 4) fp32, while that stays within
+    4 GiB; a negative setting always streams."""
+    n = ctypes.c_size_t()
+    lib, h = _handle(chunk=16384)
+    assert lib.indexer_workspace_bytes(h, 64, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 64 * 262144 * 4
+    assert lib.indexer_workspace_bytes(h, 1, 1001, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 1 * 1004 * 4
+    assert lib.indexer_workspace_bytes(h, 65, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 65 * 20736 * 8            # above the default: streaming buffers
+    assert lib.indexer_workspace_bytes(h, 64, 2 ** 25, 64, 128, 1, 2048, ctypes.byref(n)) == 0
+    assert n.value == 64 * 20736 * 8            # 8 GiB of dense scores: streams instead
+    lib.indexer_destroy(h)
+    lib, h = _handle(few=-1)
+    assert lib.indexer_workspace_bytes(h, 1, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 1 * 20736 * 8
+    lib.indexer_destroy(h)
+    lib, h = _handle(few=1000)
+    assert lib.indexer_workspace_bytes(h, 1000, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 1000 * 4096 * 4
     lib.indexer_destroy(h)
 
 
