@@ -76,9 +76,10 @@ def stored_traffic():
     return float(val.group(1))
 
 
-def cpu_baseline(inp, budget_s, seed):
+def cpu_baseline(inp, budget_s, seed, docs=None):
     """The oracle on seeded uniform rows of the same workload, for about
-    budget_s seconds of host time; a rate, so no extrapolation is needed."""
+    budget_s seconds of host time; a rate, so no extrapolation is needed.
+    With docs (packed documents) the oracle runs per document."""
     from oracle import oracle as orc
     rng = np.random.default_rng(seed)
     cores = len(os.sched_getaffinity(0))
@@ -87,11 +88,20 @@ def cpu_baseline(inp, budget_s, seed):
     while spent < budget_s:
         rows = np.sort(rng.integers(0, inp.S, size=4 * threads))
         t0 = time.perf_counter()
-        orc.select_rows(inp, rows, nthreads=threads)
+        if docs:
+            cq = np.asarray(docs["cu_q_host"])
+            orc.select_rows_varlen(inp, cq, docs["cu_k_host"], rows=rows, nthreads=threads,
+                                   cu_tok=cq[:-1] if inp.expand else None)
+            doc = np.searchsorted(cq, rows, side="right") - 1
+            vis = [min(docs["nkeys"][i], (int(r) - int(cq[i]) + 1) // inp.m)
+                   for r, i in zip(rows, doc)]
+        else:
+            orc.select_rows(inp, rows, nthreads=threads)
+            vis = [min(inp.T, (int(r) + inp.q_pos0 + 1) // inp.m) if inp.causal else inp.T
+                   for r in rows]
         spent += time.perf_counter() - t0
         done_rows += rows.size
-        done_triples += sum(min(inp.T, (int(r) + inp.q_pos0 + 1) // inp.m) if inp.causal
-                            else inp.T for r in rows) * inp.H
+        done_triples += sum(vis) * inp.H
     return dict(value=done_triples / spent, unit="triples/s", cores=threads, kind="oracle",
                 sample=f"{done_rows} seeded uniform rows of the {inp.name} workload "
                        f"({done_triples} triples, {spent:.1f} s, fp64, {threads} threads)")
@@ -107,6 +117,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
+    ap.add_argument("--varlen", type=int, default=0, metavar="N",
+                    help="pack the workload's sequence as N equal documents (per-document "
+                         "pools, causality and keys) and time the varlen entry point")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="few-query shape: N query rows at the end of the workload's full "
                          "context (every key visible), timed through the few-query path")
@@ -142,18 +155,39 @@ def main():
                       query_chunk=inp.query_chunk or 0,
                       few_query_rows=max(64, args.decode) if args.decode else 0, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
+    docs = None
+    if args.varlen:
+        # N equal documents; document i owns rows [i*L, (i+1)*L) and its own
+        # L // m complete pools (the last document takes the remainder)
+        L = inp.S // args.varlen
+        lens = [L] * (args.varlen - 1) + [inp.S - L * (args.varlen - 1)]
+        nkeys = [n // inp.m for n in lens]
+        cu_q = np.concatenate([[0], np.cumsum(lens)])
+        cu_k = np.concatenate([[0], np.cumsum(nkeys)])
+        if cu_k[-1] > inp.T:
+            raise SystemExit("the workload has fewer keys than its documents' pools")
+        t32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32, device=dev)
+        docs = dict(cu_q=t32(cu_q), cu_k=t32(cu_k), cu_tok=t32(cu_q[:-1]) if inp.expand else None,
+                    lens=lens, nkeys=nkeys, cu_q_host=cu_q, cu_k_host=cu_k)
     idx = torch.empty((inp.S, W), dtype=torch.int32, device=dev)
     vl = torch.empty((inp.S,), dtype=torch.int32, device=dev)
-    ws = torch.empty((ix.workspace_bytes(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk),),
+    wsb = ix.workspace_bytes_varlen if docs else ix.workspace_bytes
+    ws = torch.empty((wsb(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk),),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
-                      q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
-                      workspace=ws, out=(idx, vl, None))
+        if docs:
+            ix.score_topk_varlen(inp.q, inp.w, inp.k, docs["cu_q"], docs["cu_k"], m=inp.m,
+                                 topk=inp.topk, causal=inp.causal, cu_tok=docs["cu_tok"],
+                                 q_scale=inp.q_scale, k_scale=inp.k_scale, workspace=ws,
+                                 out=(idx, vl, None))
+        else:
+            ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
+                          q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
+                          workspace=ws, out=(idx, vl, None))
         if ev:
             ev[1].record(stream)
         shared = dsai.pair_overlap(idx, vl)
@@ -177,14 +211,18 @@ def main():
     peak_bytes = torch.cuda.max_memory_allocated(dev)
 
     ms_per_step = wall * 1e3 / args.steps
-    pairs = visible_pairs(inp.S, inp.T, inp.m, inp.causal, inp.q_pos0)
+    if docs:
+        pairs = sum(visible_pairs(n, k, inp.m, inp.causal) for n, k in
+                    zip(docs["lens"], docs["nkeys"]))
+    else:
+        pairs = visible_pairs(inp.S, inp.T, inp.m, inp.causal, inp.q_pos0)
     triples = pairs * inp.H
     flops = 2 * inp.d * triples
     n_launch = math.ceil(inp.S / (inp.query_chunk or inp.S))
     score_s = float(np.mean(score_ms)) / 1e3
     achieved_tflops = flops / score_s / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
-    traffic = stored_traffic()
+    traffic = stored_traffic() if not (args.decode or args.varlen) else None
 
     st = dsai.overlap_summary(shared, vl)
     if args.copy_calibration:
@@ -197,8 +235,13 @@ def main():
         torch.cuda.synchronize()
         log("bench: copy calibration: 1 GiB read + 1 GiB written (neg kernel)")
 
-    workload_name = inp.name if not args.decode else \
-        f"{inp.name} decode: {inp.S} rows at positions {inp.q_pos0}..{inp.q_pos0 + inp.S - 1}"
+    workload_name = inp.name
+    if args.decode:
+        workload_name = f"{inp.name} decode: {inp.S} rows at positions " \
+                        f"{inp.q_pos0}..{inp.q_pos0 + inp.S - 1}"
+    if docs:
+        workload_name = f"{inp.name} packed as {args.varlen} documents of {docs['lens'][0]} " \
+                        f"tokens (varlen)"
     roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved_tflops / peak,
                 "traffic": None if traffic is None else traffic,
@@ -244,7 +287,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle for ~{args.cpu_budget:.0f} s")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, inp.seed)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, inp.seed, docs)
     print(json.dumps(result), flush=True)
 
 

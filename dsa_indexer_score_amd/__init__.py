@@ -57,8 +57,10 @@ class Indexer:
                  query_chunk: int = 0, few_query_rows: int = 0, device=None):
         if dtype not in _DTYPE_CODE:
             raise TypeError(f"unsupported dtype {dtype}")
-        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
-            else torch.device(device)
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.dtype, self.expand, self.tail = dtype, bool(expand), bool(tail)
         self.query_chunk = int(query_chunk or 0)
         self.few_query_rows = int(few_query_rows or 0)
@@ -129,6 +131,67 @@ class Indexer:
             d, m, topk, int(bool(causal)), int(q_pos0), _ptr(idx), _ptr(valid_len), _ptr(sel),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(self.device))
         _lib.check(rc, "indexer_score_topk")
+        return (idx, valid_len, sel) if with_scores else (idx, valid_len)
+
+
+    def workspace_bytes_varlen(self, S: int, T: int, H: int, d: int, m: int, topk: int) -> int:
+        n = ctypes.c_size_t(0)
+        _lib.check(self._lib.indexer_workspace_bytes_varlen(self._h, S, T, H, d, m, topk,
+                                                            ctypes.byref(n)),
+                   "indexer_workspace_bytes_varlen")
+        return n.value
+
+    def score_topk_varlen(self, q, w, k, cu_q, cu_k, *, m: int = 1, topk: int,
+                          causal: bool = True, pos0=None, cu_tok=None, q_scale=None,
+                          k_scale=None, with_scores: bool = False,
+                          workspace: Optional[torch.Tensor] = None, out=None):
+        """Packed documents: rows [cu_q[i], cu_q[i+1]) see keys [cu_k[i], cu_k[i+1])
+        (int32 device tensors of ndoc + 1 entries); pos0 (int64 [ndoc]) is each
+        document's first-row position, cu_tok (int32 [ndoc], expand mode) its
+        token offset.  Returns (idx, valid_len[, sel_score])."""
+        if q.dim() != 3 or k.dim() != 2:
+            raise ValueError("q must be [S, H, d] and k [T, d]")
+        S, H, d = q.shape
+        T = k.shape[0]
+        if q.dtype != self.dtype or k.dtype != self.dtype or w.dtype != torch.float32:
+            raise TypeError(f"q and k must be {self.dtype}, w float32")
+        ndoc = cu_q.numel() - 1
+        if ndoc < 0 or cu_k.numel() != ndoc + 1:
+            raise ValueError("cu_q and cu_k must both have ndoc + 1 entries")
+        for name, t, dt in (("cu_q", cu_q, torch.int32), ("cu_k", cu_k, torch.int32),
+                            ("pos0", pos0, torch.int64), ("cu_tok", cu_tok, torch.int32)):
+            if t is None:
+                continue
+            if t.dtype != dt or t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous {dt} tensor on {self.device}")
+            if name in ("pos0", "cu_tok") and t.numel() != ndoc:
+                raise ValueError(f"{name} must have ndoc entries")
+        for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+            if t is not None and (t.device != self.device or not t.is_contiguous()):
+                raise ValueError(f"{name} must be contiguous on {self.device}")
+        if w.dim() == 1 and w.shape[0] == H:
+            w_stride = 0
+        elif w.dim() == 2 and tuple(w.shape) == (S, H):
+            w_stride = H
+        else:
+            raise ValueError("w must be [H] or [S, H]")
+        W = output_width(topk, m, self.expand, self.tail)
+        if out is None:
+            idx = torch.empty((S, W), dtype=torch.int32, device=self.device)
+            valid_len = torch.empty((S,), dtype=torch.int32, device=self.device)
+            sel = torch.empty((S, W), dtype=torch.float32, device=self.device) \
+                if with_scores else None
+        else:
+            idx, valid_len, sel = out
+        nbytes = self.workspace_bytes_varlen(S, T, H, d, m, topk)
+        if workspace is None:
+            workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
+        rc = self._lib.indexer_score_topk_varlen(
+            self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
+            d, m, topk, int(bool(causal)), _ptr(cu_q), _ptr(cu_k), _ptr(pos0), _ptr(cu_tok), ndoc,
+            _ptr(idx), _ptr(valid_len), _ptr(sel), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(self.device))
+        _lib.check(rc, "indexer_score_topk_varlen")
         return (idx, valid_len, sel) if with_scores else (idx, valid_len)
 
 

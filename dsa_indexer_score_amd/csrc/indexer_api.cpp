@@ -155,11 +155,22 @@ int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int
     return IDX_OK;
 }
 
-int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const float *w,
-                       int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
-                       int64_t T, int H, int d, int m, int topk, int causal, int64_t q_pos0,
-                       int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
-                       size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+struct Docs {  // packed-document layout (varlen); on = false: one document
+    bool on = false;
+    const int32_t *cu_q = nullptr, *cu_k = nullptr, *cu_tok = nullptr;
+    const int64_t *pos0 = nullptr;
+    int ndoc = 0;
+};
+
+int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const float *w,
+                    int64_t w_stride_s, const void *k, const float *k_scale, int64_t S, int64_t T,
+                    int H, int d, int m, int topk, int causal, int64_t q_pos0, const Docs &docs,
+                    int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
+                    size_t workspace_bytes, void *stream)
 {
     if (!h) return IDX_EINVAL;
     const indexer_config &cfg = h->cfg;
@@ -171,7 +182,10 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     if (w_stride_s != 0 && w_stride_s < H) return IDX_EINVAL;
     if (expand && topk % m) return IDX_EINVAL;
     if (tail && !causal) return IDX_EINVAL;
-    if (tail && T < (q_pos0 + S) / m) return IDX_EINVAL;
+    if (tail && !docs.on && T < (q_pos0 + S) / m) return IDX_EINVAL;
+    if (docs.on && (docs.ndoc < 0 || (docs.ndoc > 0 && (!docs.cu_q || !docs.cu_k)) ||
+                    (docs.ndoc > 0 && expand && !docs.cu_tok)))
+        return IDX_EINVAL;
     int W = 0;
     if (indexer_output_width(topk, m, flags, &W) != IDX_OK) return IDX_EINVAL;
     if (!shape_supported(cfg.dtype, H, d)) return IDX_EUNSUPPORTED;
@@ -189,11 +203,12 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     if (!fp8 && (q_scale || k_scale)) return IDX_EINVAL;
     if (!aligned(q, 16) || (k && !aligned(k, 16)) || !aligned(w, 4)) return IDX_EINVAL;
     // ---- workspace
-    const int64_t pmax = causal ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
+    const int64_t pmax = causal && !docs.on ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
     const int64_t rows = rows_per_launch(cfg, S);
-    const bool dense = use_dense(cfg, S, T);
-    const size_t need = (size_t)workspace_need(cfg, S, T, ksel, pmax);
+    const bool dense = !docs.on && use_dense(cfg, S, T);
+    const size_t need = docs.on ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
+                                : (size_t)workspace_need(cfg, S, T, ksel, pmax);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
 
     DeviceGuard guard(h->device);
@@ -222,6 +237,11 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     p.cap = (int)cap;
     p.nsplit = 1;
     p.split_keys = round_up(std::max<int64_t>(T, 1), dsai::kKeysPerTile);
+    p.cu_q = docs.cu_q;
+    p.cu_k = docs.cu_k;
+    p.pos0 = docs.pos0;
+    p.cu_tok = docs.cu_tok;
+    p.ndoc = docs.ndoc;
     const int nb = (H + 31) / 32;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dense) {
@@ -240,7 +260,7 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
         p.split_keys = tiles_per * dsai::kKeysPerTile;
         p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
         bool supported = true;
-        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, true, p, st, &supported);
+        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, true, false, p, st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
         e = dsai::launch_select_dense(p, st);
@@ -251,11 +271,57 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
         p.row0 = r0;
         p.nrows = std::min(rows, S - r0);
         bool supported = true;
-        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, false, p, st, &supported);
+        hipError_t e =
+            dsai::launch_score_select(cfg.dtype, nb, d, false, docs.on, p, st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
     }
     return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const float *w,
+                       int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
+                       int64_t T, int H, int d, int m, int topk, int causal, int64_t q_pos0,
+                       int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
+                           q_pos0, Docs{}, idx, valid_len, sel_score, workspace, workspace_bytes,
+                           stream);
+}
+
+int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
+                                   int topk, size_t *bytes)
+{
+    if (!h || !bytes || S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1) return IDX_EINVAL;
+    if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
+    const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
+    if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
+    *bytes = (size_t)(rows_per_launch(h->cfg, S) * capacity(ksel, T) * (int64_t)sizeof(uint2));
+    return IDX_OK;
+}
+
+int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, const float *w,
+                              int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
+                              int64_t T, int H, int d, int m, int topk, int causal,
+                              const int32_t *cu_q, const int32_t *cu_k, const int64_t *pos0,
+                              const int32_t *cu_tok, int ndoc, int32_t *idx, int32_t *valid_len,
+                              float *sel_score, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    Docs docs;
+    docs.on = true;
+    docs.cu_q = cu_q;
+    docs.cu_k = cu_k;
+    docs.pos0 = pos0;
+    docs.cu_tok = cu_tok;
+    docs.ndoc = ndoc;
+    return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
+                           0, docs, idx, valid_len, sel_score, workspace, workspace_bytes, stream);
 }
 
 int indexer_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,

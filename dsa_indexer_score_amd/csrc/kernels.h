@@ -35,6 +35,15 @@ struct ScoreSelectParams {
     int64_t sstride;
     int nsplit;             // key ranges per query group; grid = groups * nsplit
     int64_t split_keys;     // keys per range, a multiple of kKeysPerTile
+    // Packed documents (varlen): rows [cu_q[i], cu_q[i+1]) are document i,
+    // whose keys are k[cu_k[i], cu_k[i+1]); pos0[i] (or 0) is the position of
+    // its first row within the document; expanded outputs are cu_tok[i] +
+    // position.  Rows from cu_q[ndoc] on are padding.
+    const int32_t *cu_q;
+    const int32_t *cu_k;
+    const int64_t *pos0;
+    const int32_t *cu_tok;
+    int ndoc;
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
@@ -42,9 +51,9 @@ constexpr int kKeysPerTile = 128;     // keys staged in LDS per step
 constexpr int kSelGroup = 64;         // keys appended per selection step (one per lane)
 
 // dtype codes match enum idx_dtype; dense = write scores (p.scores) instead
-// of selecting
-hipError_t launch_score_select(int dtype, int nb, int d, bool dense, const ScoreSelectParams &p,
-                               hipStream_t stream, bool *supported);
+// of selecting; varlen = rows and keys are packed documents (p.cu_q ...)
+hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen,
+                               const ScoreSelectParams &p, hipStream_t stream, bool *supported);
 
 // Exact top-k of each row's dense scores (one block per row) and its
 // canonical output row.

@@ -189,7 +189,7 @@ template <int D> struct Op<0, D> {  // fp32
     __device__ static A zero() { return 0.f; }
 };
 
-template <int DT, int NB, int D, bool DENSE>
+template <int DT, int NB, int D, bool DENSE, bool VARLEN>
 __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectParams p)
 {
     using O = Op<DT, D>;
@@ -215,13 +215,58 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const int64_t qrow = grp * kQueriesPerBlock + wave;
     const bool active = qrow < p.nrows;
     const int64_t t = p.row0 + qrow;
-    const int64_t pos = p.q_pos0 + t;
-    const int64_t Pq = active ? visible_keys(pos, p.T, p.m, p.causal) : 0;
-    int64_t last = grp * kQueriesPerBlock + kQueriesPerBlock - 1;
-    if (last > p.nrows - 1) last = p.nrows - 1;
-    const int64_t Pblk = visible_keys(p.q_pos0 + p.row0 + last, p.T, p.m, p.causal);
-    const int64_t kbeg = DENSE ? (int64_t)sp * p.split_keys : 0;
-    const int64_t kend = DENSE && kbeg + p.split_keys < Pblk ? kbeg + p.split_keys : Pblk;
+    // This row's key window [klo, klo + Pq) and the token position of its
+    // key 0 (tok0, expanded outputs).  One document: every key from 0, the
+    // row at position q_pos0 + t.  Packed documents: the row's document's
+    // keys, its position inside that document.
+    int64_t pos, Pq, klo = 0, tok0 = 0;
+    int64_t kbeg, kend;  // keys this block walks
+    if constexpr (VARLEN) {
+        __shared__ int64_t wlo[kQueriesPerBlock], whi[kQueriesPerBlock];
+        int doc = -1;
+        if (active && p.ndoc > 0 && t >= p.cu_q[0] && t < p.cu_q[p.ndoc]) {
+            int lo = 0, hi = p.ndoc;  // largest doc with cu_q[doc] <= t
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.cu_q[mid] <= t) lo = mid;
+                else hi = mid;
+            }
+            doc = lo;
+        }
+        pos = -1;
+        Pq = 0;
+        if (doc >= 0) {
+            pos = (p.pos0 ? p.pos0[doc] : 0) + (t - p.cu_q[doc]);
+            const int64_t a = p.cu_k[doc], b = p.cu_k[doc + 1];
+            klo = a < 0 ? 0 : (a > p.T ? p.T : a);
+            const int64_t khi_doc = b < klo ? klo : (b > p.T ? p.T : b);
+            Pq = visible_keys(pos, khi_doc - klo, p.m, p.causal);
+            if (pos < 0) Pq = 0;
+            tok0 = p.cu_tok ? p.cu_tok[doc] : 0;
+        }
+        if (lane == 0) {
+            wlo[wave] = Pq > 0 ? klo : INT64_MAX;
+            whi[wave] = Pq > 0 ? klo + Pq : INT64_MIN;
+        }
+        __syncthreads();
+        kbeg = INT64_MAX;
+        kend = INT64_MIN;
+#pragma unroll
+        for (int i = 0; i < kQueriesPerBlock; ++i) {
+            kbeg = wlo[i] < kbeg ? wlo[i] : kbeg;
+            kend = whi[i] > kend ? whi[i] : kend;
+        }
+        if (kend <= kbeg) kbeg = kend = 0;
+    } else {
+        pos = p.q_pos0 + t;
+        Pq = active ? visible_keys(pos, p.T, p.m, p.causal) : 0;
+        int64_t last = grp * kQueriesPerBlock + kQueriesPerBlock - 1;
+        if (last > p.nrows - 1) last = p.nrows - 1;
+        const int64_t Pblk = visible_keys(p.q_pos0 + p.row0 + last, p.T, p.m, p.causal);
+        kbeg = DENSE ? (int64_t)sp * p.split_keys : 0;
+        kend = DENSE && kbeg + p.split_keys < Pblk ? kbeg + p.split_keys : Pblk;
+    }
+    const int64_t khi = klo + Pq;
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + kKeysPerTile - 1) / kKeysPerTile) : 0;
 
     uint32_t *hist = hist_all[wave];
@@ -311,12 +356,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             }
             return;
         }
-        const bool full = j0 + kKeysPerTile <= Pq;
+        const bool full = j0 >= klo && j0 + kKeysPerTile <= khi;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const int64_t key = j0 + g * kSelGroup + lane;
             const uint32_t bits = __float_as_uint(sg[g]);
-            const bool pass = sg[g] >= tau_f && (full || key < Pq);
+            const bool pass = sg[g] >= tau_f && (full || (key >= klo && key < khi));
             const uint64_t mask = __ballot(pass);
             if (mask) {
                 const uint32_t u = ord_code(bits);
@@ -373,7 +418,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             select_tile(pend, pend_j0);
             pend_j0 = -1;
         }
-        if (active && j0 < Pq) {
+        if (active && j0 < khi && j0 + kKeysPerTile > klo) {
             // Software pipeline over steps (cb, b): the MFMAs of step s run
             // while the signed-ReLU epilogue of step s-1 is issued between
             // them; B of the next column block is fetched during the last
@@ -455,6 +500,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     wave_sync_mem();
 
     const int mexp = p.expand ? p.m : 1;
+    const int64_t obase = VARLEN && p.expand ? tok0 - klo * p.m : 0;  // key -> output index
     int32_t *orow = p.idx + t * (int64_t)p.W;
     float *srow = p.sel_score ? p.sel_score + t * (int64_t)p.W : nullptr;
     int wcnt = 0, eqseen = 0;
@@ -473,50 +519,54 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         if (keep) {
             const int o = (wcnt + lane_rank(km)) * mexp;
             for (int x = 0; x < mexp; ++x) {
-                orow[o + x] = (int32_t)(v.y * (uint32_t)mexp + (uint32_t)x);
+                orow[o + x] = (int32_t)(obase + (int64_t)v.y * mexp + x);
                 if (srow) srow[o + x] = __uint_as_float(v.x);
             }
         }
         wcnt += __popcll(km);
     });
     const int body = wcnt * mexp;
-    const int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - Pq * p.m) : 0;
+    int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - Pq * p.m) : 0;
+    if (VARLEN) tl = tl < 0 ? 0 : (tl > p.W - body ? p.W - body : tl);  // keys missing: clip
     for (int s = body + lane; s < p.W; s += 64) {
         const bool in_tail = s < body + tl;
-        orow[s] = in_tail ? (int32_t)(Pq * p.m + (s - body)) : -1;
+        orow[s] = in_tail ? (int32_t)(tok0 + Pq * p.m + (s - body)) : -1;
         if (srow) srow[s] = 0.f;
     }
     if (lane == 0) p.valid_len[t] = body + tl;
 }
 
-template <int DT, int NB, int D, bool DENSE>
+template <int DT, int NB, int D, bool DENSE, bool VARLEN>
 hipError_t launch_one(const ScoreSelectParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock * p.nsplit;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, DENSE>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, DENSE, VARLEN>), dim3((unsigned)blocks),
                        dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DT, int NB, int D>
-hipError_t launch_mode(bool dense, const ScoreSelectParams &p, hipStream_t stream)
+hipError_t launch_mode(bool dense, bool varlen, const ScoreSelectParams &p, hipStream_t stream)
 {
-    return dense ? launch_one<DT, NB, D, true>(p, stream) : launch_one<DT, NB, D, false>(p, stream);
+    if (varlen) return launch_one<DT, NB, D, false, true>(p, stream);
+    return dense ? launch_one<DT, NB, D, true, false>(p, stream)
+                 : launch_one<DT, NB, D, false, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_select(int dtype, int nb, int d, bool dense, const ScoreSelectParams &p,
-                               hipStream_t stream, bool *supported)
+hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen,
+                               const ScoreSelectParams &p, hipStream_t stream, bool *supported)
 {
     *supported = true;
-    if (p.nsplit < 1 || p.split_keys < kKeysPerTile || p.split_keys % kKeysPerTile) {
+    if (p.nsplit < 1 || p.split_keys < kKeysPerTile || p.split_keys % kKeysPerTile ||
+        (varlen && (dense || p.nsplit != 1))) {
         *supported = false;
         return hipSuccess;
     }
 #define DSAI_CASE(DT, NB, D) \
-    if (dtype == DT && nb == NB && d == D) return launch_mode<DT, NB, D>(dense, p, stream);
+    if (dtype == DT && nb == NB && d == D) return launch_mode<DT, NB, D>(dense, varlen, p, stream);
     DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
     DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
     DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)

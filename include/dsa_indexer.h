@@ -143,6 +143,54 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
                        size_t workspace_bytes, void *stream);
 
 /*
+ * Packed documents ("varlen"; GLM-5.3-Flash Module 06 "DSA & KPool", section
+ * 3: a pool may not span a document boundary, and one document's tokens may
+ * not influence another document's selection).  The same operation as
+ * indexer_score_topk, per document: row t of document i sits at position
+ * p = pos0[i] + (t - cu_q[i]) of that document and sees the document's keys
+ * j (local index) with (j+1)*m - 1 <= p (causal) or all of them; pools are
+ * the caller's per-document keys, so none spans a boundary.
+ *
+ *   cu_q    device int32 [ndoc + 1]: rows of document i are
+ *           [cu_q[i], cu_q[i+1]); non-decreasing, cu_q[0] = 0,
+ *           cu_q[ndoc] <= S.  Rows from cu_q[ndoc] on are padding: their
+ *           output row is all -1 and valid_len 0.
+ *   cu_k    device int32 [ndoc + 1]: keys of document i are
+ *           k[cu_k[i], cu_k[i+1]); non-decreasing, cu_k[ndoc] <= T.
+ *   pos0    device int64 [ndoc] or NULL (all 0): position within document i
+ *           of its first row (a later prefill chunk, or one decode row per
+ *           sequence at the end of its context).
+ *   cu_tok  device int32 [ndoc], required with IDX_EXPAND: packed-token
+ *           index of document i's position 0.
+ *   Output entries: compressed keys as global key indices cu_k[i] + j;
+ *   with IDX_EXPAND, token indices cu_tok[i] + position (pool j expands to
+ *   positions j*m .. j*m+m-1; with IDX_TAIL the positions from P*m to p of
+ *   the document's incomplete pool follow).
+ *
+ * Every other argument, the width W, the tie rule and the ordering are as
+ * in indexer_score_topk (its q_pos0 has no counterpart here).  The offset
+ * arrays are read on the device only, so their preconditions are not
+ * checked on the host; offsets are clamped to [0, T], and a row whose
+ * document lacks complete pools gets a tail clipped to the row width.  With
+ * IDX_EXPAND the caller keeps every output index below 2^31.  This call
+ * always uses the streaming path; workspace from
+ * indexer_workspace_bytes_varlen.
+ */
+int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, const float *w,
+                              int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
+                              int64_t T, int H, int d, int m, int topk, int causal,
+                              const int32_t *cu_q, const int32_t *cu_k, const int64_t *pos0,
+                              const int32_t *cu_tok, int ndoc, int32_t *idx, int32_t *valid_len,
+                              float *sel_score, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Device workspace bytes for indexer_score_topk_varlen (candidate buffers
+ * for one query chunk of up to min(S, query_chunk) rows, each bounded by T
+ * keys).  Host-only. */
+int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
+                                   int topk, size_t *bytes);
+
+/*
  * Adjacent-pair overlap diagnostic ("Adjacent-Query KV-Index Overlap in
  * 256K DSA Training", sections 1 and 3): for each non-overlapping pair
  * (rows 2i, 2i+1), i < S/2, shared[i] = |A_2i ∩ A_2i+1| where A_t is

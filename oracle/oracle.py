@@ -8,6 +8,8 @@ through the seeded inputs of ``workloads``.
 Pieces:
 * ``select_rows`` / ``pair_scores``: the fp64 C oracle (indexer_oracle.c),
   naive score loops plus a full sort, see that file's header.
+* ``select_rows_varlen``: packed documents, each document solved on its own
+  rows and keys by the same oracle and mapped to global indices.
 * ``output_width``, ``visible_keys``, ``tail_len``, ``expected_valid_len``:
   the visibility and slot arithmetic of GLM-5.3-Flash Module 06 "DSA &
   KPool" (section 2: 512 pools x 4 + 3 tail = 2,051 slots; section 3:
@@ -148,13 +150,20 @@ def select_rows(inp, rows, nthreads: int = 0):
     Returns a dict of numpy arrays: idx [n, W], valid_len [n], key_idx
     [n, Ksel], key_score [n, Ksel] (fp64), n_sel [n], tau [n].
     """
+    rows = np.asarray(rows, dtype=np.int64)
+    return _select(inp, rows, rows + inp.q_pos0, inp.k, inp.k_scale, inp.T, nthreads)
+
+
+def _select(inp, rows, positions, k_t, ks_t, T, nthreads):
+    """The C oracle on q rows ``rows`` of inp at the given absolute positions,
+    against keys k_t [T, d] (scales ks_t)."""
     lib = _load()
     rows = np.asarray(rows, dtype=np.int64)
     n = rows.shape[0]
     q, qs, w, wst = _gather_rows(inp, rows)
-    k = _host(inp.k)
-    ks = None if inp.k_scale is None else _host(inp.k_scale).astype(np.float32)
-    pos = np.ascontiguousarray(rows + inp.q_pos0, dtype=np.int64)
+    k = _host(k_t)
+    ks = None if ks_t is None else _host(ks_t).astype(np.float32)
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
     W = output_width(inp.topk, inp.m, inp.expand, inp.tail)
     Ksel = inp.topk // inp.m if inp.expand else inp.topk
     out = dict(
@@ -164,11 +173,51 @@ def select_rows(inp, rows, nthreads: int = 0):
     )
     rc = lib.oracle_select_rows(
         _ptr(q), _ptr(qs), _ptr(w), wst, _ptr(k), _ptr(ks), DTYPE_CODE[inp.dtype], n,
-        _ptr(pos), inp.T, inp.H, inp.d, inp.m, inp.topk, int(inp.causal), int(inp.expand),
+        _ptr(pos), T, inp.H, inp.d, inp.m, inp.topk, int(inp.causal), int(inp.expand),
         int(inp.tail), _ptr(out["idx"]), _ptr(out["valid_len"]), _ptr(out["key_idx"]),
         _ptr(out["key_score"]), _ptr(out["n_sel"]), _ptr(out["tau"]), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_select_rows failed with status {rc}")
+    return out
+
+
+def select_rows_varlen(inp, cu_q, cu_k, pos0=None, cu_tok=None, rows=None, nthreads: int = 0):
+    """Packed documents -- GLM-5.3-Flash Module 06 "DSA & KPool", section 3
+    and "Ship it": a pool never spans a document boundary and no document's
+    tokens reach another document's selection.  Document i is the
+    single-document problem on its own rows [cu_q[i], cu_q[i+1]), at
+    positions pos0[i] + (row - cu_q[i]), against its own keys
+    k[cu_k[i], cu_k[i+1]); its output entries are mapped to global indices:
+    keys -> cu_k[i] + j, expanded positions (tail included) -> cu_tok[i] +
+    position.  Rows outside every document are padding: all -1, length 0.
+    Returns idx [n, W], valid_len [n] and key_idx [n, Ksel] (global keys,
+    -1 past n_sel), n_sel [n]."""
+    cu_q = np.asarray(cu_q, np.int64)
+    cu_k = np.asarray(cu_k, np.int64)
+    ndoc = cu_q.shape[0] - 1
+    pos0 = np.zeros(ndoc, np.int64) if pos0 is None else np.asarray(pos0, np.int64)
+    rows = np.arange(inp.S) if rows is None else np.asarray(rows, np.int64)
+    W = output_width(inp.topk, inp.m, inp.expand, inp.tail)
+    Ksel = inp.topk // inp.m if inp.expand else inp.topk
+    n = rows.shape[0]
+    out = dict(idx=np.full((n, W), -1, np.int32), valid_len=np.zeros(n, np.int32),
+               key_idx=np.full((n, Ksel), -1, np.int64), n_sel=np.zeros(n, np.int32))
+    for i in range(ndoc):
+        at = np.nonzero((rows >= cu_q[i]) & (rows < cu_q[i + 1]))[0]
+        if at.size == 0:
+            continue
+        k0, k1 = int(cu_k[i]), int(cu_k[i + 1])
+        res = _select(inp, rows[at], pos0[i] + (rows[at] - cu_q[i]), inp.k[k0:k1],
+                      None if inp.k_scale is None else inp.k_scale[k0:k1], k1 - k0, nthreads)
+        base = int(cu_tok[i]) if inp.expand else k0
+        idx = res["idx"].astype(np.int64)
+        idx[idx >= 0] += base
+        out["idx"][at] = idx.astype(np.int32)
+        out["valid_len"][at] = res["valid_len"]
+        for r, a in enumerate(at):
+            ns = res["n_sel"][r]
+            out["n_sel"][a] = ns
+            out["key_idx"][a, :ns] = res["key_idx"][r, :ns] + k0
     return out
 
 

@@ -1,0 +1,113 @@
+"""Packed documents (varlen) on the GPU against the oracle.
+
+GLM-5.3-Flash Module 06 "DSA & KPool", section 3 and "Ship it": the watch
+lengths repeated inside packed multi-document batches, with padding, and no
+cross-document leakage.  Integer-valued problems are compared bit for bit
+with the oracle's per-document composition; float problems per document
+under the tolerance rule; one document through the varlen call equals the
+plain call bit for bit.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import log
+from oracle import check
+from oracle import oracle as orc
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _layout(rng, lens, m, pos0=None):
+    ndoc = len(lens)
+    pos0 = np.zeros(ndoc, np.int64) if pos0 is None else np.asarray(pos0, np.int64)
+    nkeys = [(int(p) + int(n)) // m for p, n in zip(pos0, lens)]   # every complete pool
+    cu_q = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(nkeys)]).astype(np.int32)
+    cu_tok = np.concatenate([[0], np.cumsum(pos0 + np.asarray(lens))])[:-1].astype(np.int32)
+    return cu_q, cu_k, pos0, cu_tok
+
+
+def _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True):
+    import dsa_indexer_score_amd as dsai
+    ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
+                      query_chunk=inp.query_chunk or 0, device=DEV)
+    t = lambda a, dt: torch.as_tensor(np.asarray(a), dtype=dt, device=DEV)
+    out = ix.score_topk_varlen(
+        inp.q, inp.w, inp.k, t(cu_q, torch.int32), t(cu_k, torch.int32), m=inp.m, topk=inp.topk,
+        causal=inp.causal, pos0=t(pos0, torch.int64),
+        cu_tok=t(cu_tok, torch.int32) if inp.expand else None, q_scale=inp.q_scale,
+        k_scale=inp.k_scale, with_scores=with_scores)
+    torch.cuda.synchronize()
+    return out
+
+
+WATCH = [3, 4, 5, 7, 8, 9]
+
+
+@pytest.mark.parametrize("m,expand,seed", [(4, True, 0), (4, False, 1), (1, False, 2),
+                                           (4, True, 3)])
+def test_varlen_integer_batches_match_oracle_exactly(m, expand, seed):
+    rng = np.random.default_rng(100 + seed)
+    lens = list(rng.choice(WATCH + [1, 2, 16, 63, 64, 65, 300], size=40))
+    pos0 = rng.integers(0, 40, size=len(lens)) if seed == 3 else None
+    cu_q, cu_k, pos0, cu_tok = _layout(rng, lens, m, pos0)
+    S, T = int(cu_q[-1]) + 5, int(cu_k[-1])              # 5 padding rows
+    H, d = 4, 32
+    q = torch.from_numpy(rng.integers(-3, 4, size=(S, H, d)).astype(np.float32))
+    k = torch.from_numpy(rng.integers(-3, 4, size=(T, d)).astype(np.float32))
+    w = torch.from_numpy(rng.choice([-1.0, -0.5, 0.5, 1.0], size=(S, H)).astype(np.float32))
+    topk = 12 if expand else 7
+    inp = gen.custom(q=q, k=k, w=w, m=m, topk=topk, expand=expand, tail=expand).to(DEV)
+    idx, vl, sc = _run(inp, cu_q, cu_k, pos0, cu_tok)
+    want = orc.select_rows_varlen(inp, cu_q, cu_k, pos0=pos0, cu_tok=cu_tok)
+    assert np.array_equal(vl.cpu().numpy(), want["valid_len"])
+    assert np.array_equal(idx.cpu().numpy(), want["idx"])
+    assert (vl[-5:] == 0).all() and (idx[-5:] == -1).all()
+    log(f"  m={m} expand={expand}: {len(lens)} documents, S={S}, T={T}")
+
+
+def test_one_document_equals_the_plain_call():
+    import dsa_indexer_score_amd as dsai
+    for name, S in (("c4_csa_256k", 3000), ("c2_glm_pooled", 2000), ("c3_dsa_token", 1500)):
+        m = gen.CONFIGS[name]["m"]
+        T = (37 + S) // m                       # every complete pool of the context
+        inp = replace(gen.generate(name, S=S, T=T, topk=256), q_pos0=37).to(DEV)
+        ref = dsai.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=True,
+                              expand=inp.expand, tail=inp.tail, q_scale=inp.q_scale,
+                              k_scale=inp.k_scale, q_pos0=inp.q_pos0, few_query_rows=-1,
+                              with_scores=True)
+        got = _run(inp, [0, S], [0, T], [inp.q_pos0], [0])
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("name", ["c4_csa_256k", "c2_glm_pooled"])
+def test_varlen_float_batch_per_document(name):
+    """A packed bf16 batch: every document's rows, mapped back to local
+    indices, pass the tolerance rule against the oracle on that document."""
+    rng = np.random.default_rng(7)
+    base = gen.generate(name, S=6000, topk=512)
+    m = base.m
+    lens = [5, 1000, 3, 2048, 7, 400, 2500]
+    cu_q, cu_k, pos0, cu_tok = _layout(rng, lens, m)
+    S, T = int(cu_q[-1]), int(cu_k[-1])
+    inp = replace(base, S=S, T=T, q=base.q[:S].contiguous(), k=base.k[:T].contiguous(),
+                  k_scale=None if base.k_scale is None else base.k_scale[:T].contiguous()).to(DEV)
+    idx, vl, sc = _run(inp, cu_q, cu_k, pos0, cu_tok)
+    idx, vl, sc = idx.cpu().numpy(), vl.cpu().numpy(), sc.cpu().numpy()
+    for i in range(len(lens)):
+        r0, r1, k0, k1 = int(cu_q[i]), int(cu_q[i + 1]), int(cu_k[i]), int(cu_k[i + 1])
+        sub = replace(inp, S=r1 - r0, T=k1 - k0, q=inp.q[r0:r1], k=inp.k[k0:k1],
+                      w=inp.w if inp.w.dim() == 1 else inp.w[r0:r1],
+                      k_scale=None if inp.k_scale is None else inp.k_scale[k0:k1])
+        loc = idx[r0:r1].astype(np.int64)
+        base_off = int(cu_tok[i]) if inp.expand else k0
+        loc[loc >= 0] -= base_off
+        rep = check.compare(sub, np.arange(r1 - r0), loc.astype(np.int32), vl[r0:r1],
+                            sc[r0:r1])
+        assert rep["ok"], (i, rep["failures"][:3])

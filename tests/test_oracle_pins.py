@@ -123,6 +123,79 @@ def test_we4_pool_leak():
                expand=True, tail=True)
 
 
+def _we6_inputs(rec, S, expand):
+    k = torch.tensor([[float(v[0])] for v in rec["k"]])
+    return gen.custom(q=torch.ones(S, 1, 1), k=k, w=torch.ones(1), m=scalar(rec, "m"),
+                      topk=scalar(rec, "topk") if expand else 1, expand=expand, tail=expand)
+
+
+def test_we6_packed_documents():
+    rec = load("we6_packed_documents.txt")
+    S = scalar(rec, "S")
+    cu_q = [int(x) for x in rec["cu_q"][0]]
+    cu_k = [int(x) for x in rec["cu_k"][0]]
+    cu_tok = [int(x) for x in rec["cu_tok"][0]]
+    out = orc.select_rows_varlen(_we6_inputs(rec, S, True), cu_q, cu_k, cu_tok=cu_tok)
+    for row in rec["exp"]:
+        t, v, *ids = (int(x) for x in row)
+        assert out["valid_len"][t] == v, t
+        assert list(out["idx"][t]) == ids, t
+    out = orc.select_rows_varlen(_we6_inputs(rec, S, False), cu_q, cu_k)
+    for row in rec["cmp"]:
+        t, v, *ids = (int(x) for x in row)
+        assert out["valid_len"][t] == v, t
+        assert list(out["idx"][t]) == ids, t
+    dq = [int(x) for x in rec["dec_cu_q"][0]]
+    dp = [int(x) for x in rec["dec_pos0"][0]]
+    out = orc.select_rows_varlen(_we6_inputs(rec, 10, True), dq, cu_k, pos0=dp, cu_tok=cu_tok)
+    for row in rec["dec"]:
+        t, v, *ids = (int(x) for x in row)
+        assert out["valid_len"][t] == v, t
+        assert list(out["idx"][t]) == ids, t
+
+
+def test_varlen_matches_brute_force_per_document():
+    """Random packed batches of tiny integer documents (lengths around the
+    pool edges, padding rows, later-chunk positions): every row equals the
+    brute-force selection over its own document's keys, offset to global
+    indices, and no row ever names another document's key or token."""
+    rng = np.random.default_rng(20261204)
+    for case in range(300):
+        m = int(rng.choice([1, 2, 4]))
+        H, d = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        expand = bool(m > 1 and rng.random() < 0.5)
+        topk = int(rng.integers(1, 5)) * (m if expand else 1)
+        ndoc = int(rng.integers(1, 5))
+        lens = rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 12], size=ndoc)
+        pos0 = rng.integers(0, 6, size=ndoc)
+        nkeys = [(int(p) + int(n)) // m for p, n in zip(pos0, lens)]  # every complete pool
+        cu_q = np.concatenate([[0], np.cumsum(lens)])
+        cu_k = np.concatenate([[0], np.cumsum(nkeys)])
+        cu_tok = np.concatenate([[0], np.cumsum([int(p) + int(n) for p, n in zip(pos0, lens)])])[:-1]
+        S, T = int(cu_q[-1]) + int(rng.integers(0, 3)), int(cu_k[-1])
+        q = torch.from_numpy(rng.integers(-3, 4, size=(S, H, d)).astype(np.float32))
+        k = torch.from_numpy(rng.integers(-3, 4, size=(max(T, 1), d)).astype(np.float32))[:T]
+        w = torch.from_numpy(rng.choice([-1.0, -0.5, 0.5, 1.0], size=H).astype(np.float32))
+        inp = gen.custom(q=q, k=k, w=w, m=m, topk=topk, expand=expand, tail=expand)
+        out = orc.select_rows_varlen(inp, cu_q, cu_k, pos0=pos0, cu_tok=cu_tok)
+        Q, Wt, K = dequant(inp)
+        for t in range(S):
+            i = int(np.searchsorted(cu_q, t, side="right")) - 1
+            if i >= ndoc:
+                assert out["valid_len"][t] == 0 and np.all(out["idx"][t] == -1), (case, t)
+                continue
+            p = int(pos0[i]) + t - int(cu_q[i])
+            Kd = K[cu_k[i]:cu_k[i + 1]]
+            pos, _, _ = brute_row(Q[t], Wt[t], Kd, p, Kd.shape[0], m, topk, True, expand, expand)
+            want = pos + (cu_tok[i] if expand else cu_k[i])
+            v = len(want)
+            assert out["valid_len"][t] == v, (case, t)
+            assert list(out["idx"][t][:v]) == list(want), (case, t)
+            lo, hi = (cu_tok[i], cu_tok[i] + int(pos0[i]) + lens[i]) if expand else \
+                (cu_k[i], cu_k[i + 1])
+            assert all(lo <= x < hi for x in out["idx"][t][:v]), (case, t)
+
+
 def test_we5_csa_counts():
     rec = load("we5_csa_counts.txt")
     m, topk = scalar(rec, "m"), scalar(rec, "topk")
