@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--varlen", type=int, default=0, metavar="N",
                     help="pack the workload's sequence as N equal documents (per-document "
                          "pools, causality and keys) and time the varlen entry point")
+    ap.add_argument("--regions", action="store_true",
+                    help="also time the three-region q-cluster split of the adjacent pairs")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="few-query shape: N query rows at the end of the workload's full "
                          "context (every key visible), timed through the few-query path")
@@ -225,6 +227,23 @@ def main():
     traffic = stored_traffic() if not (args.decode or args.varlen) else None
 
     st = dsai.overlap_summary(shared, vl)
+    regions = None
+    if args.regions:
+        # fixed-capacity outputs: 2 rows read, 3 rows + 3 counts written per pair
+        W_ = idx.shape[1]
+        npairs = inp.S // 2
+        rb = npairs * (2 * W_ * 4 + 2 * 4 + 3 * W_ * 4 + 3 * 4)
+        for _ in range(2):
+            dsai.pair_regions(idx, vl)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dsai.pair_regions(idx, vl)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / 10
+        regions = {"ms": rms, "bytes": rb, "GB/s": rb / rms / 1e6,
+                   "frac_of_hbm": rb / rms / 1e6 / HBM_PEAK_GBS}
     if args.copy_calibration:
         # One elementwise kernel of known size (reads 1 GiB, writes 1 GiB): the
         # scale for the FETCH_SIZE / WRITE_SIZE counters of the same run.
@@ -284,6 +303,7 @@ def main():
         "peak_hbm_bytes_allocated": int(peak_bytes),
         "roofline": roofline,
         "overlap": {k: st[k] for k in ("mean_overlap", "median_overlap", "mean_jaccard")},
+        **({"pair_regions": regions} if regions else {}),
     }
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle for ~{args.cpu_budget:.0f} s")

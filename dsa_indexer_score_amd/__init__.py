@@ -232,6 +232,25 @@ def pair_overlap(idx: torch.Tensor, valid_len: torch.Tensor) -> torch.Tensor:
     return shared
 
 
+def pair_regions(idx: torch.Tensor, valid_len: torch.Tensor):
+    """Per adjacent pair: (shared, left_only, right_only) rows [S//2, W]
+    (ascending, then -1) and counts [S//2, 3], all device int32."""
+    if idx.dim() != 2 or idx.dtype != torch.int32 or valid_len.dtype != torch.int32:
+        raise TypeError("idx must be int32 [S, W] and valid_len int32 [S]")
+    if not (idx.is_cuda and idx.is_contiguous() and valid_len.is_cuda):
+        raise ValueError("idx / valid_len must be contiguous device tensors")
+    S, W = idx.shape
+    n = S // 2
+    shared, left, right = (torch.empty((n, W), dtype=torch.int32, device=idx.device)
+                           for _ in range(3))
+    counts = torch.empty((n, 3), dtype=torch.int32, device=idx.device)
+    lib = _lib.load()
+    _lib.check(lib.indexer_pair_regions(_ptr(idx), _ptr(valid_len), S, W, _ptr(shared),
+                                        _ptr(left), _ptr(right), _ptr(counts),
+                                        _stream(idx.device)), "indexer_pair_regions")
+    return shared, left, right, counts
+
+
 def overlap_summary(shared: torch.Tensor, valid_len: torch.Tensor) -> dict:
     """Page-1 style statistics (host computation over host copies)."""
     sh = shared.detach().to("cpu", torch.int32).contiguous()

@@ -40,6 +40,7 @@ SIGNATURES = {
     "indexer_workspace_bytes_varlen": (_I, [_P, _I64, _I64, _I, _I, _I, _I,
                                             ctypes.POINTER(_SZ)]),
     "indexer_pair_overlap": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "indexer_pair_regions": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),
     "indexer_overlap_summary": (_I, [_P, _P, _I64, ctypes.POINTER(OverlapStats)]),
     "indexer_strerror": (ctypes.c_char_p, [_I]),
 }

@@ -324,6 +324,19 @@ int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, 
                            0, docs, idx, valid_len, sel_score, workspace, workspace_bytes, stream);
 }
 
+int indexer_pair_regions(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,
+                         int32_t *shared, int32_t *left, int32_t *right, int32_t *counts,
+                         void *stream)
+{
+    if (S < 0 || W < 1) return IDX_EINVAL;
+    const int64_t npairs = S / 2;
+    if (npairs == 0) return IDX_OK;
+    if (!idx || !valid_len || !shared || !left || !right || !counts) return IDX_EINVAL;
+    hipError_t e = dsai::launch_pair_regions(idx, valid_len, npairs, W, shared, left, right,
+                                             counts, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? IDX_OK : fail_hip(e);
+}
+
 int indexer_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,
                          int32_t *shared, void *stream)
 {

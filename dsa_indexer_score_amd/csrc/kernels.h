@@ -62,4 +62,8 @@ hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream);
 hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t npairs,
                                int W, int32_t *shared, hipStream_t stream);
 
+hipError_t launch_pair_regions(const int32_t *idx, const int32_t *valid_len, int64_t npairs, int W,
+                               int32_t *shared, int32_t *left, int32_t *right, int32_t *counts,
+                               hipStream_t stream);
+
 }  // namespace dsai

@@ -52,6 +52,24 @@ __device__ __forceinline__ void for_each_index(const int32_t *row, int n, int la
     }
 }
 
+// f(valid, x) for every lane of every batch, in row order (entry base +
+// 64 i + lane), kUnroll loads in flight; lanes past the row get valid = false
+// so wave-uniform state in f stays uniform.
+template <class F>
+__device__ __forceinline__ void for_each_index_ordered(const int32_t *row, int n, int lane, F &&f)
+{
+    for (int base = 0; base < n; base += 64 * kUnroll) {
+        int32_t v[kUnroll];
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const int e = base + i * 64 + lane;
+            v[i] = e < n ? row[e] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) f(base + i * 64 + lane < n, v[i]);
+    }
+}
+
 __global__ void __launch_bounds__(kWaves * 64) pair_overlap_kernel(const int32_t *idx,
                                                                    const int32_t *valid_len,
                                                                    int64_t npairs, int W,
@@ -122,6 +140,85 @@ __global__ void __launch_bounds__(kWaves * 64) pair_overlap_kernel(const int32_t
     if (lane == 0) shared[pr] = c;
 }
 
+// Three-region split of each pair (Overlap page, sections 6.1 and 6.4): the
+// entries both rows hold, those only row 2i holds and those only row 2i+1
+// holds, each ascending, written into fixed-capacity rows of width W (then
+// -1) with the three counts.  Same bitmap windows as above, twice per
+// window: row B's bits classify row A's entries, then row A's bits pick row
+// B's unique entries.  Entries are visited in row order (e = 64 i + lane),
+// so ballot-ranked appends keep every region sorted.
+__global__ void __launch_bounds__(kWaves * 64) pair_regions_kernel(
+    const int32_t *idx, const int32_t *valid_len, int64_t npairs, int W, int32_t *shared,
+    int32_t *left, int32_t *right, int32_t *counts)
+{
+    __shared__ uint32_t bitmap_all[kWaves][kWords];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t pr = (int64_t)blockIdx.x * kWaves + wave;
+    if (pr >= npairs) return;  // no block-level barrier below
+    uint32_t *bm = bitmap_all[wave];
+    const int32_t *a = idx + (2 * pr) * (int64_t)W;
+    const int32_t *b = a + W;
+    int32_t *osh = shared + pr * (int64_t)W, *ol = left + pr * (int64_t)W,
+            *orr = right + pr * (int64_t)W;
+    int va = valid_len[2 * pr], vb = valid_len[2 * pr + 1];
+    va = va < 0 ? 0 : (va > W ? W : va);
+    vb = vb < 0 ? 0 : (vb > W ? W : vb);
+    int nsh = 0, nl = 0, nr = 0;
+    auto put = [&](int32_t *dst, int &n, bool take, int32_t x) {
+        const uint64_t m = __ballot(take);
+        if (take) dst[n + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = x;
+        n += __popcll(m);
+    };
+    if (va > 0 || vb > 0) {
+        const int64_t lo = va == 0 ? b[0] : (vb == 0 ? a[0] : (a[0] < b[0] ? a[0] : b[0]));
+        const int64_t hi = va == 0 ? b[vb - 1]
+                                   : (vb == 0 ? a[va - 1]
+                                              : (a[va - 1] > b[vb - 1] ? a[va - 1] : b[vb - 1]));
+        clear_words(bm, kWindow, lane);
+        wave_sync_lds();
+        for (int64_t w0 = lo; w0 <= hi; w0 += kWindow) {
+            const int64_t nbits = hi - w0 + 1 < kWindow ? hi - w0 + 1 : kWindow;
+            auto in_win = [&](int32_t x) { return (int64_t)x >= w0 && (int64_t)x - w0 < kWindow; };
+            // row B's bits; row A's entries -> shared or left-only
+            for_each_index(b, vb, lane, [&](int32_t x) {
+                if (in_win(x)) atomicOr(&bm[(x - w0) >> 5], 1u << ((x - w0) & 31));
+            });
+            wave_sync_lds();
+            for_each_index_ordered(a, va, lane, [&](bool valid, int32_t x) {
+                const bool in = valid && in_win(x);
+                const bool hit = in && ((bm[(x - w0) >> 5] >> ((x - w0) & 31)) & 1u);
+                put(osh, nsh, hit, x);
+                put(ol, nl, in && !hit, x);
+            });
+            wave_sync_lds();
+            clear_words(bm, nbits, lane);
+            wave_sync_lds();
+            // row A's bits; row B's entries -> right-only
+            for_each_index(a, va, lane, [&](int32_t x) {
+                if (in_win(x)) atomicOr(&bm[(x - w0) >> 5], 1u << ((x - w0) & 31));
+            });
+            wave_sync_lds();
+            for_each_index_ordered(b, vb, lane, [&](bool valid, int32_t x) {
+                const bool in = valid && in_win(x);
+                const bool hit = in && ((bm[(x - w0) >> 5] >> ((x - w0) & 31)) & 1u);
+                put(orr, nr, in && !hit, x);
+            });
+            wave_sync_lds();
+            clear_words(bm, nbits, lane);
+            wave_sync_lds();
+        }
+    }
+    for (int s = nsh + lane; s < W; s += 64) osh[s] = -1;
+    for (int s = nl + lane; s < W; s += 64) ol[s] = -1;
+    for (int s = nr + lane; s < W; s += 64) orr[s] = -1;
+    if (lane == 0) {
+        counts[3 * pr] = nsh;
+        counts[3 * pr + 1] = nl;
+        counts[3 * pr + 2] = nr;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t npairs,
@@ -131,6 +228,21 @@ hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int
     const int64_t blocks = (npairs + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(pair_overlap_kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream,
                        idx, valid_len, npairs, W, shared);
+    return hipGetLastError();
+}
+
+}  // namespace dsai
+
+namespace dsai {
+
+hipError_t launch_pair_regions(const int32_t *idx, const int32_t *valid_len, int64_t npairs, int W,
+                               int32_t *shared, int32_t *left, int32_t *right, int32_t *counts,
+                               hipStream_t stream)
+{
+    if (npairs <= 0) return hipSuccess;
+    const int64_t blocks = (npairs + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(pair_regions_kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream,
+                       idx, valid_len, npairs, W, shared, left, right, counts);
     return hipGetLastError();
 }
 

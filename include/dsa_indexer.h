@@ -202,6 +202,26 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
 int indexer_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,
                          int32_t *shared, void *stream);
 
+/*
+ * q-cluster preprocessing ("Adjacent-Query KV-Index Overlap in 256K DSA
+ * Training", sections 6.1, 6.2 and 6.4): for each non-overlapping pair
+ * (rows 2i, 2i+1), i < S/2, split the two index rows into the entries both
+ * hold, the entries only row 2i holds and the entries only row 2i+1 holds.
+ * The exact split is computed here (no fixed shared count is assumed), into
+ * fixed-capacity buffers with device-side counts, so a captured launch
+ * sequence stays valid whatever the overlap.
+ *   idx [S, W] int32, valid_len [S] int32: device, in; each row's first
+ *     valid_len entries ascending (as indexer_score_topk writes them).
+ *   shared, left, right: device [S/2, W] int32, out: the region's entries
+ *     ascending, then -1.
+ *   counts: device [S/2, 3] int32, out: sizes of shared, left, right
+ *     (shared + left = valid_len[2i], shared + right = valid_len[2i+1]).
+ * An odd last row is unpaired.
+ */
+int indexer_pair_regions(const int32_t *idx, const int32_t *valid_len, int64_t S, int W,
+                         int32_t *shared, int32_t *left, int32_t *right, int32_t *counts,
+                         void *stream);
+
 /* Summary of the adjacent-pair statistic over host copies of shared[S/2]
  * and valid_len[S].  Overlap of a pair = shared / min(vA, vB) (normalised by
  * the rows' valid top-k lengths); Jaccard = shared / (vA + vB - shared).

@@ -266,6 +266,26 @@ def pair_overlap(idx: np.ndarray, valid_len: np.ndarray) -> np.ndarray:
     return shared
 
 
+def pair_regions(idx: np.ndarray, valid_len: np.ndarray):
+    """Three-region split of each adjacent pair ("Adjacent-Query KV-Index
+    Overlap in 256K DSA Training", sections 6.1 and 6.4): entries of both
+    rows, only the left (row 2i), only the right (row 2i+1), each ascending
+    and padded with -1 to the row width; counts [n, 3]."""
+    idx = np.asarray(idx)
+    vl = np.asarray(valid_len)
+    n, W = idx.shape[0] // 2, idx.shape[1]
+    out = [np.full((n, W), -1, np.int32) for _ in range(3)]
+    counts = np.zeros((n, 3), np.int32)
+    for i in range(n):
+        a = idx[2 * i, :vl[2 * i]]
+        b = idx[2 * i + 1, :vl[2 * i + 1]]
+        parts = (np.intersect1d(a, b), np.setdiff1d(a, b), np.setdiff1d(b, a))
+        for r, part in enumerate(parts):
+            out[r][i, :part.size] = part
+            counts[i, r] = part.size
+    return out[0], out[1], out[2], counts
+
+
 def overlap_stats(shared: np.ndarray, valid_len: np.ndarray) -> dict:
     """Page-1 table columns from per-pair shared counts and row valid lengths.
     Pairs with an empty row are excluded (their overlap is undefined)."""

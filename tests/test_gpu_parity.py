@@ -303,6 +303,41 @@ def test_pair_overlap_wide_ranges_and_ragged_rows(W):
         assert (vl > 2304).any()
 
 
+@pytest.mark.parametrize("W", [2051, 5000])
+def test_pair_regions_match_oracle(W):
+    """The three-region q-cluster split (shared / left-only / right-only with
+    device counts) on rows spanning several bitmap windows, ragged and empty
+    rows and rows longer than the register path, then on indexer output."""
+    import dsa_indexer_score_amd as dsai
+    rng = np.random.default_rng(23 + W)
+    S = 201
+    idx = np.full((S, W), -1, np.int32)
+    vl = np.zeros(S, np.int32)
+    for t in range(S):
+        span = int(rng.choice([50, 5000, 140000, 400000]))
+        n = min(int(rng.choice([0, 1, 63, 64, 65, 1000, 2400, W])), span, W)
+        if t % 2 == 1 and vl[t - 1] > 0 and rng.random() < 0.7:
+            prev = idx[t - 1, :vl[t - 1]]
+            row = np.unique(np.concatenate([prev[rng.random(prev.size) < 0.6],
+                                            rng.choice(span, size=n, replace=False)]))[:W]
+        else:
+            row = np.sort(rng.choice(span, size=n, replace=False))
+        idx[t, :row.size] = row
+        vl[t] = row.size
+    got = dsai.pair_regions(torch.from_numpy(idx).to(DEV), torch.from_numpy(vl).to(DEV))
+    want = orc.pair_regions(idx, vl)
+    for g, w_ in zip(got, want):
+        assert np.array_equal(g.cpu().numpy(), w_)
+    inp = gen.generate("c3_dsa_token", S=3001, topk=256).to(DEV)
+    idx_d, vl_d, _ = run(inp)
+    got = dsai.pair_regions(idx_d, vl_d)
+    want = orc.pair_regions(idx_d.cpu().numpy(), vl_d.cpu().numpy())
+    for g, w_ in zip(got, want):
+        assert np.array_equal(g.cpu().numpy(), w_)
+    shared = dsai.pair_overlap(idx_d, vl_d)
+    assert torch.equal(shared, got[3][:, 0])
+
+
 def test_fp8_every_code_is_widened_exactly():
     """Each of the 254 finite e4m3 codes, read through the kernel's widening
     and contraction, reproduces the oracle's hand-decoded value exactly:

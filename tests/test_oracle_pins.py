@@ -54,6 +54,42 @@ def test_we1_pair_overlap():
     assert st["mean_jaccard"] == pytest.approx((0.5 + 1 / 3) / 2)
 
 
+def test_we1_pair_regions():
+    """WE1's rows by hand: pair (0,1) = {0} / {0,1}: shared {0}, left {},
+    right {1}; pair (2,3) = {0,2} / {0,3}: shared {0}, left {2}, right {3}
+    (the three regions of the q-cluster split, Overlap page section 6.1)."""
+    rec = load("we1_signed_relu.txt")
+    out = orc.select_rows(_we_inputs(rec, S=4), np.arange(4))
+    sh, le, ri, cnt = orc.pair_regions(out["idx"], out["valid_len"])
+    assert cnt.tolist() == [[1, 0, 1], [1, 1, 1]]
+    assert sh[0, :1].tolist() == [0] and ri[0, :1].tolist() == [1]
+    assert sh[1, :1].tolist() == [0] and le[1, :1].tolist() == [2] and ri[1, :1].tolist() == [3]
+    assert (le[0] == -1).all() and (sh[0, 1:] == -1).all()
+
+
+def test_pair_regions_closed_cases_and_partition():
+    W = 9
+    idx = np.full((5, W), -1, np.int32)
+    vl = np.array([4, 4, 3, 2, 5], np.int32)
+    idx[0, :4] = idx[1, :4] = [1, 5, 9, 12]          # identical rows
+    idx[2, :3], idx[3, :2] = [0, 2, 4], [1, 3]       # disjoint rows; row 4 unpaired
+    sh, le, ri, cnt = orc.pair_regions(idx, vl)
+    assert cnt.tolist() == [[4, 0, 0], [0, 3, 2]]
+    assert sh[0, :4].tolist() == [1, 5, 9, 12] and le[1, :3].tolist() == [0, 2, 4]
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        a = np.unique(rng.integers(0, 60, size=rng.integers(0, 30)))
+        b = np.unique(rng.integers(0, 60, size=rng.integers(0, 30)))
+        idx = np.full((2, 64), -1, np.int32)
+        idx[0, :a.size], idx[1, :b.size] = a, b
+        sh, le, ri, cnt = orc.pair_regions(idx, np.array([a.size, b.size]))
+        s_, l_, r_ = (set(x[0, :c].tolist()) for x, c in zip((sh, le, ri), cnt[0]))
+        assert s_ | l_ == set(a.tolist()) and s_ | r_ == set(b.tolist())
+        assert not (s_ & l_) and not (s_ & r_) and not (l_ & r_)
+        for x, c in zip((sh, le, ri), cnt[0]):
+            assert list(x[0, :c]) == sorted(x[0, :c]) and (x[0, c:] == -1).all()
+
+
 def test_we2_tie_rule():
     rec = load("we2_tie_rule.txt")
     inp = _we_inputs(rec, S=5)
