@@ -74,17 +74,35 @@ constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
 
 int64_t dense_stride(int64_t T) { return round_up(std::max<int64_t>(T, 1), 4); }
 
-// Few-query path: the S rows' visible scores fit a dense workspace.
+// Few-query workspace: the rows' dense scores [S, stride] (f32), the
+// per-row threshold estimates [S] (u32), the candidate counts [S, nseg]
+// and the candidate keys [S, nseg, segment] (i32), each 256-byte aligned.
+struct DenseLayout {
+    int64_t stride, nseg, est, cnt, key, bytes;
+    DenseLayout(int64_t S, int64_t T)
+    {
+        const int64_t seg = dsai::dense_segment_keys();
+        stride = dense_stride(T);
+        nseg = (std::max<int64_t>(T, 1) + seg - 1) / seg;
+        est = round_up(S * stride * 4, 256);
+        cnt = est + round_up(S * 4, 256);
+        key = cnt + round_up(S * nseg * 4, 256);
+        bytes = key + S * nseg * seg * 4;
+    }
+};
+
+// Few-query path: the S rows' visible scores (and the selection's scratch)
+// fit a dense workspace.
 bool use_dense(const indexer_config &cfg, int64_t S, int64_t T)
 {
     const int64_t lim = cfg.few_query_rows == 0 ? kFewRowsDefault : cfg.few_query_rows;
-    return lim > 0 && S <= lim && S * dense_stride(T) * 4 <= kDenseMaxBytes;
+    return lim > 0 && S <= lim && S <= 65535 && DenseLayout(S, T).bytes <= kDenseMaxBytes;
 }
 
 int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int64_t ksel,
                        int64_t pmax)
 {
-    if (use_dense(cfg, S, T)) return S * dense_stride(T) * 4;
+    if (use_dense(cfg, S, T)) return DenseLayout(S, T).bytes;
     return rows_per_launch(cfg, S) * capacity(ksel, pmax) * (int64_t)sizeof(uint2);
 }
 
@@ -246,10 +264,17 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dense) {
         // Few-query path: all CUs score the rows' key ranges into the dense
-        // workspace, then one block per row selects.
+        // workspace, then the selection runs per row (estimate), per
+        // (row, key segment) (candidate filter) and per row (exact cut).
+        const DenseLayout L(S, T);
+        char *base = static_cast<char *>(workspace);
         p.ws = nullptr;
-        p.scores = static_cast<float *>(workspace);
-        p.sstride = dense_stride(T);
+        p.scores = reinterpret_cast<float *>(base);
+        p.sstride = L.stride;
+        p.est = reinterpret_cast<uint32_t *>(base + L.est);
+        p.seg_cnt = reinterpret_cast<int32_t *>(base + L.cnt);
+        p.seg_key = reinterpret_cast<int32_t *>(base + L.key);
+        p.nseg = (int)L.nseg;
         p.row0 = 0;
         p.nrows = S;
         const int64_t groups = (S + dsai::kQueriesPerBlock - 1) / dsai::kQueriesPerBlock;

@@ -44,6 +44,13 @@ struct ScoreSelectParams {
     const int64_t *pos0;
     const int32_t *cu_tok;
     int ndoc;
+    // Few-query selection scratch (dense mode): per-row threshold estimate,
+    // per (row, segment of dense_segment_keys() keys) candidate counts and
+    // candidate keys (nseg segments per row, dense_segment_keys() slots each).
+    uint32_t *est;
+    int32_t *seg_cnt;
+    int32_t *seg_key;
+    int nseg;
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
@@ -55,9 +62,11 @@ constexpr int kSelGroup = 64;         // keys appended per selection step (one p
 hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen,
                                const ScoreSelectParams &p, hipStream_t stream, bool *supported);
 
-// Exact top-k of each row's dense scores (one block per row) and its
-// canonical output row.
+// Exact top-k of each row's dense scores and its canonical output row:
+// threshold estimate per row, candidate filter per (row, key chunk), exact
+// cut and output per row.
 hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream);
+int dense_segment_keys();
 
 hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t npairs,
                                int W, int32_t *shared, hipStream_t stream);

@@ -38,6 +38,8 @@ constexpr int kDenseThreads = 1024;
 constexpr int kDenseWaves = kDenseThreads / 64;
 constexpr int kPer = 16;                        // consecutive keys per thread per chunk
 constexpr int kChunk = kDenseThreads * kPer;    // keys per chunk
+constexpr int kFilterThreads = 256;             // candidate filter block
+constexpr int kSeg = kFilterThreads * kPer;     // keys per filter segment
 
 // The KP consecutive scores of this thread's slice of chunk `base` (raw
 // bits); all loads are issued before any is used.
@@ -65,7 +67,9 @@ struct SliceT {
 };
 using Slice = SliceT<kPer>;
 
-// Exclusive prefix sum over the block's threads (thread order) and its total.
+// Exclusive prefix sum over the block's NW waves of threads (thread order)
+// and its total.
+template <int NW = kDenseWaves>
 __device__ uint32_t block_excl_scan(uint32_t x, uint32_t *red, uint32_t &total)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -74,7 +78,7 @@ __device__ uint32_t block_excl_scan(uint32_t x, uint32_t *red, uint32_t &total)
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kDenseWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const uint32_t v = red[i];
         off += i < wave ? v : 0u;
         tot += v;
@@ -177,23 +181,109 @@ struct CutCounter {
     __device__ uint32_t kept() const { return gt_run + (eq_run < need_eq ? eq_run : need_eq); }
 };
 
-__global__ void __launch_bounds__(kDenseThreads) select_dense_kernel(ScoreSelectParams p)
+constexpr int kCap = 8192;            // candidate list (LDS), also the sample size
+constexpr int kSampleBlock = 64;      // consecutive keys per sample block
+constexpr uint32_t kAllKeys = 0u;     // estimate: every key is a candidate
+constexpr uint32_t kNoList = 0xFFFFFFFFu;  // estimate: select from the full row
+
+struct RowView {  // one row of the dense scores
+    int64_t t, pos, P;
+    int n;
+    const uint32_t *sc;
+    uint32_t need;
+    __device__ RowView(const ScoreSelectParams &p, int64_t qrow)
+    {
+        t = p.row0 + qrow;
+        pos = p.q_pos0 + t;
+        P = visible_keys(pos, p.T, p.m, p.causal);
+        n = (int)P;
+        sc = reinterpret_cast<const uint32_t *>(p.scores + qrow * p.sstride);
+        need = (uint32_t)(n < p.ksel ? n : p.ksel);
+    }
+};
+
+// Threshold estimate of each row: the c-th best code of a sample of 128
+// blocks of 64 keys spread over the row, c about 1.5x the sample's expected
+// share of the selection plus a margin, so that the keys at or above it
+// almost always hold the whole selection and fit the candidate list.
+__global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectParams p)
 {
-    constexpr int kCap = 8192;           // candidate list (LDS), also the sample size
-    constexpr int kSampleBlock = 64;     // consecutive keys per sample block
+    __shared__ uint32_t hist[kBins1];
+    __shared__ uint32_t sample[kCap];
+    __shared__ uint32_t red[kDenseWaves];
+    __shared__ uint32_t res[3];
+    const RowView rv(p, blockIdx.x);
+    uint32_t est = kAllKeys;
+    if (rv.n > kCap) {
+        const uint32_t c =
+            (uint32_t)((3ull * rv.need * kCap) / (2ull * (uint64_t)rv.n)) + 8u;
+        est = kNoList;
+        if (c <= (uint32_t)kCap) {
+            const int spacing = (rv.n - kSampleBlock) / (kCap / kSampleBlock - 1);
+            for (int s = threadIdx.x; s < kCap; s += kDenseThreads)
+                sample[s] = ord_code(rv.sc[(s / kSampleBlock) * spacing + s % kSampleBlock]);
+            __syncthreads();
+            uint32_t est_eq;
+            bool est_exact;
+            block_exact_cut(
+                [&](auto &&f) {
+                    for (int i = threadIdx.x; i < kCap; i += kDenseThreads) f(sample[i]);
+                },
+                c, hist, red, res, est, est_exact, est_eq);
+            if (est == kNoList) est = kNoList - 1;  // keep the marker unambiguous
+        }
+    }
+    if (threadIdx.x == 0) p.est[blockIdx.x] = est;
+}
+
+// Candidates of one segment (kSeg keys) of one row: every visible key
+// whose code is >= the row's estimate, as key indices in key order, into the
+// segment's slot; the segment count is always written.
+__global__ void __launch_bounds__(kFilterThreads) filter_kernel(ScoreSelectParams p)
+{
+    __shared__ uint32_t red[kFilterThreads / 64];
+    const int seg = blockIdx.x;
+    const RowView rv(p, blockIdx.y);
+    const uint32_t est = p.est[blockIdx.y];
+    const int base = seg * kSeg;
+    const int64_t slot = (int64_t)blockIdx.y * p.nseg + seg;
+    if (est == kNoList || base >= rv.n) {
+        if (threadIdx.x == 0) p.seg_cnt[slot] = 0;
+        return;
+    }
+    Slice sl;
+    sl.load(rv.sc, base, rv.n);
+    const int j0 = base + (int)threadIdx.x * kPer;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) cnt += (j0 + i < rv.n && ord_code(sl.bits[i]) >= est) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t o = block_excl_scan<kFilterThreads / 64>(cnt, red, tot);
+    int32_t *dst = p.seg_key + slot * (int64_t)kSeg;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (j0 + i < rv.n && ord_code(sl.bits[i]) >= est) dst[o++] = j0 + i;
+    if (threadIdx.x == 0) p.seg_cnt[slot] = (int32_t)tot;
+}
+
+// Exact selection of one row and its canonical output row: from the
+// candidate list (segments concatenated in key order) when it holds the
+// selection and fits in LDS, else from the full row.
+__global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams p)
+{
     __shared__ uint32_t hist[kBins1];
     __shared__ uint32_t ccode[kCap];
     __shared__ int32_t ckey[kCap];
+    __shared__ uint32_t soff[kDenseThreads];
     __shared__ uint32_t red[kDenseWaves];
     __shared__ uint32_t res[3];
 
     const int64_t qrow = blockIdx.x;
-    const int64_t t = p.row0 + qrow;
-    const int64_t pos = p.q_pos0 + t;
-    const int64_t P = visible_keys(pos, p.T, p.m, p.causal);
-    const int n = (int)P;
-    const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scores + qrow * p.sstride);
-    const uint32_t need = (uint32_t)(n < p.ksel ? n : p.ksel);
+    const RowView rv(p, qrow);
+    const int64_t t = rv.t, pos = rv.pos, P = rv.P;
+    const int n = rv.n;
+    const uint32_t *sc = rv.sc;
+    const uint32_t need = rv.need;
     const int mexp = p.expand ? p.m : 1;
     int32_t *orow = p.idx + t * (int64_t)p.W;
     float *srow = p.sel_score ? p.sel_score + t * (int64_t)p.W : nullptr;
@@ -209,67 +299,43 @@ __global__ void __launch_bounds__(kDenseThreads) select_dense_kernel(ScoreSelect
         }
     };
 
-    // ---- candidate list: every visible key whose code is >= an estimated
-    // threshold, in key order.  The estimate is the c-th best code of a
-    // sample of 128 blocks of 64 keys spread over the row, with c about 1.5x
-    // the sample's expected share of the selection plus a margin, so the
-    // list almost always holds the whole selection and fits in LDS.  When
-    // the row itself fits, every key is a candidate.
+    // ---- the segments' candidates, concatenated in key order
     int ncand = -1;  // -1: the list is not usable, select from the full row
-    if (n <= kCap) {
-        for (int i = threadIdx.x; i < n; i += kDenseThreads) {
-            ccode[i] = ord_code(sc[i]);
-            ckey[i] = i;
+    if (p.est[qrow] != kNoList) {
+        const int nseg_row = (n + kSeg - 1) / kSeg;
+        const int32_t *cnts = p.seg_cnt + qrow * (int64_t)p.nseg;
+        const int32_t *keys = p.seg_key + qrow * (int64_t)p.nseg * kSeg;
+        uint32_t total = 0;
+        for (int s0 = 0; s0 < nseg_row; s0 += kDenseThreads) {
+            const int sg = s0 + (int)threadIdx.x;
+            uint32_t tot;
+            block_excl_scan(sg < nseg_row ? (uint32_t)cnts[sg] : 0u, red, tot);
+            total += tot;
         }
-        ncand = n;
-        __syncthreads();
-    } else {
-        const uint32_t c = (uint32_t)((3ull * need * kCap) / (2ull * (uint64_t)n)) + 8u;
-        if (c <= (uint32_t)kCap) {
-            const int spacing = (n - kSampleBlock) / (kCap / kSampleBlock - 1);
-            for (int s = threadIdx.x; s < kCap; s += kDenseThreads) {
-                const int key = (s / kSampleBlock) * spacing + s % kSampleBlock;
-                ccode[s] = ord_code(sc[key]);
-            }
-            __syncthreads();
-            uint32_t est, est_eq;
-            bool est_exact;
-            block_exact_cut(
-                [&](auto &&f) {
-                    for (int i = threadIdx.x; i < kCap; i += kDenseThreads) f(ccode[i]);
-                },
-                c, hist, red, res, est, est_exact, est_eq);
-            __syncthreads();  // the sample is dead from here on
-            // one pass over the row; the next chunk's loads are issued before
-            // this chunk is compacted
-            uint32_t total = 0;
-            Slice nxt;
-            nxt.load(sc, 0, n);
-            for (int base = 0; base < n; base += kChunk) {
-                const Slice sl = nxt;
-                if (base + kChunk < n) nxt.load(sc, base + kChunk, n);
-                const int j0 = base + (int)threadIdx.x * kPer;
-                uint32_t cnt = 0;
-#pragma unroll
-                for (int i = 0; i < kPer; ++i)
-                    cnt += (j0 + i < n && ord_code(sl.bits[i]) >= est) ? 1u : 0u;
+        if (total >= need && total <= (uint32_t)kCap) {
+            ncand = (int)total;
+            const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+            uint32_t done = 0;
+            for (int s0 = 0; s0 < nseg_row; s0 += kDenseThreads) {
+                const int sg = s0 + (int)threadIdx.x;
+                const uint32_t c = sg < nseg_row ? (uint32_t)cnts[sg] : 0u;
                 uint32_t tot;
-                uint32_t o = total + block_excl_scan(cnt, red, tot);
-#pragma unroll
-                for (int i = 0; i < kPer; ++i) {
-                    const uint32_t u = ord_code(sl.bits[i]);
-                    if (j0 + i < n && u >= est) {
-                        if (o < (uint32_t)kCap) {
-                            ccode[o] = u;
-                            ckey[o] = j0 + i;
-                        }
-                        ++o;
+                soff[threadIdx.x] = done + block_excl_scan(c, red, tot);
+                __syncthreads();
+                const int nr = nseg_row - s0 < kDenseThreads ? nseg_row - s0 : kDenseThreads;
+                for (int r = wave; r < nr; r += kDenseWaves) {  // one segment per wave
+                    const uint32_t off = soff[r];
+                    const uint32_t end = r + 1 < nr ? soff[r + 1] : done + tot;
+                    const int32_t *src = keys + (int64_t)(s0 + r) * kSeg;
+                    for (uint32_t i = lane; off + i < end; i += 64) {
+                        const int key = src[i];
+                        ccode[off + i] = ord_code(sc[key]);
+                        ckey[off + i] = key;
                     }
                 }
-                total += tot;
+                __syncthreads();
+                done += tot;
             }
-            __syncthreads();
-            if (total >= need && total <= (uint32_t)kCap) ncand = (int)total;
         }
     }
 
@@ -369,9 +435,17 @@ __global__ void __launch_bounds__(kDenseThreads) select_dense_kernel(ScoreSelect
 hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream)
 {
     if (p.nrows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(select_dense_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL(estimate_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)p.nseg, (unsigned)p.nrows), dim3(kFilterThreads),
+                       0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream, p);
     return hipGetLastError();
 }
+
+int dense_segment_keys() { return kSeg; }
 
 }  // namespace dsai

@@ -70,11 +70,16 @@ typedef struct {
     int64_t query_chunk; /* queries per launch (bounds the workspace); 0 = all */
     /* Few-query path (decode, small batches against a long key set): when
      * S <= few_query_rows, every visible score of the S rows is written to
-     * the workspace by all CUs and each row is then selected by one block;
-     * otherwise rows are scored and selected in one streaming pass per query
-     * chunk.  0 = default (64); negative = never.  Both paths give identical
-     * results.  The dense workspace (S * T * 4 bytes, T rounded up to 4) is
-     * used only while it stays within 4 GiB. */
+     * the workspace by all CUs, candidates at or above a per-row threshold
+     * estimate are filtered out by all CUs, and each row is then cut exactly
+     * by one block; otherwise rows are scored and selected in one streaming
+     * pass per query chunk.  0 = default (64); negative = never.  Both paths
+     * give identical results.  The dense workspace holds, each part starting
+     * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
+     * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
+     * G = ceil(max(T, 1) / 4096)) and the candidate keys (S * G * 4096 * 4),
+     * about 8 bytes per (row, key); it is used only while it stays within
+     * 4 GiB. */
     int64_t few_query_rows;
 } indexer_config;
 

@@ -82,16 +82,25 @@ def test_workspace_bytes_scale_with_chunk_and_selection():
     lib.indexer_destroy(h)
 
 
+def _dense_bytes(S, T):
+    """The documented few-query layout: scores, estimates, candidate counts
+    and candidate keys, each part 256-byte aligned."""
+    up = lambda x, a: -(-x // a) * a
+    G = -(-max(T, 1) // 4096)
+    return up(S * up(max(T, 1), 4) * 4, 256) + up(S * 4, 256) + up(S * G * 4, 256) + \
+        S * G * 4096 * 4
+
+
 def test_workspace_bytes_of_the_few_query_path():
     """At or below few_query_rows (default 64) the workspace holds the rows'
-    dense scores: S x T (T rounded up to 4) fp32, while that stays within
-    4 GiB; a negative setting always streams."""
+    dense scores and the selection's candidate scratch while that stays
+    within 4 GiB; a negative setting always streams."""
     n = ctypes.c_size_t()
     lib, h = _handle(chunk=16384)
     assert lib.indexer_workspace_bytes(h, 64, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == 64 * 262144 * 4
+    assert n.value == _dense_bytes(64, 262144) == 64 * 262144 * 8 + 256 + 64 * 64 * 4
     assert lib.indexer_workspace_bytes(h, 1, 1001, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == 1 * 1004 * 4
+    assert n.value == _dense_bytes(1, 1001) == 4096 + 256 + 256 + 4096 * 4
     assert lib.indexer_workspace_bytes(h, 65, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 65 * 20736 * 8            # above the default: streaming buffers
     assert lib.indexer_workspace_bytes(h, 64, 2 ** 25, 64, 128, 1, 2048, ctypes.byref(n)) == 0
@@ -103,7 +112,7 @@ def test_workspace_bytes_of_the_few_query_path():
     lib.indexer_destroy(h)
     lib, h = _handle(few=1000)
     assert lib.indexer_workspace_bytes(h, 1000, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == 1000 * 4096 * 4
+    assert n.value == _dense_bytes(1000, 4096)
     lib.indexer_destroy(h)
 
 
