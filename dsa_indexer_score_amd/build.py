@@ -13,12 +13,14 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
-SOURCES = ["score_select.hip", "select_dense.hip", "pair_overlap.hip", "indexer_api.cpp"]
+SOURCES = ["score_select.hip", "score_rows.hip", "select_dense.hip", "pair_overlap.hip",
+           "indexer_api.cpp"]
 
 # Per-file extra flags.  The scoring kernel assumes finite inputs (a documented
 # precondition), so IEEE NaN quieting is switched off there: ReLU then lowers
 # to a single v_max_f32 instead of a canonicalising max followed by the max.
-FILE_FLAGS = {"score_select.hip": ["-fno-honor-nans", "-Xclang", "-mno-amdgpu-ieee"]}
+_NO_NAN = ["-fno-honor-nans", "-Xclang", "-mno-amdgpu-ieee"]
+FILE_FLAGS = {"score_select.hip": _NO_NAN, "score_rows.hip": _NO_NAN}
 
 # Packed fp32 VALU ops are kept out of the generated code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

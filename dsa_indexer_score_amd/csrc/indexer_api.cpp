@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/dsa_indexer.h: argument checks,
 // output-width and workspace arithmetic, the query-chunk loop and launches.
 // Nothing here computes scores or selections; every step of the indexer runs
-// in the HIP kernels (score_select.hip, select_dense.hip, pair_overlap.hip).
+// in the HIP kernels (score_select.hip, score_rows.hip, select_dense.hip,
+// pair_overlap.hip).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -71,6 +72,7 @@ int64_t rows_per_launch(const indexer_config &cfg, int64_t S)
 constexpr int64_t kFewRowsDefault = 64;
 constexpr int64_t kDenseMaxBytes = int64_t(1) << 32;
 constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
+constexpr int64_t kRowsKernelMax = 2;  // rows scored with q in registers, keys from HBM
 
 int64_t dense_stride(int64_t T) { return round_up(std::max<int64_t>(T, 1), 4); }
 
@@ -285,7 +287,10 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.split_keys = tiles_per * dsai::kKeysPerTile;
         p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
         bool supported = true;
-        hipError_t e = dsai::launch_score_select(cfg.dtype, nb, d, true, false, p, st, &supported);
+        hipError_t e = S <= kRowsKernelMax
+                           ? dsai::launch_score_rows(cfg.dtype, nb, d, p, st, &supported)
+                           : dsai::launch_score_select(cfg.dtype, nb, d, true, false, p, st,
+                                                       &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
         e = dsai::launch_select_dense(p, st);

@@ -62,6 +62,12 @@ constexpr int kSelGroup = 64;         // keys appended per selection step (one p
 hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen,
                                const ScoreSelectParams &p, hipStream_t stream, bool *supported);
 
+// Dense scores of one or two rows (p.scores, as the dense mode of
+// launch_score_select writes them, bit for bit), every CU streaming its own
+// slice of the keys.
+hipError_t launch_score_rows(int dtype, int nb, int d, const ScoreSelectParams &p,
+                             hipStream_t stream, bool *supported);
+
 // Exact top-k of each row's dense scores and its canonical output row:
 // threshold estimate per row, candidate filter per (row, key chunk), exact
 // cut and output per row.

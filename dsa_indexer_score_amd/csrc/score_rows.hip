@@ -1,0 +1,198 @@
+// score_rows: dense scoring of one or two query rows (decode) for gfx950.
+//
+// Writes, for every key j visible to row t,
+//     s_tj = sum_h w[t,h] * ReLU(q[t,h,:] . k[j,:])
+// (DoSA: Dots Sparse Attention, summary page, "Prerequisites") into the row's
+// dense score array, which the few-query selection then cuts exactly.  The
+// dot products use the same MFMA operands and instruction order as the fused
+// streaming kernel, and the signed-ReLU head sum the same fma order (head
+// block by head block, accumulator element by element, then the two lane
+// halves, then k_scale), so every score is bit-identical to the one the
+// streaming selection sees.
+//
+// Why a kernel of its own: the streaming kernel's block shares each LDS key
+// tile among 8 waves that hold 8 different rows; with one row, 7 of them idle
+// and each block walks its key range through barriers.  Here every wave holds
+// the rows' q operands in registers and owns a run of 64-key groups of one
+// row slab; it loads its keys' B operands straight from global memory (each
+// lane the contiguous half of one key row that its MFMA slots cover, so 32
+// keys arrive as whole rows), one group ahead, with no LDS and no barrier.
+// All CUs stream disjoint slices of the key set, so one row is bound by
+// reading the keys from HBM.  Slabs of the same key range sit in blocks a
+// multiple of 8 apart, so they land on the same XCD and share its L2.
+#include "kernels.h"
+#include "mfma_ops.h"
+#include "select_common.h"
+
+namespace dsai {
+namespace {
+
+constexpr int kRowsWaves = 4;
+constexpr int kRowsThreads = kRowsWaves * 64;
+constexpr int kTargetWaves = 1024;  // about one wave per SIMD; each streams several groups
+
+template <int DT, int NB, int D, int SQ>
+__global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectParams p, int gpw)
+{
+    using O = Op<DT, D>;
+    using A = typename O::A;
+    constexpr int KS = O::KS, ES = O::ES, RAW = O::RAW;
+    constexpr int64_t ROWB = (int64_t)D * ES;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int hh = lane >> 5, l32 = lane & 31;
+
+    // rows of this slab and the keys they see
+    const int64_t r0 = (int64_t)blockIdx.y * SQ;
+    int64_t Pq[SQ];
+    int64_t Pmax = 0;
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        const int64_t r = r0 + i;
+        Pq[i] = r < p.nrows ? visible_keys(p.q_pos0 + p.row0 + r, p.T, p.m, p.causal) : 0;
+        Pmax = Pq[i] > Pmax ? Pq[i] : Pmax;
+    }
+    const int64_t ngroups = (Pmax + kSelGroup - 1) / kSelGroup;
+    const int64_t g0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * gpw;
+    if (g0 >= ngroups) return;
+    const int64_t g1 = g0 + gpw < ngroups ? g0 + gpw : ngroups;
+
+    // q operands and folded head weights of the slab's rows.  Every load is
+    // issued unconditionally from a clamped, valid address and masked
+    // afterwards, so the loads are in flight together instead of one
+    // branch (and one wait) each.
+    A qa[SQ][NB][KS];
+    float wv[SQ][NB][16];
+    const char *qbytes = static_cast<const char *>(p.q);
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        const bool active = r0 + i < p.nrows;
+        const int64_t t = p.row0 + (active ? r0 + i : 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int head = 32 * b + l32;
+            const bool okq = active && head < p.H;
+            O::load_a(qbytes + ((t * p.H + (okq ? head : 0)) * (int64_t)D) * ES, hh, qa[i][b]);
+            if (!okq) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qa[i][b][ks] = O::zero();
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int h2 = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
+                const bool ok = active && h2 < p.H;
+                const int hc = ok ? h2 : 0;
+                float wt = p.w[t * p.w_stride + hc];
+                if (DT == 2) wt *= p.q_scale[t * p.H + hc];
+                wv[i][b][v] = ok ? wt : 0.f;
+            }
+        }
+    }
+
+    // B operands of one 64-key group: column block c holds keys 64g + 32c + l32.
+    // A key at or past T is read at key T - 1 instead: column j of the
+    // product depends on key j alone, and such keys' scores are never stored.
+    const char *kbytes = static_cast<const char *>(p.k);
+    uint4 raw[2][RAW], nraw[2][RAW];
+    float ksc = 0.f, nksc = 0.f;
+    auto load_group = [&](int64_t g, uint4 (&dst)[2][RAW], float &sc) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int64_t key = g * kSelGroup + 32 * c + l32;
+            raw_row<O, D>(kbytes + (key < p.T ? key : p.T - 1) * ROWB, hh, dst[c]);
+        }
+        if (DT == 2) {
+            const int64_t key = g * kSelGroup + lane;
+            sc = p.k_scale[key < p.T ? key : p.T - 1];
+        }
+    };
+
+    load_group(g0, raw, ksc);
+    for (int64_t g = g0; g < g1; ++g) {
+        if (g + 1 < g1) load_group(g + 1, nraw, nksc);
+        float part[SQ][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            A bfr[KS];
+            O::from_raw(raw[c], bfr);
+#pragma unroll
+            for (int i = 0; i < SQ; ++i) {
+                float e = 0.f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    f32x16 acc;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) acc = O::mma(qa[i][b][ks], bfr[ks], acc);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) e = fmaf(wv[i][b][v], fmaxf(acc[v], 0.f), e);
+                }
+                part[i][c] = e;
+            }
+        }
+        const int64_t key = g * kSelGroup + lane;  // the key whose score this lane finishes
+#pragma unroll
+        for (int i = 0; i < SQ; ++i) {
+            // lanes < 32 own keys 0..31 of the group, lanes >= 32 keys 32..63:
+            // each adds the two 16-head halves of its key's sum
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[i][0]),
+                                                             __float_as_uint(part[i][1]), false,
+                                                             false);
+            float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (DT == 2) s *= ksc;
+            if (key < Pq[i]) p.scores[(r0 + i) * p.sstride + key] = s;
+        }
+        if (g + 1 < g1) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int x = 0; x < RAW; ++x) raw[c][x] = nraw[c][x];
+            ksc = nksc;
+        }
+    }
+}
+
+template <int DT, int NB, int D, int SQ>
+hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
+{
+    // the last row sees the most keys
+    const int64_t pmax = visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
+    const int64_t ngroups = (pmax + kSelGroup - 1) / kSelGroup;
+    const int64_t nslab = (p.nrows + SQ - 1) / SQ;
+    if (ngroups <= 0 || nslab <= 0) return hipSuccess;
+    int64_t gpw = (ngroups * nslab + kTargetWaves - 1) / kTargetWaves;
+    gpw = gpw < 1 ? 1 : gpw;
+    const int64_t waves = (ngroups + gpw - 1) / gpw;
+    const int64_t blocks = ((waves + kRowsWaves - 1) / kRowsWaves + 7) / 8 * 8;
+    hipLaunchKernelGGL((score_rows_kernel<DT, NB, D, SQ>), dim3((unsigned)blocks, (unsigned)nslab),
+                       dim3(kRowsThreads), 0, stream, p, (int)gpw);
+    return hipGetLastError();
+}
+
+template <int DT, int NB, int D>
+hipError_t launch_sq(const ScoreSelectParams &p, hipStream_t stream)
+{
+    return p.nrows == 1 ? launch_rows<DT, NB, D, 1>(p, stream)
+                        : launch_rows<DT, NB, D, 2>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_score_rows(int dtype, int nb, int d, const ScoreSelectParams &p,
+                             hipStream_t stream, bool *supported)
+{
+    *supported = true;
+#define DSAI_CASE(DT, NB, D) \
+    if (dtype == DT && nb == NB && d == D) return launch_sq<DT, NB, D>(p, stream);
+    DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
+    DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
+    DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)
+    DSAI_CASE(2, 2, 32) DSAI_CASE(2, 2, 64) DSAI_CASE(2, 2, 128)
+    DSAI_CASE(0, 1, 32) DSAI_CASE(0, 1, 64)
+    DSAI_CASE(0, 2, 32) DSAI_CASE(0, 2, 64)
+#undef DSAI_CASE
+    *supported = false;
+    return hipSuccess;
+}
+
+}  // namespace dsai

@@ -63,131 +63,13 @@
 //    pools expand to m positions and the incomplete tail follows
 //    (GLM-5.3-Flash Module 06 "DSA & KPool", section 2), then -1 padding.
 #include "kernels.h"
+#include "mfma_ops.h"
 #include "select_common.h"
 
 namespace dsai {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kThreads = kQueriesPerBlock * 64;
-
-// ---------------------------------------------------------------------------
-// MFMA operand handling.  For every dtype, lane (hh = lane / 32, r = lane % 32)
-// supplies row r of A and column r of B; the contraction slots a lane owns
-// are the contiguous half d in [hh*D/2, hh*D/2 + D/2), split into KS steps.
-// A and B use the same slot -> d map, so the products pair up correctly.
-// ---------------------------------------------------------------------------
-template <int DT, int D> struct Op;
-
-template <int D> struct Op<1, D> {  // bf16
-    using A = bf16x8;
-    static constexpr int ES = 2, KS = D / 16, NCH = D * 2 / 16, GCH = NCH;
-    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
-    {
-        tile[r * NCH + (gch ^ swz)] = v;
-    }
-    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
-    {
-        const uint4 *p = reinterpret_cast<const uint4 *>(row + hh * (D / 2) * 2);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a[ks] = __builtin_bit_cast(A, p[ks]);
-    }
-    __device__ static void load_b(const uint4 *tile, int r, int hh, int swz, A (&b)[KS])
-    {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            b[ks] = __builtin_bit_cast(A, tile[r * NCH + ((hh * KS + ks) ^ swz)]);
-    }
-    __device__ static void load_b_one(const uint4 *tile, int r, int hh, int swz, int ks, A &b)
-    {
-        b = __builtin_bit_cast(A, tile[r * NCH + ((hh * KS + ks) ^ swz)]);
-    }
-    __device__ static f32x16 mma(A a, A b, f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static A zero() { return __builtin_bit_cast(A, make_uint4(0, 0, 0, 0)); }
-};
-
-// OCP e4m3 codes, widened exactly to bf16 (every e4m3 value is a bf16 value)
-// and contracted on the bf16 MFMA with fp32 accumulation.  The native
-// f8f6f4 MFMA is not used: its 64-product dot is accumulated at reduced
-// precision (measured on gfx950: error up to 2^-12 of the sum of |products|
-// on random codes, 2^-15 on normal-like data), against 2^-24 for bf16.
-template <int D> struct Op<2, D> : Op<1, D> {
-    using A = bf16x8;
-    static constexpr int ES = 1, KS = D / 16, NCH = D * 2 / 16, GCH = D / 16;
-    template <bool HI> __device__ static uint32_t widen2(uint32_t w)
-    {
-        auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
-        return __builtin_bit_cast(uint32_t, v);
-    }
-    // 16 fp8 codes -> two 16-B chunks of 8 bf16
-    __device__ static void widen16(uint4 x, uint4 &lo, uint4 &hi)
-    {
-        lo = make_uint4(widen2<false>(x.x), widen2<true>(x.x), widen2<false>(x.y), widen2<true>(x.y));
-        hi = make_uint4(widen2<false>(x.z), widen2<true>(x.z), widen2<false>(x.w), widen2<true>(x.w));
-    }
-    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
-    {
-        const uint4 *p = reinterpret_cast<const uint4 *>(row + hh * (D / 2));
-#pragma unroll
-        for (int c = 0; c < KS / 2; ++c) {
-            uint4 lo, hi;
-            widen16(p[c], lo, hi);
-            a[2 * c] = __builtin_bit_cast(A, lo);
-            a[2 * c + 1] = __builtin_bit_cast(A, hi);
-        }
-    }
-    // global chunk gch of a key row (16 codes) -> LDS chunks 2*gch, 2*gch+1
-    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
-    {
-        uint4 lo, hi;
-        widen16(v, lo, hi);
-        tile[r * NCH + ((2 * gch) ^ swz)] = lo;
-        tile[r * NCH + ((2 * gch + 1) ^ swz)] = hi;
-    }
-};
-
-template <int D> struct Op<0, D> {  // fp32
-    using A = float;
-    static constexpr int ES = 4, KS = D / 2, NCH = D * 4 / 16, GCH = NCH;
-    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
-    {
-        tile[r * NCH + (gch ^ swz)] = v;
-    }
-    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
-    {
-        const float4 *p = reinterpret_cast<const float4 *>(row + hh * (D / 2) * 4);
-#pragma unroll
-        for (int c = 0; c < KS / 4; ++c) {
-            float4 v = p[c];
-            a[4 * c] = v.x; a[4 * c + 1] = v.y; a[4 * c + 2] = v.z; a[4 * c + 3] = v.w;
-        }
-    }
-    __device__ static void load_b(const uint4 *tile, int r, int hh, int swz, A (&b)[KS])
-    {
-#pragma unroll
-        for (int c = 0; c < KS / 4; ++c) {
-            uint4 v = tile[r * NCH + ((hh * (KS / 4) + c) ^ swz)];
-            b[4 * c] = __uint_as_float(v.x); b[4 * c + 1] = __uint_as_float(v.y);
-            b[4 * c + 2] = __uint_as_float(v.z); b[4 * c + 3] = __uint_as_float(v.w);
-        }
-    }
-    __device__ static void load_b_one(const uint4 *tile, int r, int hh, int swz, int ks, A &b)
-    {
-        const uint4 v = tile[r * NCH + ((hh * (KS / 4) + ks / 4) ^ swz)];
-        const uint32_t w = ks % 4 == 0 ? v.x : ks % 4 == 1 ? v.y : ks % 4 == 2 ? v.z : v.w;
-        b = __uint_as_float(w);
-    }
-    __device__ static f32x16 mma(A a, A b, f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-    }
-    __device__ static A zero() { return 0.f; }
-};
 
 template <int DT, int NB, int D, bool DENSE, bool VARLEN>
 __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectParams p)
@@ -272,28 +154,30 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     uint32_t *hist = hist_all[wave];
     if (!DENSE) hist_clear(hist, lane);
 
-    // q fragments and folded head weights of this wave's query
+    // q fragments and folded head weights of this wave's query; every load
+    // is issued from a clamped, valid address and masked afterwards, so the
+    // loads are in flight together rather than one branch and wait each
     A qa[NB][KS];
     float wv[NB][16];
     const char *qbytes = static_cast<const char *>(p.q);
+    const int64_t tq = active ? t : p.row0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int head = 32 * b + l32;
-        if (active && head < p.H) {
-            O::load_a(qbytes + ((t * p.H + head) * (int64_t)D) * ES, hh, qa[b]);
-        } else {
+        const bool okq = active && head < p.H;
+        O::load_a(qbytes + ((tq * p.H + (okq ? head : 0)) * (int64_t)D) * ES, hh, qa[b]);
+        if (!okq) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) qa[b][ks] = O::zero();
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int h2 = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
-            float wt = 0.f;
-            if (active && h2 < p.H) {
-                wt = p.w[t * p.w_stride + h2];
-                if (DT == 2) wt *= p.q_scale[t * p.H + h2];
-            }
-            wv[b][v] = wt;
+            const bool ok = active && h2 < p.H;
+            const int hc = ok ? h2 : 0;
+            float wt = p.w[tq * p.w_stride + hc];
+            if (DT == 2) wt *= p.q_scale[tq * p.H + hc];
+            wv[b][v] = ok ? wt : 0.f;
         }
     }
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ void wave_sync_mem()
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ int64_t visible_keys(int64_t pos, int64_t T, int m, int causal)
+__host__ __device__ __forceinline__ int64_t visible_keys(int64_t pos, int64_t T, int m, int causal)
 {
     if (!causal) return T;
     int64_t c = (pos + 1) / m;

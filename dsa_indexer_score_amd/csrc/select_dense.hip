@@ -3,20 +3,22 @@
 // For a handful of query rows (decode, small batches against a long key
 // set) the scoring kernel runs in its dense mode and writes each row's
 // visible scores to the workspace (a [rows, T] array: kilobytes to tens of
-// megabytes here, never the prefill-sized tensor).  This kernel then gives
-// every row one 1024-thread block and finds the same exact result as the
-// streaming selection -- the Ksel best keys under the total order (higher
-// score first, equal scores to the lower key index, DoSA summary,
-// "Prerequisites") written in ascending key order ("Adjacent-Query KV-Index
-// Overlap in 256K DSA Training", section 3), expanded and followed by the
-// tail (GLM-5.3-Flash Module 06 "DSA & KPool", section 2):
-//  1. candidates: a sample of the row (128 blocks of 64 keys) gives an
-//     estimated threshold a little below the expected Ksel-th score; one
-//     pass keeps every key at or above it, in key order, in an LDS list.  The
-//     true selection is contained in that list whenever the list holds at
-//     least Ksel keys (all of them are >= the estimate, so the Ksel-th best
-//     is too); otherwise -- or if the list overflows, e.g. under massive
-//     ties -- the steps below run over the full row instead;
+// megabytes here, never the prefill-sized tensor).  Three kernels then find
+// the same exact result as the streaming selection -- the Ksel best keys
+// under the total order (higher score first, equal scores to the lower key
+// index, DoSA summary, "Prerequisites") written in ascending key order
+// ("Adjacent-Query KV-Index Overlap in 256K DSA Training", section 3),
+// expanded and followed by the tail (GLM-5.3-Flash Module 06 "DSA & KPool",
+// section 2):
+//  1. candidates: per row, a sample (128 blocks of 64 keys) gives an
+//     estimated threshold a little below the expected Ksel-th score
+//     (estimate_kernel); per (row, 4096-key segment), every key at or above
+//     it is kept in key order (filter_kernel, all CUs); per row, the
+//     segments are concatenated in order into an LDS list (finish_kernel).
+//     The true selection is contained in that list whenever the list holds
+//     at least Ksel keys (all of them are >= the estimate, so the Ksel-th
+//     best is too); otherwise -- or if the list would overflow, e.g. under
+//     massive ties -- the steps below run over the full row instead;
 //  2. exact cut: a 4096-bin histogram of the order codes' top 12 bits gives
 //     the bin holding the Ksel-th code; if that bin does not end the
 //     selection exactly, two more 10-bit histograms over the codes of that
@@ -275,6 +277,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
     __shared__ uint32_t ccode[kCap];
     __shared__ int32_t ckey[kCap];
     __shared__ uint32_t soff[kDenseThreads];
+    __shared__ uint16_t owner[kCap];
     __shared__ uint32_t red[kDenseWaves];
     __shared__ uint32_t res[3];
 
@@ -322,15 +325,32 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
                 uint32_t tot;
                 soff[threadIdx.x] = done + block_excl_scan(c, red, tot);
                 __syncthreads();
+                // owner segment of each list slot of this round (LDS only) ...
                 const int nr = nseg_row - s0 < kDenseThreads ? nseg_row - s0 : kDenseThreads;
-                for (int r = wave; r < nr; r += kDenseWaves) {  // one segment per wave
+                for (int r = wave; r < nr; r += kDenseWaves) {
                     const uint32_t off = soff[r];
                     const uint32_t end = r + 1 < nr ? soff[r + 1] : done + tot;
-                    const int32_t *src = keys + (int64_t)(s0 + r) * kSeg;
-                    for (uint32_t i = lane; off + i < end; i += 64) {
-                        const int key = src[i];
-                        ccode[off + i] = ord_code(sc[key]);
-                        ckey[off + i] = key;
+                    for (uint32_t i = off + lane; i < end; i += 64) owner[i] = (uint16_t)r;
+                }
+                __syncthreads();
+                // ... then one slot per thread and step, every load independent
+                constexpr int kSlots = kCap / kDenseThreads;
+                int kk[kSlots];
+#pragma unroll
+                for (int x = 0; x < kSlots; ++x) {
+                    const uint32_t i = done + threadIdx.x + (uint32_t)x * kDenseThreads;
+                    kk[x] = 0;
+                    if (i < done + tot) {
+                        const int r = owner[i];
+                        kk[x] = keys[(int64_t)(s0 + r) * kSeg + (i - soff[r])];
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < kSlots; ++x) {
+                    const uint32_t i = done + threadIdx.x + (uint32_t)x * kDenseThreads;
+                    if (i < done + tot) {
+                        ccode[i] = ord_code(sc[kk[x]]);
+                        ckey[i] = kk[x];
                     }
                 }
                 __syncthreads();

@@ -1,5 +1,5 @@
-"""The few-query path (dense scores + one selection block per row) against
-the streaming path and the oracle.
+"""The few-query path (dense scores + candidate filter + exact cut per row)
+against the streaming path and the oracle.
 
 Both paths share the scoring arithmetic and implement the same exact
 selection, so on the same inputs they must agree bit for bit (indices,
@@ -59,6 +59,40 @@ def test_few_query_path_is_bit_identical_to_streaming(name, S, T, topk):
     log(f"  {name} S={S} T={T}: valid_len {dense[1].min().item()}..{dense[1].max().item()}")
 
 
+DECODE_T = {"c4_csa_256k": 65536, "c5_csa_1m": 262144, "c3_dsa_token": 131072,
+            "c2_glm_pooled": 8192, "c1_tiny_int": 1024}
+
+
+@pytest.mark.parametrize("S", [1, 2])
+@pytest.mark.parametrize("name", list(DECODE_T))
+def test_one_and_two_rows_bit_identical_to_streaming(name, S):
+    """One or two rows are scored by the register-resident row kernel; its
+    scores, and so the selections, equal the streaming kernel's bit for bit."""
+    inp = _decode(name, S, DECODE_T[name])
+    _assert_identical(*_both_paths(inp))
+
+
+@pytest.mark.parametrize("dtype,H,d", [(torch.float32, 17, 32), (torch.float32, 40, 64),
+                                       (torch.bfloat16, 5, 32), (torch.bfloat16, 33, 64),
+                                       (torch.float8_e4m3fn, 64, 32),
+                                       (torch.float8_e4m3fn, 20, 64),
+                                       (torch.float8_e4m3fn, 48, 128)])
+def test_one_and_two_rows_every_operand_shape(dtype, H, d):
+    """Every (dtype, head blocks, d) instance of the row kernel, with missing
+    heads, a ragged key count and rows that do not see every key."""
+    g = torch.Generator().manual_seed(H * 1000 + d)
+    T = 3001
+    for S in (1, 2):
+        q = torch.randn(S, H, d, generator=g).to(dtype)
+        k = torch.randn(T, d, generator=g).to(dtype)
+        w = torch.randn(S, H, generator=g)
+        fp8 = dtype == torch.float8_e4m3fn
+        inp = gen.custom(q=q, k=k, w=w, topk=200, q_pos0=T - 40,
+                         q_scale=torch.rand(S, H, generator=g) + 0.5 if fp8 else None,
+                         k_scale=torch.rand(T, generator=g) + 0.5 if fp8 else None).to(DEV)
+        _assert_identical(*_both_paths(inp))
+
+
 def test_few_query_path_prefix_rows_and_non_causal():
     """Rows at the start of the context (few visible keys, empty rows) and a
     non-causal ragged problem take the same results through both paths."""
@@ -69,7 +103,8 @@ def test_few_query_path_prefix_rows_and_non_causal():
     _assert_identical(*_both_paths(inp))
 
 
-@pytest.mark.parametrize("name,S,T", [("c5_csa_1m", 3, 262144), ("c4_csa_256k", 8, 65536),
+@pytest.mark.parametrize("name,S,T", [("c5_csa_1m", 1, 262144), ("c4_csa_256k", 2, 65536),
+                                      ("c5_csa_1m", 3, 262144), ("c4_csa_256k", 8, 65536),
                                       ("c2_glm_pooled", 5, 8192)])
 def test_decode_rows_match_oracle(name, S, T):
     inp = _decode(name, S, T)
