@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer (q,k,head) triples/s + queries/s at S=256K,H=64; % MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}  # fp8 codes run on the bf16 MFMA
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", "score_select.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", f) for f in
+               ("score_select.hip", "mfma_ops.h", "select_common.h", "kernels.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_select_c4_csa_256k_pmc.md")
 
 
@@ -59,8 +60,12 @@ def visible_pairs(S, T, m, causal, q_pos0=0):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the sources the streaming kernel is compiled from."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic():
