@@ -11,6 +11,10 @@
 // loading the two rows, not by the latency of a search; rows of up to 2304
 // entries are loaded once into registers (one memory round trip per pair).
 // Ranges wider than the bitmap are covered in consecutive windows.
+// With few pairs (decode: a handful of rows spread over the whole context)
+// one wave per pair would leave the chip idle and walk many small windows,
+// so each pair gets a 1024-thread block and a 128 KB bitmap instead, which
+// covers 2^20 positions per window (a 4M-token context in four).
 // shared[i] counts the entries of row 2i present in row 2i+1.
 #include "kernels.h"
 
@@ -22,6 +26,10 @@ constexpr int kWords = 2048;                 // 8 KB of bitmap per wave
 constexpr int64_t kWindow = (int64_t)kWords * 32;
 constexpr int kRegPerLane = 36;              // rows up to 2304 entries stay in registers
 constexpr int kUnroll = 8;                   // row entries in flight per lane (long rows)
+constexpr int kWideThreads = 1024;           // few pairs: one block per pair ...
+constexpr int kWideWords = 32768;            // ... with 128 KB of bitmap
+constexpr int64_t kWideWindow = (int64_t)kWideWords * 32;
+constexpr int64_t kWidePairsMax = 512;       // at most this many pairs take the block path
 
 __device__ __forceinline__ void wave_sync_lds()
 {
@@ -140,6 +148,52 @@ __global__ void __launch_bounds__(kWaves * 64) pair_overlap_kernel(const int32_t
     if (lane == 0) shared[pr] = c;
 }
 
+__global__ void __launch_bounds__(kWideThreads) pair_overlap_wide_kernel(
+    const int32_t *idx, const int32_t *valid_len, int W, int32_t *shared)
+{
+    __shared__ __align__(16) uint32_t bm[kWideWords];
+    __shared__ int red[kWideThreads / 64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t pr = blockIdx.x;
+    const int32_t *a = idx + (2 * pr) * (int64_t)W;
+    const int32_t *b = a + W;
+    int va = valid_len[2 * pr], vb = valid_len[2 * pr + 1];
+    va = va < 0 ? 0 : (va > W ? W : va);
+    vb = vb < 0 ? 0 : (vb > W ? W : vb);
+    int c = 0;
+    if (va > 0 && vb > 0) {  // block-uniform
+        const int64_t lo = a[0] < b[0] ? a[0] : b[0];
+        const int64_t hi = a[va - 1] > b[vb - 1] ? a[va - 1] : b[vb - 1];
+        for (int64_t w0 = lo; w0 <= hi; w0 += kWideWindow) {
+            const int64_t nbits = hi - w0 + 1 < kWideWindow ? hi - w0 + 1 : kWideWindow;
+            const int nq = (int)((nbits + 127) >> 7);  // 16-byte words of bitmap in use
+            uint4 *bm4 = reinterpret_cast<uint4 *>(bm);
+            for (int i = threadIdx.x; i < nq; i += kWideThreads) bm4[i] = make_uint4(0, 0, 0, 0);
+            __syncthreads();
+            for (int e = threadIdx.x; e < vb; e += kWideThreads) {
+                const int64_t r = (int64_t)b[e] - w0;
+                if (r >= 0 && r < nbits) atomicOr(&bm[r >> 5], 1u << (r & 31));
+            }
+            __syncthreads();
+            for (int e = threadIdx.x; e < va; e += kWideThreads) {
+                const int64_t r = (int64_t)a[e] - w0;
+                if (r >= 0 && r < nbits) c += (bm[r >> 5] >> (r & 31)) & 1u;
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) red[wave] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < kWideThreads / 64; ++i) sum += red[i];
+        shared[pr] = sum;
+    }
+}
+
 // Three-region split of each pair (Overlap page, sections 6.1 and 6.4): the
 // entries both rows hold, those only row 2i holds and those only row 2i+1
 // holds, each ascending, written into fixed-capacity rows of width W (then
@@ -225,6 +279,11 @@ hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int
                                int W, int32_t *shared, hipStream_t stream)
 {
     if (npairs <= 0) return hipSuccess;
+    if (npairs <= kWidePairsMax) {
+        hipLaunchKernelGGL(pair_overlap_wide_kernel, dim3((unsigned)npairs), dim3(kWideThreads), 0,
+                           stream, idx, valid_len, W, shared);
+        return hipGetLastError();
+    }
     const int64_t blocks = (npairs + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(pair_overlap_kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream,
                        idx, valid_len, npairs, W, shared);

@@ -301,6 +301,12 @@ def test_pair_overlap_wide_ranges_and_ragged_rows(W):
     assert want.max() > 0 and (want == 0).any()
     if W > 2304:
         assert (vl > 2304).any()
+    # 150 pairs take the block-per-pair kernel; the same pairs repeated into a
+    # batch of 600 take the wave-per-pair kernel
+    big = torch.from_numpy(np.tile(idx[:300], (4, 1))).to(DEV)
+    big_vl = torch.from_numpy(np.tile(vl[:300], 4)).to(DEV)
+    shared4 = dsai.pair_overlap(big, big_vl)
+    assert np.array_equal(shared4.cpu().numpy(), np.tile(want[:150], 4))
 
 
 @pytest.mark.parametrize("W", [2051, 5000])
