@@ -29,7 +29,10 @@ Choices the page leaves open, and the reading taken: the anchor of an
 omitted positive head is the kept positive head maximising
 [q_h . q_j]_+ / ||q_j|| (the one that removes the most of q_h); when no
 positive head is kept the omitted positive heads are bounded by
-w_h ||q_h|| ||k|| alone; the seed set is supplied by the caller.  The joint
+w_h ||q_h|| ||k|| alone; the seed set is supplied by the caller, and with
+an empty seed set every activation frequency p_h is taken as 1/2 (the
+negative-head priority is then |w_h| ||q_h|| / 2) and no omitted negative
+head counts as majority-active (the aggregate a_A is zero).  The joint
 residual bound (a tightening of E) is not used: the plain allowance is
 already a valid certificate.
 """
@@ -54,7 +57,8 @@ def certificate(q: np.ndarray, w: np.ndarray, seed_keys: np.ndarray, r: int):
     w = np.asarray(w, np.float64)
     H = q.shape[0]
     X = q @ np.asarray(seed_keys, np.float64).T
-    p = (X > 0).mean(axis=1) if X.shape[1] else np.zeros(H)
+    # no seed keys: no activation statistics, every p_h taken as 1/2
+    p = (X > 0).mean(axis=1) if X.shape[1] else np.full(H, 0.5)
     norms = np.linalg.norm(q, axis=1)
     pos = [h for h in range(H) if w[h] > 0]
     neg = [h for h in range(H) if w[h] < 0]
@@ -75,7 +79,8 @@ def certificate(q: np.ndarray, w: np.ndarray, seed_keys: np.ndarray, r: int):
             E += w[h] * np.linalg.norm(q[h] - beta * q[j])
         else:
             E += w[h] * norms[h]
-    A = [h for h in neg if h not in kept and p[h] >= 0.5]
+    # the majority-active set needs activation evidence: empty without seeds
+    A = [h for h in neg if h not in kept and p[h] >= 0.5] if X.shape[1] else []
     aA = np.zeros(q.shape[1])
     for h in A:
         aA += abs(w[h]) * q[h]

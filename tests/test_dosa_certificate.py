@@ -61,6 +61,28 @@ def test_positive_multiple_folds_exactly():
                                atol=1e-12)
 
 
+def test_without_seeds_negative_heads_rank_by_weighted_norm():
+    """An empty seed set: p_h = 1/2 for every head, so with at most r
+    positive heads the remaining budget goes to the negative heads of
+    largest |w_h| ||q_h||, no head is majority-active, and the bound still
+    holds."""
+    rng = np.random.default_rng(12)
+    H, d = 48, 16
+    q = rng.standard_normal((H, d))
+    w = rng.standard_normal(H)
+    w[:10] = np.abs(w[:10]) + 0.1                      # 10 positive heads ...
+    w[10:] = -np.abs(w[10:]) - 0.1                     # ... and 38 negative ones
+    cert = dosa.certificate(q, w, np.zeros((0, d)), r=32)
+    neg = np.arange(10, H)
+    want_neg = neg[np.argsort(-(np.abs(w[neg]) * np.linalg.norm(q[neg], axis=1)),
+                              kind="stable")[:22]]
+    assert sorted(cert["kept"]) == sorted(list(range(10)) + want_neg.tolist())
+    assert cert["E"] == 0.0                            # every positive head is kept
+    assert not cert["aA"].any()                        # no activation evidence, A empty
+    keys = rng.standard_normal((500, d))
+    assert np.all(dosa.upper_bounds(cert, keys) >= _scores(q, w, keys) - 1e-9)
+
+
 def test_seed_threshold_is_a_lower_bound_of_the_kth_score():
     rng = np.random.default_rng(5)
     s = rng.standard_normal(5000)
