@@ -127,6 +127,8 @@ def main():
                          "pools, causality and keys) and time the varlen entry point")
     ap.add_argument("--regions", action="store_true",
                     help="also time the three-region q-cluster split of the adjacent pairs")
+    ap.add_argument("--screen", action="store_true",
+                    help="DoSA certificate screening on the streaming path (lossless)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="few-query shape: N query rows at the end of the workload's full "
                          "context (every key visible), timed through the few-query path")
@@ -160,7 +162,8 @@ def main():
 
     ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
                       query_chunk=inp.query_chunk or 0,
-                      few_query_rows=max(64, args.decode) if args.decode else 0, device=dev)
+                      few_query_rows=max(64, args.decode) if args.decode else 0,
+                      screen=args.screen, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
     docs = None
     if args.varlen:
@@ -229,7 +232,7 @@ def main():
     score_s = float(np.mean(score_ms)) / 1e3
     achieved_tflops = flops / score_s / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
-    traffic = stored_traffic() if not (args.decode or args.varlen) else None
+    traffic = stored_traffic() if not (args.decode or args.varlen or args.screen) else None
 
     st = dsai.overlap_summary(shared, vl)
     regions = None
@@ -300,7 +303,8 @@ def main():
         "data": "synthetic (seeded, generated on device; no datasets or weights)",
         "config": {"workload": workload_name, "S": inp.S, "T": inp.T, "H": inp.H, "d": inp.d,
                    "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
-                   inp.query_chunk, "launches_per_step": n_launch, "parallelism": "none (1 GPU)"},
+                   inp.query_chunk, "launches_per_step": n_launch, "screen": bool(args.screen),
+                   "parallelism": "none (1 GPU)"},
         "queries_per_s": inp.S / (ms_per_step / 1e3),
         "mfma_frac": achieved_tflops / peak,
         "score_select_ms": float(np.mean(score_ms)),

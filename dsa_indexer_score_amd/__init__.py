@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import IDX_BF16, IDX_EXPAND, IDX_F32, IDX_FP8_E4M3, IDX_TAIL  # noqa: F401
+from ._lib import IDX_BF16, IDX_EXPAND, IDX_F32, IDX_FP8_E4M3, IDX_SCREEN, IDX_TAIL  # noqa: F401
 
 __all__ = ["Indexer", "score_topk", "output_width", "pair_overlap", "overlap_summary",
            "library_path"]
@@ -29,8 +29,9 @@ def library_path() -> str:
     return _lib.LIB_PATH
 
 
-def _flags(expand: bool, tail: bool) -> int:
-    return (IDX_EXPAND if expand else 0) | (IDX_TAIL if tail else 0)
+def _flags(expand: bool, tail: bool, screen: bool = False) -> int:
+    return (IDX_EXPAND if expand else 0) | (IDX_TAIL if tail else 0) | \
+        (IDX_SCREEN if screen else 0)
 
 
 def output_width(topk: int, m: int = 1, expand: bool = False, tail: bool = False) -> int:
@@ -49,12 +50,14 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 class Indexer:
-    """A library handle: element dtype, output mode, query chunk size and the
+    """A library handle: element dtype, output mode, query chunk size, the
     row count at or below which the few-query path runs (0: the library's
-    default, negative: never)."""
+    default, negative: never) and DoSA certificate screening of the
+    streaming path (screen=True; used when 33 <= H <= 64)."""
 
     def __init__(self, dtype: torch.dtype, *, expand: bool = False, tail: bool = False,
-                 query_chunk: int = 0, few_query_rows: int = 0, device=None):
+                 query_chunk: int = 0, few_query_rows: int = 0, screen: bool = False,
+                 device=None):
         if dtype not in _DTYPE_CODE:
             raise TypeError(f"unsupported dtype {dtype}")
         dev = torch.device("cuda") if device is None else torch.device(device)
@@ -64,8 +67,9 @@ class Indexer:
         self.dtype, self.expand, self.tail = dtype, bool(expand), bool(tail)
         self.query_chunk = int(query_chunk or 0)
         self.few_query_rows = int(few_query_rows or 0)
-        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail), self.query_chunk,
-                                 self.few_query_rows)
+        self.screen = bool(screen)
+        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail, screen),
+                                 self.query_chunk, self.few_query_rows)
         h = ctypes.c_void_p()
         lib = _lib.load()
         _lib.check(lib.indexer_create(ctypes.byref(cfg), self.device.index or 0, ctypes.byref(h)),
@@ -198,24 +202,60 @@ class Indexer:
 _HANDLES = {}
 
 
-def _handle(dtype, expand, tail, query_chunk, few_query_rows, device) -> Indexer:
+def _handle(dtype, expand, tail, query_chunk, few_query_rows, device, screen=False) -> Indexer:
     key = (dtype, bool(expand), bool(tail), int(query_chunk or 0), int(few_query_rows or 0),
-           str(device))
+           bool(screen), str(torch.device(device)))
     h = _HANDLES.get(key)
     if h is None:
         h = _HANDLES[key] = Indexer(dtype, expand=expand, tail=tail, query_chunk=query_chunk,
-                                    few_query_rows=few_query_rows, device=device)
+                                    few_query_rows=few_query_rows, screen=screen,
+                                    device=device)
     return h
 
 
 def score_topk(q, w, k, *, m: int = 1, topk: int, causal: bool = True, expand: bool = False,
                tail: bool = False, q_scale=None, k_scale=None, q_pos0: int = 0,
-               query_chunk: int = 0, few_query_rows: int = 0, with_scores: bool = False,
-               workspace=None):
+               query_chunk: int = 0, few_query_rows: int = 0, screen: bool = False,
+               with_scores: bool = False, workspace=None):
     """One indexer step; see Indexer.score_topk."""
-    return _handle(q.dtype, expand, tail, query_chunk, few_query_rows, q.device).score_topk(
+    return _handle(q.dtype, expand, tail, query_chunk, few_query_rows, q.device,
+                   screen).score_topk(
         q, w, k, m=m, topk=topk, causal=causal, q_scale=q_scale, k_scale=k_scale,
         q_pos0=q_pos0, with_scores=with_scores, workspace=workspace)
+
+
+def screen_certificates(q: torch.Tensor, w: torch.Tensor, q_scale=None):
+    """The DoSA certificates the screened path builds for each row of q
+    [S, H, d] (33 <= H <= 64): (perm int32 [S, 64], weights [S, 64],
+    bound_weights [S, 32], knorm_coef [S]) on q's device; see
+    indexer_screen_certificates."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [S, H, d] tensor")
+    S, H, d = q.shape
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.device != q.device:
+        raise ValueError("w must be contiguous float32 on q's device")
+    if w.dim() == 1 and w.shape[0] == H:
+        w_stride = 0
+    elif w.dim() == 2 and tuple(w.shape) == (S, H):
+        w_stride = H
+    else:
+        raise ValueError("w must be [H] or [S, H]")
+    if (q.dtype == torch.float8_e4m3fn) != (q_scale is not None):
+        raise ValueError("q_scale [S, H] float32 is required exactly for fp8")
+    if q_scale is not None and (tuple(q_scale.shape) != (S, H) or
+                                q_scale.dtype != torch.float32 or
+                                not q_scale.is_contiguous() or q_scale.device != q.device):
+        raise ValueError("q_scale must be contiguous float32 [S, H] on q's device")
+    h = _handle(q.dtype, False, False, 0, 0, q.device)
+    dev = h.device
+    perm = torch.empty((S, 64), dtype=torch.int32, device=dev)
+    wv = torch.empty((S, 64), dtype=torch.float32, device=dev)
+    wt = torch.empty((S, 32), dtype=torch.float32, device=dev)
+    e = torch.empty((S,), dtype=torch.float32, device=dev)
+    _lib.check(h._lib.indexer_screen_certificates(
+        h._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, S, H, d, _ptr(perm), _ptr(wv),
+        _ptr(wt), _ptr(e), _stream(dev)), "indexer_screen_certificates")
+    return perm, wv, wt, e
 
 
 def pair_overlap(idx: torch.Tensor, valid_len: torch.Tensor) -> torch.Tensor:

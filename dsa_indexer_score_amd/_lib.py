@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa_indexer.so")
 
 IDX_F32, IDX_BF16, IDX_FP8_E4M3 = 0, 1, 2
-IDX_EXPAND, IDX_TAIL = 1, 2
+IDX_EXPAND, IDX_TAIL, IDX_SCREEN = 1, 2, 4
 IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EWORKSPACE, IDX_EHIP = 0, -1, -2, -3, -4
 
 
@@ -42,6 +42,8 @@ SIGNATURES = {
     "indexer_pair_overlap": (_I, [_P, _P, _I64, _I, _P, _P]),
     "indexer_pair_regions": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),
     "indexer_overlap_summary": (_I, [_P, _P, _I64, ctypes.POINTER(OverlapStats)]),
+    "indexer_screen_certificates": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _P, _P,
+                                         _P]),
     "indexer_strerror": (ctypes.c_char_p, [_I]),
 }
 

@@ -101,11 +101,36 @@ bool use_dense(const indexer_config &cfg, int64_t S, int64_t T)
     return lim > 0 && S <= lim && S <= 65535 && DenseLayout(S, T).bytes <= kDenseMaxBytes;
 }
 
-int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int64_t ksel,
+// Screening (IDX_SCREEN) on the streaming path: needs two head blocks.
+bool use_screen(const indexer_config &cfg, int H)
+{
+    return (cfg.flags & IDX_SCREEN) && H > 32 && H <= 64;
+}
+
+// Streaming workspace: the candidate buffers [rows, cap] of (score bits,
+// key), then with screening the certificates of one launch's rows (head
+// order [rows, 64] i32, weights [rows, 64], bound weights [rows, 32], key
+// norm coefficient [rows]) and the key norms [T], each 256-byte aligned.
+struct StreamLayout {
+    int64_t perm, w, wt, e, knorm, bytes;
+    StreamLayout(int64_t rows, int64_t cap, int64_t T, bool screen)
+    {
+        bytes = rows * cap * (int64_t)sizeof(uint2);
+        if (!screen) return;
+        perm = round_up(bytes, 256);
+        w = perm + round_up(rows * 64 * 4, 256);
+        wt = w + round_up(rows * 64 * 4, 256);
+        e = wt + round_up(rows * 32 * 4, 256);
+        knorm = e + round_up(rows * 4, 256);
+        bytes = knorm + std::max<int64_t>(T, 1) * 4;
+    }
+};
+
+int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int H, int64_t ksel,
                        int64_t pmax)
 {
     if (use_dense(cfg, S, T)) return DenseLayout(S, T).bytes;
-    return rows_per_launch(cfg, S) * capacity(ksel, pmax) * (int64_t)sizeof(uint2);
+    return StreamLayout(rows_per_launch(cfg, S), capacity(ksel, pmax), T, use_screen(cfg, H)).bytes;
 }
 
 struct DeviceGuard {
@@ -136,7 +161,7 @@ int indexer_create(const indexer_config *cfg, int device, indexer_t *out)
 {
     if (!cfg || !out || device < 0) return IDX_EINVAL;
     if (!dtype_ok(cfg->dtype)) return IDX_EINVAL;
-    if (cfg->flags & ~(IDX_EXPAND | IDX_TAIL)) return IDX_EINVAL;
+    if (cfg->flags & ~(IDX_EXPAND | IDX_TAIL | IDX_SCREEN)) return IDX_EINVAL;
     if ((cfg->flags & IDX_TAIL) && !(cfg->flags & IDX_EXPAND)) return IDX_EINVAL;
     if (cfg->query_chunk < 0) return IDX_EINVAL;
     indexer_s *h = new (std::nothrow) indexer_s;
@@ -155,7 +180,8 @@ int indexer_destroy(indexer_t h)
 
 int indexer_output_width(int topk, int m, int flags, int *W)
 {
-    if (!W || topk < 1 || m < 1 || (flags & ~(IDX_EXPAND | IDX_TAIL))) return IDX_EINVAL;
+    if (!W || topk < 1 || m < 1 || (flags & ~(IDX_EXPAND | IDX_TAIL | IDX_SCREEN)))
+        return IDX_EINVAL;
     if ((flags & IDX_TAIL) && !(flags & IDX_EXPAND)) return IDX_EINVAL;
     if ((flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     int64_t w = (int64_t)topk + ((flags & IDX_TAIL) ? (m - 1) : 0);
@@ -171,7 +197,7 @@ int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
-    *bytes = (size_t)workspace_need(h->cfg, S, T, ksel, T);
+    *bytes = (size_t)workspace_need(h->cfg, S, T, H, ksel, T);
     return IDX_OK;
 }
 
@@ -227,8 +253,9 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     const int64_t cap = capacity(ksel, pmax);
     const int64_t rows = rows_per_launch(cfg, S);
     const bool dense = !docs.on && use_dense(cfg, S, T);
+    const bool screen = !docs.on && !dense && use_screen(cfg, H);
     const size_t need = docs.on ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
-                                : (size_t)workspace_need(cfg, S, T, ksel, pmax);
+                                : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
 
     DeviceGuard guard(h->device);
@@ -289,20 +316,40 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         bool supported = true;
         hipError_t e = S <= kRowsKernelMax
                            ? dsai::launch_score_rows(cfg.dtype, nb, d, p, st, &supported)
-                           : dsai::launch_score_select(cfg.dtype, nb, d, true, false, p, st,
-                                                       &supported);
+                           : dsai::launch_score_select(cfg.dtype, nb, d, true, false, false, p,
+                                                       st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
         e = dsai::launch_select_dense(p, st);
         if (e != hipSuccess) return fail_hip(e);
         return IDX_OK;
     }
+    if (screen) {
+        // DoSA screening: key norms once, certificates per launch
+        const StreamLayout L(rows, cap, T, true);
+        char *base = static_cast<char *>(workspace);
+        p.cert_perm = reinterpret_cast<int32_t *>(base + L.perm);
+        p.cert_w = reinterpret_cast<float *>(base + L.w);
+        p.cert_wt = reinterpret_cast<float *>(base + L.wt);
+        p.cert_e = reinterpret_cast<float *>(base + L.e);
+        p.knorm = reinterpret_cast<float *>(base + L.knorm);
+        bool supported = true;
+        const hipError_t e = dsai::launch_key_norms(cfg.dtype, d, p, st, &supported);
+        if (!supported) return IDX_EUNSUPPORTED;
+        if (e != hipSuccess) return fail_hip(e);
+    }
     for (int64_t r0 = 0; r0 < S; r0 += rows) {
         p.row0 = r0;
         p.nrows = std::min(rows, S - r0);
         bool supported = true;
-        hipError_t e =
-            dsai::launch_score_select(cfg.dtype, nb, d, false, docs.on, p, st, &supported);
+        hipError_t e = hipSuccess;
+        if (screen) {
+            // the certificate buffers hold one launch's rows
+            e = dsai::launch_certificates(cfg.dtype, d, p, st, &supported);
+            if (!supported) return IDX_EUNSUPPORTED;
+            if (e != hipSuccess) return fail_hip(e);
+        }
+        e = dsai::launch_score_select(cfg.dtype, nb, d, false, docs.on, screen, p, st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
     }
@@ -444,3 +491,37 @@ const char *indexer_strerror(int code)
 }
 
 }  // extern "C"
+
+extern "C" int indexer_screen_certificates(indexer_t h, const void *q, const float *q_scale,
+                                           const float *w, int64_t w_stride_s, int64_t S, int H,
+                                           int d, int32_t *perm, float *weights,
+                                           float *bound_weights, float *knorm_coef, void *stream)
+{
+    if (!h || S < 0 || H < 1 || d < 1) return IDX_EINVAL;
+    if (w_stride_s != 0 && w_stride_s < H) return IDX_EINVAL;
+    if (!shape_supported(h->cfg.dtype, H, d) || H <= 32 || H > 64) return IDX_EUNSUPPORTED;
+    if (S == 0) return IDX_OK;
+    const bool fp8 = h->cfg.dtype == IDX_FP8_E4M3;
+    if (!q || !w || !perm || !weights || !bound_weights || !knorm_coef) return IDX_EINVAL;
+    if (fp8 != (q_scale != nullptr)) return IDX_EINVAL;
+    if (!aligned(q, 16) || !aligned(w, 4)) return IDX_EINVAL;
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return fail_hip(guard.err);
+    dsai::ScoreSelectParams p{};
+    p.q = q;
+    p.q_scale = q_scale;
+    p.w = w;
+    p.w_stride = w_stride_s;
+    p.H = H;
+    p.row0 = 0;
+    p.nrows = S;
+    p.cert_perm = perm;
+    p.cert_w = weights;
+    p.cert_wt = bound_weights;
+    p.cert_e = knorm_coef;
+    bool supported = true;
+    const hipError_t e =
+        dsai::launch_certificates(h->cfg.dtype, d, p, static_cast<hipStream_t>(stream), &supported);
+    if (!supported) return IDX_EUNSUPPORTED;
+    return e == hipSuccess ? IDX_OK : fail_hip(e);
+}

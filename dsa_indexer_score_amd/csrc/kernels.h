@@ -51,6 +51,15 @@ struct ScoreSelectParams {
     int32_t *seg_cnt;
     int32_t *seg_key;
     int nseg;
+    // Screening (DoSA certificates), per row of the launch: head order with
+    // the kept heads first [nrows, 64] (-1 = no head), weights w * q_scale in
+    // that order [nrows, 64], folded bound weights of the kept heads
+    // [nrows, 32], key-norm coefficient [nrows]; key norms ||k_j|| [T].
+    int32_t *cert_perm;
+    float *cert_w;
+    float *cert_wt;
+    float *cert_e;
+    float *knorm;
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
@@ -59,8 +68,15 @@ constexpr int kSelGroup = 64;         // keys appended per selection step (one p
 
 // dtype codes match enum idx_dtype; dense = write scores (p.scores) instead
 // of selecting; varlen = rows and keys are packed documents (p.cu_q ...)
-hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen,
+hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen, bool screen,
                                const ScoreSelectParams &p, hipStream_t stream, bool *supported);
+
+// DoSA certificates of rows [p.row0, p.row0 + p.nrows) into p.cert_* (one
+// wave per row), and the key norms p.knorm of all T keys.
+hipError_t launch_certificates(int dtype, int d, const ScoreSelectParams &p, hipStream_t stream,
+                               bool *supported);
+hipError_t launch_key_norms(int dtype, int d, const ScoreSelectParams &p, hipStream_t stream,
+                            bool *supported);
 
 // Dense scores of one or two rows (p.scores, as the dense mode of
 // launch_score_select writes them, bit for bit), every CU streaming its own

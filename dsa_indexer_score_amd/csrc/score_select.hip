@@ -71,9 +71,10 @@ namespace {
 
 constexpr int kThreads = kQueriesPerBlock * 64;
 
-template <int DT, int NB, int D, bool DENSE, bool VARLEN>
+template <int DT, int NB, int D, bool DENSE, bool VARLEN, bool SCREEN>
 __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectParams p)
 {
+    static_assert(!SCREEN || (NB == 2 && !DENSE && !VARLEN), "screening: two head blocks");
     using O = Op<DT, D>;
     using A = typename O::A;
     constexpr int KS = O::KS, NCH = O::NCH, GCH = O::GCH, ES = O::ES;
@@ -86,6 +87,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     __shared__ uint4 ktile[2][TILE_CH];
     __shared__ float kscale_tile[2][kKeysPerTile];
     __shared__ uint32_t hist_all[kQueriesPerBlock][kHistWords];
+    // screening only: key norms of the staged tiles, each wave's kept-head
+    // partial sums of one tile (two lane halves) and its survivor list
+    constexpr int kScr = SCREEN ? 1 : 0;
+    __shared__ float knorm_tile[2][kScr * kKeysPerTile + 1];
+    __shared__ float p0_all[kQueriesPerBlock][kScr * 2 * kKeysPerTile + 1];
+    __shared__ uint16_t sl_all[kQueriesPerBlock][kScr * kKeysPerTile + 1];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = lane >> 5, l32 = lane & 31;
@@ -161,10 +168,13 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     float wv[NB][16];
     const char *qbytes = static_cast<const char *>(p.q);
     const int64_t tq = active ? t : p.row0;
+    // screening: A rows follow the certificate's head order (kept heads in
+    // block 0), weights come from the certificate (w * q_scale, permuted)
+    const int64_t crow = active ? qrow : 0;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const int head = 32 * b + l32;
-        const bool okq = active && head < p.H;
+        const int head = SCREEN ? p.cert_perm[crow * 64 + 32 * b + l32] : 32 * b + l32;
+        const bool okq = active && head >= 0 && head < p.H;
         O::load_a(qbytes + ((tq * p.H + (okq ? head : 0)) * (int64_t)D) * ES, hh, qa[b]);
         if (!okq) {
 #pragma unroll
@@ -175,10 +185,24 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             const int h2 = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
             const bool ok = active && h2 < p.H;
             const int hc = ok ? h2 : 0;
-            float wt = p.w[tq * p.w_stride + hc];
-            if (DT == 2) wt *= p.q_scale[tq * p.H + hc];
-            wv[b][v] = ok ? wt : 0.f;
+            if constexpr (SCREEN) {
+                wv[b][v] = active ? p.cert_w[crow * 64 + h2] : 0.f;
+            } else {
+                float wt = p.w[tq * p.w_stride + hc];
+                if (DT == 2) wt *= p.q_scale[tq * p.H + hc];
+                wv[b][v] = ok ? wt : 0.f;
+            }
         }
+    }
+    // screening: folded bound weights of the kept heads and the key-norm
+    // coefficient (residual allowance plus rounding margin)
+    float wtb[16];
+    float emu = 0.f;
+    if constexpr (SCREEN) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            wtb[v] = active ? p.cert_wt[crow * 32 + 8 * (v >> 2) + 4 * hh + (v & 3)] : 0.f;
+        emu = active ? p.cert_e[crow] : 0.f;
     }
 
     uint2 *buf = p.ws + (active && !DENSE ? qrow : 0) * (int64_t)p.cap;
@@ -191,7 +215,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
 
     const char *kbytes = static_cast<const char *>(p.k);
     uint4 stage[CPT];
-    float ksc = 0.f;
+    float ksc = 0.f, kn = 0.f;
     auto load_tile = [&](int it) {
         const int64_t j0 = kbeg + (int64_t)it * kKeysPerTile;
 #pragma unroll
@@ -208,6 +232,10 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             const int64_t key = j0 + threadIdx.x;
             ksc = key < p.T ? p.k_scale[key] : 0.f;
         }
+        if (SCREEN && threadIdx.x < kKeysPerTile) {
+            const int64_t key = j0 + threadIdx.x;
+            kn = key < p.T ? p.knorm[key] : 0.f;
+        }
     };
     auto store_tile = [&](int slot) {
 #pragma unroll
@@ -219,6 +247,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             }
         }
         if (DT == 2 && threadIdx.x < kKeysPerTile) kscale_tile[slot][threadIdx.x] = ksc;
+        if (SCREEN && threadIdx.x < kKeysPerTile) knorm_tile[slot][threadIdx.x] = kn;
     };
 
     if (ntiles > 0) {
@@ -230,22 +259,11 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // Selection of one tile's scores (NG groups of 64 keys, one key per lane).
     constexpr int NCB = kKeysPerTile / 32;  // 32-key column blocks per tile
     constexpr int NG = NCB / 2;             // 64-key selection groups per tile
-    auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
-        if constexpr (DENSE) {
-            float *srow = p.scores + qrow * p.sstride;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int64_t key = j0 + g * kSelGroup + lane;
-                if (key < Pq) srow[key] = sg[g];
-            }
-            return;
-        }
-        const bool full = j0 >= klo && j0 + kKeysPerTile <= khi;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int64_t key = j0 + g * kSelGroup + lane;
-            const uint32_t bits = __float_as_uint(sg[g]);
-            const bool pass = sg[g] >= tau_f && (full || (key >= klo && key < khi));
+    // One selection step: each lane offers one (score, key), ok = the key
+    // is visible to this row; keys arrive in ascending order across calls.
+    auto consider = [&](float sc, int64_t key, bool ok) __attribute__((always_inline)) {
+            const uint32_t bits = __float_as_uint(sc);
+            const bool pass = sc >= tau_f && ok;
             const uint64_t mask = __ballot(pass);
             if (mask) {
                 const uint32_t u = ord_code(bits);
@@ -282,14 +300,147 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                     find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
                 }
             }
+    };
+    auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
+        if constexpr (DENSE) {
+            float *srow = p.scores + qrow * p.sstride;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int64_t key = j0 + g * kSelGroup + lane;
+                if (key < Pq) srow[key] = sg[g];
+            }
+            return;
         }
+        const bool full = j0 >= klo && j0 + kKeysPerTile <= khi;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int64_t key = j0 + g * kSelGroup + lane;
+            consider(sg[g], key, full || (key >= klo && key < khi));
+        }
+    };
+
+    // Screened tile (DoSA summary, "Method steps": certificate screening and
+    // survivor rescoring).  Block 0 holds the certificate's kept heads: their
+    // MFMAs and signed-ReLU sum run for every key, and the same ReLU values
+    // give the bound U = sum_kept w~ ReLU(x) + emu * ||k|| (times k_scale).
+    // A key with U < tau cannot enter the selection, since its exact score
+    // is at most U and tau never exceeds the final Ksel-th score; the others
+    // are gathered 32 per MFMA column block, get block 1's heads (B read
+    // from the staged tile at the survivor's row), and continue the exact
+    // sum from their block-0 partial in the same order as an unscreened
+    // tile, so a survivor's score does not depend on the screen.
+    auto screen_tile = [&](int cur, int64_t j0) __attribute__((always_inline)) {
+        constexpr int EPK = (16 + KS - 1) / KS;
+        float part[NCB], ub[NCB];
+        A bfr[KS];
+        O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
+        f32x16 accp;
+#pragma unroll
+        for (int s = 0; s <= NCB; ++s) {  // MFMAs of column block s, epilogue of s - 1
+            const bool loads = s + 1 < NCB;
+            f32x16 acc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+            float e = 0.f, u = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (s < NCB) acc = O::mma(qa[0][ks], bfr[ks], acc);
+                if (loads) {
+                    const int r = (s + 1) * 32 + l32;
+                    O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
+                }
+                if (s > 0) {
+#pragma unroll
+                    for (int x = 0; x < EPK; ++x) {
+                        const int v = ks * EPK + x;
+                        if (v < 16) {
+                            const float r = fmaxf(accp[v], 0.f);
+                            e = fmaf(wv[0][v], r, e);
+                            u = fmaf(wtb[v], r, u);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (s > 0) {
+                part[s - 1] = e;
+                ub[s - 1] = u;
+            }
+            if (s < NCB) accp = acc;
+        }
+        float *p0 = p0_all[wave];
+        uint16_t *sl = sl_all[wave];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) p0[hh * kKeysPerTile + cb * 32 + l32] = part[cb];
+        const bool full = j0 >= klo && j0 + kKeysPerTile <= khi;
+        int ns = 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ub[2 * g]),
+                                                             __float_as_uint(ub[2 * g + 1]),
+                                                             false, false);
+            const int kl = g * kSelGroup + lane;
+            float U = __uint_as_float(sw[0]) + __uint_as_float(sw[1]) + emu * knorm_tile[cur][kl];
+            if (DT == 2) U *= kscale_tile[cur][kl];
+            const int64_t key = j0 + kl;
+            const bool surv = (full || (key >= klo && key < khi)) && U >= tau_f;
+            const uint64_t m = __ballot(surv);
+            if (surv) sl[ns + lane_rank(m)] = (uint16_t)kl;
+            ns += __popcll(m);
+        }
+        wave_sync_mem();
+        // 64 survivors per round: two gathered column blocks (survivors
+        // sb + 32c + l32), the MFMAs of the second issued with the epilogue
+        // of the first, then the two lane halves added as for a plain tile
+        for (int sb = 0; sb < ns; sb += 2 * 32) {
+            int kl[2];
+            float pc[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int i = sb + 32 * c + l32;
+                kl[c] = sl[i < ns ? i : sb];
+                pc[c] = p0[hh * kKeysPerTile + kl[c]];
+            }
+            O::load_b(ktile[cur], kl[0], hh, kl[0] & SWZ, bfr);
+#pragma unroll
+            for (int s = 0; s <= 2; ++s) {  // MFMAs of gathered block s, epilogue of s - 1
+                f32x16 acc;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+                float e = s > 0 ? pc[s - 1] : 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (s < 2) acc = O::mma(qa[1][ks], bfr[ks], acc);
+                    if (s == 0) O::load_b_one(ktile[cur], kl[1], hh, kl[1] & SWZ, ks, bfr[ks]);
+                    if (s > 0) {
+#pragma unroll
+                        for (int x = 0; x < EPK; ++x) {
+                            const int v = ks * EPK + x;
+                            if (v < 16) e = fmaf(wv[1][v], fmaxf(accp[v], 0.f), e);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (s > 0) pc[s - 1] = e;
+                if (s < 2) accp = acc;
+            }
+            // lane L < 32: survivor sb + L from block 0; lane L >= 32: survivor
+            // sb + L from block 1 -- the same lane's kl[hh]
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pc[0]),
+                                                             __float_as_uint(pc[1]), false, false);
+            const int klane = hh ? kl[1] : kl[0];
+            float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (DT == 2) sc *= kscale_tile[cur][klane];
+            consider(sc, j0 + klane, sb + lane < ns);
+        }
+        wave_sync_mem();  // the next tile's survivor list reuses sl and p0
     };
 
     // The two waves sharing a SIMD (w and w + 4) run their selection at
     // opposite ends of a tile: waves 0-3 right after their MFMA/epilogue work,
     // waves 4-7 one tile later, before their MFMAs -- so one wave's branchy
     // selection code always has the other wave's MFMAs to overlap with.
-    const bool lagged = !DENSE && wave >= kQueriesPerBlock / 2;
+    const bool lagged = !DENSE && !SCREEN && wave >= kQueriesPerBlock / 2;
     float pend[NG];
     int64_t pend_j0 = -1;
 
@@ -302,7 +453,9 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             select_tile(pend, pend_j0);
             pend_j0 = -1;
         }
-        if (active && j0 < khi && j0 + kKeysPerTile > klo) {
+        if (SCREEN && active && j0 < khi && j0 + kKeysPerTile > klo) {
+            screen_tile(cur, j0);
+        } else if (active && j0 < khi && j0 + kKeysPerTile > klo) {
             // Software pipeline over steps (cb, b): the MFMAs of step s run
             // while the signed-ReLU epilogue of step s-1 is issued between
             // them; B of the next column block is fetched during the last
@@ -420,37 +573,42 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     if (lane == 0) p.valid_len[t] = body + tl;
 }
 
-template <int DT, int NB, int D, bool DENSE, bool VARLEN>
+template <int DT, int NB, int D, bool DENSE, bool VARLEN, bool SCREEN>
 hipError_t launch_one(const ScoreSelectParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock * p.nsplit;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, DENSE, VARLEN>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, DENSE, VARLEN, SCREEN>),
+                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DT, int NB, int D>
-hipError_t launch_mode(bool dense, bool varlen, const ScoreSelectParams &p, hipStream_t stream)
+hipError_t launch_mode(bool dense, bool varlen, bool screen, const ScoreSelectParams &p,
+                       hipStream_t stream)
 {
-    if (varlen) return launch_one<DT, NB, D, false, true>(p, stream);
-    return dense ? launch_one<DT, NB, D, true, false>(p, stream)
-                 : launch_one<DT, NB, D, false, false>(p, stream);
+    if (varlen) return launch_one<DT, NB, D, false, true, false>(p, stream);
+    if (dense) return launch_one<DT, NB, D, true, false, false>(p, stream);
+    if constexpr (NB == 2) {
+        if (screen) return launch_one<DT, NB, D, false, false, true>(p, stream);
+    }
+    return launch_one<DT, NB, D, false, false, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen,
+hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen, bool screen,
                                const ScoreSelectParams &p, hipStream_t stream, bool *supported)
 {
     *supported = true;
     if (p.nsplit < 1 || p.split_keys < kKeysPerTile || p.split_keys % kKeysPerTile ||
-        (varlen && (dense || p.nsplit != 1))) {
+        (varlen && (dense || p.nsplit != 1)) || (screen && (dense || varlen || nb != 2))) {
         *supported = false;
         return hipSuccess;
     }
 #define DSAI_CASE(DT, NB, D) \
-    if (dtype == DT && nb == NB && d == D) return launch_mode<DT, NB, D>(dense, varlen, p, stream);
+    if (dtype == DT && nb == NB && d == D) \
+        return launch_mode<DT, NB, D>(dense, varlen, screen, p, stream);
     DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
     DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
     DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)

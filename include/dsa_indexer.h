@@ -53,7 +53,8 @@ enum idx_dtype { IDX_F32 = 0, IDX_BF16 = 1, IDX_FP8_E4M3 = 2 };
 /* Output mode flags. */
 enum {
     IDX_EXPAND = 1, /* selected pools expand to their m token positions   */
-    IDX_TAIL = 2    /* append the incomplete pool (needs EXPAND, causal)  */
+    IDX_TAIL = 2,   /* append the incomplete pool (needs EXPAND, causal)  */
+    IDX_SCREEN = 4  /* DoSA certificate screening, see below              */
 };
 
 enum {
@@ -66,7 +67,7 @@ enum {
 
 typedef struct {
     int dtype;           /* enum idx_dtype                                     */
-    int flags;           /* IDX_EXPAND | IDX_TAIL                              */
+    int flags;           /* IDX_EXPAND | IDX_TAIL | IDX_SCREEN                 */
     int64_t query_chunk; /* queries per launch (bounds the workspace); 0 = all */
     /* Few-query path (decode, small batches against a long key set): when
      * S <= few_query_rows, every visible score of the S rows is written to
@@ -240,6 +241,39 @@ typedef struct {
 
 int indexer_overlap_summary(const int32_t *shared, const int32_t *valid_len, int64_t S,
                             indexer_overlap_stats *out);
+
+/* DoSA certificate screening ("DoSA: Dots Sparse Attention", summary page,
+ * "Core method" and "Method steps").  With IDX_SCREEN in the flags, the
+ * streaming path (not the few-query or packed-document paths) with
+ * 33 <= H <= 64 first builds one certificate per query row: 32 kept heads
+ * (all positive heads of the row plus the negative heads of largest
+ * |w_h q_scale_h| ||q_h||, or the 32 positive heads of largest w_h
+ * q_scale_h ||q_h|| when there are more), each omitted positive head folded
+ * onto the kept positive head closest in direction, and a coefficient of
+ * ||k|| that holds the residual allowance plus a rounding margin.  Every
+ * key's upper bound U = sum_kept w~_h ReLU(q_h . k) + coef ||k|| (times
+ * k_scale) is computed from the kept heads alone; a key with U below the
+ * row's running Ksel-th score lower bound is not scored further, the others
+ * get the remaining heads.  Lossless: the selection equals the unscreened
+ * one up to the order in which the 64 head terms are summed (the kept heads
+ * come first).  The workspace grows by 644 bytes per row of a launch plus 4
+ * per key (indexer_workspace_bytes accounts for it).
+ *
+ * indexer_screen_certificates writes the certificates of S rows as the
+ * screened path uses them, for inspection:
+ *   q, q_scale, w, w_stride: as for indexer_score_topk (device).
+ *   perm: device int32 [S, 64], out: head order, kept heads first (by head
+ *     index), then the omitted heads (by index), then -1.
+ *   weights: device fp32 [S, 64], out: w_h * q_scale_h (w_h for bf16 and
+ *     fp32) in that order.
+ *   bound_weights: device fp32 [S, 32], out: the kept heads' folded weights.
+ *   knorm_coef: device fp32 [S], out: the coefficient of ||k|| (raw codes).
+ * Requires 33 <= H <= 64 (else IDX_EUNSUPPORTED).  Asynchronous on `stream`.
+ */
+int indexer_screen_certificates(indexer_t h, const void *q, const float *q_scale, const float *w,
+                                int64_t w_stride, int64_t S, int H, int d, int32_t *perm,
+                                float *weights, float *bound_weights, float *knorm_coef,
+                                void *stream);
 
 /* Static text for a status code, followed (for IDX_EHIP) by the calling
  * thread's last HIP error.  Never NULL. */

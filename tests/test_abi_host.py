@@ -60,7 +60,7 @@ def _handle(dtype=_lib.IDX_BF16, flags=0, chunk=0, few=0):
 def test_create_rejects_bad_configs():
     lib = _lib.load()
     h = ctypes.c_void_p()
-    for dtype, flags, chunk, dev in ((7, 0, 0, 0), (1, 4, 0, 0), (1, _lib.IDX_TAIL, 0, 0),
+    for dtype, flags, chunk, dev in ((7, 0, 0, 0), (1, 8, 0, 0), (1, _lib.IDX_TAIL, 0, 0),
                                      (1, 0, -1, 0), (1, 0, 0, -1)):
         cfg = _lib.IndexerConfig(dtype, flags, chunk)
         assert lib.indexer_create(ctypes.byref(cfg), dev, ctypes.byref(h)) == _lib.IDX_EINVAL
@@ -113,6 +113,23 @@ def test_workspace_bytes_of_the_few_query_path():
     lib, h = _handle(few=1000)
     assert lib.indexer_workspace_bytes(h, 1000, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == _dense_bytes(1000, 4096)
+    lib.indexer_destroy(h)
+
+
+def test_workspace_bytes_with_screening():
+    """IDX_SCREEN adds, on the streaming path with 33 <= H <= 64, the
+    certificates of one launch's rows (644 bytes a row in four 256-byte
+    aligned parts) and 4 bytes per key; H <= 32 cannot screen."""
+    up = lambda x, a: -(-x // a) * a
+    n = ctypes.c_size_t()
+    lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL | _lib.IDX_SCREEN)
+    S, T, cap = 100, 5000, up(5000, 64) + 64          # cap: every visible key fits
+    base = S * cap * 8
+    want = up(base, 256) + 2 * up(S * 256, 256) + up(S * 128, 256) + up(S * 4, 256) + T * 4
+    assert lib.indexer_workspace_bytes(h, S, T, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == want
+    assert lib.indexer_workspace_bytes(h, S, T, 32, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == base
     lib.indexer_destroy(h)
 
 
