@@ -127,6 +127,8 @@ def main():
                          "pools, causality and keys) and time the varlen entry point")
     ap.add_argument("--regions", action="store_true",
                     help="also time the three-region q-cluster split of the adjacent pairs")
+    ap.add_argument("--wdist", default=None, choices=["normal_bcast", "lognormal_bcast"],
+                    help="override the workload's head-weight distribution")
     ap.add_argument("--screen", action="store_true",
                     help="DoSA certificate screening on the streaming path (lossless)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
@@ -148,13 +150,14 @@ def main():
     torch.cuda.set_device(dev)
     log(f"bench: library {dsai.library_path()}")
     t0 = time.perf_counter()
+    over = {"wdist": args.wdist} if args.wdist else {}
     if args.decode:
         from dataclasses import replace
         full_T = gen.CONFIGS[args.workload]["T"]
-        inp = gen.generate(args.workload, S=args.decode, T=full_T, device=dev)
+        inp = gen.generate(args.workload, S=args.decode, T=full_T, device=dev, **over)
         inp = replace(inp, q_pos0=full_T * inp.m - args.decode, query_chunk=None)
     else:
-        inp = gen.generate(args.workload, device=dev)
+        inp = gen.generate(args.workload, device=dev, **over)
     torch.cuda.synchronize()
     log(f"bench: generated {args.workload} S={inp.S} T={inp.T} H={inp.H} d={inp.d} m={inp.m} "
         f"topk={inp.topk} dtype={inp.dtype} chunk={inp.query_chunk} in "
@@ -304,6 +307,7 @@ def main():
         "config": {"workload": workload_name, "S": inp.S, "T": inp.T, "H": inp.H, "d": inp.d,
                    "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
                    inp.query_chunk, "launches_per_step": n_launch, "screen": bool(args.screen),
+                   "wdist": inp.meta.get("wdist"),
                    "parallelism": "none (1 GPU)"},
         "queries_per_s": inp.S / (ms_per_step / 1e3),
         "mfma_frac": achieved_tflops / peak,

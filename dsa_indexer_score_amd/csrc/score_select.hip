@@ -392,7 +392,8 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         // 64 survivors per round: two gathered column blocks (survivors
         // sb + 32c + l32), the MFMAs of the second issued with the epilogue
         // of the first, then the two lane halves added as for a plain tile
-        for (int sb = 0; sb < ns; sb += 2 * 32) {
+        int sb = 0;
+        for (; sb + 32 < ns; sb += 2 * 32) {
             int kl[2];
             float pc[2];
 #pragma unroll
@@ -432,6 +433,25 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
             if (DT == 2) sc *= kscale_tile[cur][klane];
             consider(sc, j0 + klane, sb + lane < ns);
+        }
+        if (sb < ns) {  // at most 32 survivors left: one gathered block
+            const int i = sb + l32;
+            const int kl = sl[i < ns ? i : sb];
+            O::load_b(ktile[cur], kl, hh, kl & SWZ, bfr);
+            f32x16 acc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = O::mma(qa[1][ks], bfr[ks], acc);
+            float e = p0[hh * kKeysPerTile + kl];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) e = fmaf(wv[1][v], fmaxf(acc[v], 0.f), e);
+            // both lane halves of survivor sb + l32 meet in lanes l32 < 32
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(e),
+                                                             __float_as_uint(e), false, false);
+            float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (DT == 2) sc *= kscale_tile[cur][kl];
+            consider(sc, j0 + kl, lane < 32 && i < ns);
         }
         wave_sync_mem();  // the next tile's survivor list reuses sl and p0
     };

@@ -152,3 +152,14 @@ def test_screened_selection_with_folds_and_pruning(dtype, H, d):
     rep = check.compare(inp, rows, idx.cpu().numpy()[rows], vl.cpu().numpy()[rows],
                         sc.cpu().numpy()[rows])
     assert rep["ok"], rep["failures"][:3]
+
+
+def test_screened_selection_on_dominant_heads():
+    """Head weights spread over decades (the stand-in where the certificate
+    prunes): the screened selection still passes the oracle's rule."""
+    inp = gen.generate("c4_csa_256k", S=3000, topk=512, wdist="lognormal_bcast").to(DEV)
+    idx, vl, sc = run(inp, screen=True)
+    rows = check.sample_rows(3000, m=inp.m, ksel=inp.topk, n_uniform=64)
+    rep = check.compare(inp, rows, idx.cpu().numpy()[rows], vl.cpu().numpy()[rows],
+                        sc.cpu().numpy()[rows])
+    assert rep["ok"], rep["failures"][:3]

@@ -247,6 +247,12 @@ def generate(name: str, *, S: Optional[int] = None, T: Optional[int] = None,
         w = vals[torch.randint(0, 4, (S, H), generator=gw, device=device)]
     elif cfg["wdist"] == "normal_bcast":
         w = torch.randn((H,), generator=gw, device=device, dtype=torch.float32)
+    elif cfg["wdist"] == "lognormal_bcast":
+        # signed weights whose magnitudes spread over decades (a few dominant
+        # heads): a synthetic stand-in for trained head weights, where
+        # certificate screening prunes (override of any config)
+        z = torch.randn((2, H), generator=gw, device=device, dtype=torch.float32)
+        w = z[0] * torch.exp(1.5 * z[1])
     else:
         raise ValueError(cfg["wdist"])
 
