@@ -163,3 +163,28 @@ def test_screened_selection_on_dominant_heads():
     rep = check.compare(inp, rows, idx.cpu().numpy()[rows], vl.cpu().numpy()[rows],
                         sc.cpu().numpy()[rows])
     assert rep["ok"], rep["failures"][:3]
+
+
+def test_screened_chunked_launches_and_modes():
+    """Certificates are built per launch: several query chunks give the same
+    result as one launch, bit for bit; expansion with the tail, a query
+    offset and the non-causal mode pass the oracle's rule screened."""
+    inp = gen.generate("c4_csa_256k", S=2500, topk=512).to(DEV)
+    one = run(inp, screen=True, query_chunk=0)
+    many = run(inp, screen=True, query_chunk=384)
+    for a, b in zip(one, many):
+        assert torch.equal(a, b)
+    g = torch.Generator().manual_seed(31)
+    S, H, d, m = 900, 48, 64, 4
+    T = (37 + S) // m
+    q = (torch.randn(S, H, d, generator=g) / d ** 0.5).bfloat16()
+    k = (torch.randn(T, d, generator=g) / d ** 0.5).bfloat16()
+    w = torch.randn(H, generator=g)
+    for causal, expand, tail in ((True, True, True), (False, False, False)):
+        inp = gen.custom(q=q, k=k, w=w, m=m, topk=256, causal=causal, expand=expand,
+                         tail=tail, q_pos0=37 if causal else 0).to(DEV)
+        idx, vl, sc = run(inp, screen=True, query_chunk=256)
+        rows = np.arange(0, S, 4)
+        rep = check.compare(inp, rows, idx.cpu().numpy()[rows], vl.cpu().numpy()[rows],
+                            sc.cpu().numpy()[rows])
+        assert rep["ok"], (causal, rep["failures"][:3])
