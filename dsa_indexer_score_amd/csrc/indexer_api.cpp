@@ -78,7 +78,8 @@ int64_t dense_stride(int64_t T) { return round_up(std::max<int64_t>(T, 1), 4); }
 
 // Few-query workspace: the rows' dense scores [S, stride] (f32), the
 // per-row threshold estimates [S] (u32), the candidate counts [S, nseg]
-// and the candidate keys [S, nseg, segment] (i32), each 256-byte aligned.
+// (i32) and the candidates [S, nseg, segment] of (score bits, key), each
+// 256-byte aligned.
 struct DenseLayout {
     int64_t stride, nseg, est, cnt, key, bytes;
     DenseLayout(int64_t S, int64_t T)
@@ -89,7 +90,7 @@ struct DenseLayout {
         est = round_up(S * stride * 4, 256);
         cnt = est + round_up(S * 4, 256);
         key = cnt + round_up(S * nseg * 4, 256);
-        bytes = key + S * nseg * seg * 4;
+        bytes = key + S * nseg * seg * 8;
     }
 };
 
@@ -302,7 +303,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.sstride = L.stride;
         p.est = reinterpret_cast<uint32_t *>(base + L.est);
         p.seg_cnt = reinterpret_cast<int32_t *>(base + L.cnt);
-        p.seg_key = reinterpret_cast<int32_t *>(base + L.key);
+        p.seg_buf = reinterpret_cast<uint2 *>(base + L.key);
         p.nseg = (int)L.nseg;
         p.row0 = 0;
         p.nrows = S;

@@ -46,10 +46,11 @@ struct ScoreSelectParams {
     int ndoc;
     // Few-query selection scratch (dense mode): per-row threshold estimate,
     // per (row, segment of dense_segment_keys() keys) candidate counts and
-    // candidate keys (nseg segments per row, dense_segment_keys() slots each).
+    // candidates as (score bits, key) (nseg segments per row,
+    // dense_segment_keys() slots each).
     uint32_t *est;
     int32_t *seg_cnt;
-    int32_t *seg_key;
+    uint2 *seg_buf;
     int nseg;
     // Screening (DoSA certificates), per row of the launch: head order with
     // the kept heads first [nrows, 64] (-1 = no head), weights w * q_scale in

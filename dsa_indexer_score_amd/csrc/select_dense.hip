@@ -239,8 +239,8 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
 }
 
 // Candidates of one segment (kSeg keys) of one row: every visible key
-// whose code is >= the row's estimate, as key indices in key order, into the
-// segment's slot; the segment count is always written.
+// whose code is >= the row's estimate, as (score bits, key) in key order,
+// into the segment's slot; the segment count is always written.
 __global__ void __launch_bounds__(kFilterThreads) filter_kernel(ScoreSelectParams p)
 {
     __shared__ uint32_t red[kFilterThreads / 64];
@@ -261,10 +261,11 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(ScoreSelectParam
     for (int i = 0; i < kPer; ++i) cnt += (j0 + i < rv.n && ord_code(sl.bits[i]) >= est) ? 1u : 0u;
     uint32_t tot;
     uint32_t o = block_excl_scan<kFilterThreads / 64>(cnt, red, tot);
-    int32_t *dst = p.seg_key + slot * (int64_t)kSeg;
+    uint2 *dst = p.seg_buf + slot * (int64_t)kSeg;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-        if (j0 + i < rv.n && ord_code(sl.bits[i]) >= est) dst[o++] = j0 + i;
+        if (j0 + i < rv.n && ord_code(sl.bits[i]) >= est)
+            dst[o++] = make_uint2(sl.bits[i], (uint32_t)(j0 + i));
     if (threadIdx.x == 0) p.seg_cnt[slot] = (int32_t)tot;
 }
 
@@ -274,7 +275,7 @@ __global__ void __launch_bounds__(kFilterThreads) filter_kernel(ScoreSelectParam
 __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams p)
 {
     __shared__ uint32_t hist[kBins1];
-    __shared__ uint32_t ccode[kCap];
+    __shared__ uint32_t cbits[kCap];  // candidates' raw score bits
     __shared__ int32_t ckey[kCap];
     __shared__ uint32_t soff[kDenseThreads];
     __shared__ uint16_t owner[kCap];
@@ -302,17 +303,26 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
         }
     };
 
-    // ---- the segments' candidates, concatenated in key order
+    // ---- the segments' candidates, concatenated in key order.  The first
+    // round's counts are loaded together with the estimate.
     int ncand = -1;  // -1: the list is not usable, select from the full row
-    if (p.est[qrow] != kNoList) {
-        const int nseg_row = (n + kSeg - 1) / kSeg;
-        const int32_t *cnts = p.seg_cnt + qrow * (int64_t)p.nseg;
-        const int32_t *keys = p.seg_key + qrow * (int64_t)p.nseg * kSeg;
-        uint32_t total = 0;
+    const int nseg_row = (n + kSeg - 1) / kSeg;
+    const int32_t *cnts = p.seg_cnt + qrow * (int64_t)p.nseg;
+    const uint32_t est = p.est[qrow];
+    const uint32_t c_first =
+        (int)threadIdx.x < nseg_row ? (uint32_t)cnts[threadIdx.x] : 0u;
+    if (est != kNoList) {
+        const uint2 *cands = p.seg_buf + qrow * (int64_t)p.nseg * kSeg;
+        uint32_t total = 0, off_first = 0, tot_first = 0;
         for (int s0 = 0; s0 < nseg_row; s0 += kDenseThreads) {
             const int sg = s0 + (int)threadIdx.x;
+            const uint32_t c = s0 == 0 ? c_first : (sg < nseg_row ? (uint32_t)cnts[sg] : 0u);
             uint32_t tot;
-            block_excl_scan(sg < nseg_row ? (uint32_t)cnts[sg] : 0u, red, tot);
+            const uint32_t off = block_excl_scan(c, red, tot);
+            if (s0 == 0) {
+                off_first = off;
+                tot_first = tot;
+            }
             total += tot;
         }
         if (total >= need && total <= (uint32_t)kCap) {
@@ -321,36 +331,36 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
             uint32_t done = 0;
             for (int s0 = 0; s0 < nseg_row; s0 += kDenseThreads) {
                 const int sg = s0 + (int)threadIdx.x;
-                const uint32_t c = sg < nseg_row ? (uint32_t)cnts[sg] : 0u;
-                uint32_t tot;
-                soff[threadIdx.x] = done + block_excl_scan(c, red, tot);
+                uint32_t off = off_first, tot = tot_first;
+                if (s0 > 0) off = block_excl_scan(sg < nseg_row ? (uint32_t)cnts[sg] : 0u, red, tot);
+                soff[threadIdx.x] = done + off;
                 __syncthreads();
                 // owner segment of each list slot of this round (LDS only) ...
                 const int nr = nseg_row - s0 < kDenseThreads ? nseg_row - s0 : kDenseThreads;
                 for (int r = wave; r < nr; r += kDenseWaves) {
-                    const uint32_t off = soff[r];
+                    const uint32_t o = soff[r];
                     const uint32_t end = r + 1 < nr ? soff[r + 1] : done + tot;
-                    for (uint32_t i = off + lane; i < end; i += 64) owner[i] = (uint16_t)r;
+                    for (uint32_t i = o + lane; i < end; i += 64) owner[i] = (uint16_t)r;
                 }
                 __syncthreads();
                 // ... then one slot per thread and step, every load independent
                 constexpr int kSlots = kCap / kDenseThreads;
-                int kk[kSlots];
+                uint2 cv[kSlots];
 #pragma unroll
                 for (int x = 0; x < kSlots; ++x) {
                     const uint32_t i = done + threadIdx.x + (uint32_t)x * kDenseThreads;
-                    kk[x] = 0;
+                    cv[x] = make_uint2(0u, 0u);
                     if (i < done + tot) {
                         const int r = owner[i];
-                        kk[x] = keys[(int64_t)(s0 + r) * kSeg + (i - soff[r])];
+                        cv[x] = cands[(int64_t)(s0 + r) * kSeg + (i - soff[r])];
                     }
                 }
 #pragma unroll
                 for (int x = 0; x < kSlots; ++x) {
                     const uint32_t i = done + threadIdx.x + (uint32_t)x * kDenseThreads;
                     if (i < done + tot) {
-                        ccode[i] = ord_code(sc[kk[x]]);
-                        ckey[i] = kk[x];
+                        cbits[i] = cv[x].x;
+                        ckey[i] = (int32_t)cv[x].y;
                     }
                 }
                 __syncthreads();
@@ -368,7 +378,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
         if ((uint32_t)ncand > need)
             block_exact_cut(
                 [&](auto &&f) {
-                    for (int i = threadIdx.x; i < ncand; i += kDenseThreads) f(ccode[i]);
+                    for (int i = threadIdx.x; i < ncand; i += kDenseThreads) f(ord_code(cbits[i]));
                 },
                 need, hist, red, res, cc.tc, cc.exact, cc.need_eq);
         constexpr int kPerC = kCap / kDenseThreads;
@@ -377,7 +387,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
 #pragma unroll
         for (int i = 0; i < kPerC; ++i) {
             const bool valid = i0 + i < ncand;
-            const uint32_t u = valid ? ccode[i0 + i] : 0u;
+            const uint32_t u = valid ? ord_code(cbits[i0 + i]) : 0u;
             ngt += cc.gt(valid, u) ? 1u : 0u;
             neq += cc.eq(valid, u) ? 1u : 0u;
         }
@@ -387,14 +397,15 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
 #pragma unroll
         for (int i = 0; i < kPerC; ++i) {
             const bool valid = i0 + i < ncand;
-            const uint32_t u = valid ? ccode[i0 + i] : 0u;
+            const uint32_t bits = valid ? cbits[i0 + i] : 0u;
+            const uint32_t u = valid ? ord_code(bits) : 0u;
             const bool gt = cc.gt(valid, u), eq = cc.eq(valid, u);
             if (gt || (eq && eq_before < cc.need_eq)) {
                 const uint32_t kb = gt_before + (eq_before < cc.need_eq ? eq_before : cc.need_eq);
                 const int key = ckey[i0 + i];
                 for (int x = 0; x < mexp; ++x) {
                     orow[(int)kb * mexp + x] = key * mexp + x;
-                    if (srow) srow[(int)kb * mexp + x] = __uint_as_float(sc[key]);
+                    if (srow) srow[(int)kb * mexp + x] = __uint_as_float(bits);
                 }
             }
             gt_before += gt ? 1u : 0u;

@@ -78,9 +78,9 @@ typedef struct {
      * give identical results.  The dense workspace holds, each part starting
      * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
      * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
-     * G = ceil(max(T, 1) / 4096)) and the candidate keys (S * G * 4096 * 4),
-     * about 8 bytes per (row, key); it is used only while it stays within
-     * 4 GiB. */
+     * G = ceil(max(T, 1) / 4096)) and the candidates as (score, key) pairs
+     * (S * G * 4096 * 8), about 12 bytes per (row, key); it is used only
+     * while it stays within 4 GiB. */
     int64_t few_query_rows;
 } indexer_config;
 

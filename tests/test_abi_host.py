@@ -84,11 +84,11 @@ def test_workspace_bytes_scale_with_chunk_and_selection():
 
 def _dense_bytes(S, T):
     """The documented few-query layout: scores, estimates, candidate counts
-    and candidate keys, each part 256-byte aligned."""
+    and (score, key) candidates, each part 256-byte aligned."""
     up = lambda x, a: -(-x // a) * a
     G = -(-max(T, 1) // 4096)
     return up(S * up(max(T, 1), 4) * 4, 256) + up(S * 4, 256) + up(S * G * 4, 256) + \
-        S * G * 4096 * 4
+        S * G * 4096 * 8
 
 
 def test_workspace_bytes_of_the_few_query_path():
@@ -98,9 +98,9 @@ def test_workspace_bytes_of_the_few_query_path():
     n = ctypes.c_size_t()
     lib, h = _handle(chunk=16384)
     assert lib.indexer_workspace_bytes(h, 64, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(64, 262144) == 64 * 262144 * 8 + 256 + 64 * 64 * 4
+    assert n.value == _dense_bytes(64, 262144) == 64 * 262144 * 12 + 256 + 64 * 64 * 4
     assert lib.indexer_workspace_bytes(h, 1, 1001, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(1, 1001) == 4096 + 256 + 256 + 4096 * 4
+    assert n.value == _dense_bytes(1, 1001) == 4096 + 256 + 256 + 4096 * 8
     assert lib.indexer_workspace_bytes(h, 65, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 65 * 20736 * 8            # above the default: streaming buffers
     assert lib.indexer_workspace_bytes(h, 64, 2 ** 25, 64, 128, 1, 2048, ctypes.byref(n)) == 0
