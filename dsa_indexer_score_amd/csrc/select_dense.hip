@@ -27,9 +27,9 @@
 //  3. ordered output: a block-wide prefix count of entries above c and of
 //     entries equal to c (packed into one 32-bit scan) gives each kept key
 //     its output slot, so ties go to the lowest keys.
-// Passes over the row read chunks of 16K keys, 16 consecutive keys per
-// thread loaded as four 16-byte vectors, so each thread has its loads in
-// flight together; no pass over the row uses atomics.
+// Passes over the row read chunks of 16K keys (the filter: segments of 4K),
+// 16 consecutive keys per thread loaded as four 16-byte vectors, so each
+// thread has its loads in flight together; histograms use LDS atomics only.
 #include "kernels.h"
 #include "select_common.h"
 
@@ -125,7 +125,9 @@ __device__ void block_boundary(const uint32_t *hist, int nbins, uint32_t need, u
 // Exact cut keeping `need` of the codes that src(f) feeds to f (each thread
 // feeds its own share): keep codes > tc plus the first need_eq codes equal
 // to tc in key order (exact), or every code >= tc.  1 <= need <= count.
-template <class Src>
+// LEVELS = 2 stops after the 22-bit prefix: tc is then the lower edge of the
+// prefix bin holding the need-th code (a lower bound, exact = false).
+template <int LEVELS = 3, class Src>
 __device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32_t *red,
                                 uint32_t *res, uint32_t &tc, bool &exact, uint32_t &need_eq)
 {
@@ -153,7 +155,7 @@ __device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32
     block_boundary(hist, 1024, need - a1, red, res, b2, a2, h2);
     const uint32_t pre = ((uint32_t)b1 << 10) | (uint32_t)b2;  // top 22 bits
     const uint32_t above = a1 + a2;
-    if (above + h2 == need) {
+    if (LEVELS == 2 || above + h2 == need) {
         tc = pre << 10;
         return;
     }
@@ -205,9 +207,10 @@ struct RowView {  // one row of the dense scores
 };
 
 // Threshold estimate of each row: the c-th best code of a sample of 128
-// blocks of 64 keys spread over the row, c about 1.5x the sample's expected
-// share of the selection plus a margin, so that the keys at or above it
-// almost always hold the whole selection and fit the candidate list.
+// blocks of 64 keys spread over the row (to a 22-bit prefix: the lower edge
+// of the prefix bin holding it), c about 1.5x the sample's expected share of
+// the selection plus a margin, so that the keys at or above it almost always
+// hold the whole selection and fit the candidate list.
 __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectParams p)
 {
     __shared__ uint32_t hist[kBins1];
@@ -227,7 +230,7 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
             __syncthreads();
             uint32_t est_eq;
             bool est_exact;
-            block_exact_cut(
+            block_exact_cut<2>(  // a lower bound of the c-th code is all it needs
                 [&](auto &&f) {
                     for (int i = threadIdx.x; i < kCap; i += kDenseThreads) f(sample[i]);
                 },
