@@ -136,6 +136,30 @@ def test_workspace_bytes_with_screening():
 FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
 
 
+def test_screen_certificates_validation():
+    """indexer_screen_certificates rejects what it cannot build before any
+    device call: H outside 33..64 or an unsupported d, missing pointers, a
+    scale that does not match the dtype, misaligned q."""
+    lib, h = _handle()
+    E, U = _lib.IDX_EINVAL, _lib.IDX_EUNSUPPORTED
+    f = lambda **kw: lib.indexer_screen_certificates(
+        h, kw.get("q", FAKE), kw.get("qs", None), kw.get("w", FAKE), kw.get("ws", 0),
+        kw.get("S", 4), kw.get("H", 64), kw.get("d", 128), kw.get("perm", FAKE),
+        kw.get("wv", FAKE), kw.get("wt", FAKE), kw.get("e", FAKE), None)
+    assert f(S=0) == 0
+    assert f(H=32) == U and f(H=65) == U and f(d=96) == U
+    assert f(q=None) == E and f(perm=None) == E and f(e=None) == E
+    assert f(qs=FAKE) == E                                # scales only for fp8
+    assert f(q=ctypes.c_void_p(0x10008)) == E
+    assert f(ws=10) == E                                  # w rows would overlap
+    lib.indexer_destroy(h)
+    lib, h = _handle(dtype=_lib.IDX_FP8_E4M3)
+    f8 = lambda **kw: lib.indexer_screen_certificates(h, FAKE, kw.get("qs", None), FAKE, 0, 4, 64,
+                                                      128, FAKE, FAKE, FAKE, FAKE, None)
+    assert f8() == E                                      # fp8 needs q_scale
+    lib.indexer_destroy(h)
+
+
 def _call(lib, h, **kw):
     a = dict(q=FAKE, q_scale=None, w=FAKE, w_stride=0, k=FAKE, k_scale=None, S=16, T=16, H=64,
              d=128, m=1, topk=4, causal=1, q_pos0=0, idx=FAKE, vl=FAKE, sel=None, ws=FAKE,
