@@ -129,6 +129,8 @@ def main():
                     help="also time the three-region q-cluster split of the adjacent pairs")
     ap.add_argument("--wdist", default=None, choices=["normal_bcast", "lognormal_bcast"],
                     help="override the workload's head-weight distribution")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step in HIP graphs once and time replays")
     ap.add_argument("--screen", action="store_true",
                     help="DoSA certificate screening on the streaming path (lossless)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
@@ -189,9 +191,7 @@ def main():
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def score():
         if docs:
             ix.score_topk_varlen(inp.q, inp.w, inp.k, docs["cu_q"], docs["cu_k"], m=inp.m,
                                  topk=inp.topk, causal=inp.causal, cu_tok=docs["cu_tok"],
@@ -201,9 +201,29 @@ def main():
             ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
                           q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
                           workspace=ws, out=(idx, vl, None))
+
+    if args.graph:
+        # The step captured once (score_topk and pair_overlap as two graphs,
+        # so each can be timed) and replayed: no host work per step.
+        score()
+        torch.cuda.synchronize()
+        g_score, g_ovl = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_score):
+            score()
+        with torch.cuda.graph(g_ovl):
+            shared_g = dsai.pair_overlap(idx, vl)
+        score, overlap = g_score.replay, lambda: (g_ovl.replay(), shared_g)[1]
+    else:
+        def overlap():
+            return dsai.pair_overlap(idx, vl)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        score()
         if ev:
             ev[1].record(stream)
-        shared = dsai.pair_overlap(idx, vl)
+        shared = overlap()
         if ev:
             ev[2].record(stream)
         return shared
@@ -307,7 +327,7 @@ def main():
         "config": {"workload": workload_name, "S": inp.S, "T": inp.T, "H": inp.H, "d": inp.d,
                    "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
                    inp.query_chunk, "launches_per_step": n_launch, "screen": bool(args.screen),
-                   "wdist": inp.meta.get("wdist"),
+                   "wdist": inp.meta.get("wdist"), "graph": bool(args.graph),
                    "parallelism": "none (1 GPU)"},
         "queries_per_s": inp.S / (ms_per_step / 1e3),
         "mfma_frac": achieved_tflops / peak,
