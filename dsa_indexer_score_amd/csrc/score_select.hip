@@ -36,6 +36,10 @@
 //    multiplies the finished score.
 //  * The two waves that share a SIMD (w and w + 4) select at opposite ends of
 //    a tile, so one wave's branchy selection overlaps the other's MFMAs.
+//  * Optional screening (SCREEN instance; DoSA summary, "Method steps"):
+//    head block 0 holds a per-row certificate's kept heads and bounds every
+//    key; only keys whose bound reaches the running threshold get block 1,
+//    gathered 32 per MFMA column block (see screen_tile below).
 //
 // Streaming selection (per wave, per query; no block barrier involved):
 //  * Scores map to an order-preserving 32-bit code u (-0 folded into +0).
@@ -262,44 +266,44 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // One selection step: each lane offers one (score, key), ok = the key
     // is visible to this row; keys arrive in ascending order across calls.
     auto consider = [&](float sc, int64_t key, bool ok) __attribute__((always_inline)) {
-            const uint32_t bits = __float_as_uint(sc);
-            const bool pass = sc >= tau_f && ok;
-            const uint64_t mask = __ballot(pass);
-            if (mask) {
-                const uint32_t u = ord_code(bits);
-                if (pass) {
-                    buf[cnt + lane_rank(mask)] = make_uint2(bits, (uint32_t)key);
-                    hist_add(hist, u >> kShift1);
-                }
-                cnt += __popcll(mask);
-                if (tracking) {
-                    // keep tau near the edge of the bin holding the Ksel-th best;
-                    // the boundary may lag by up to one group of entries
-                    above += __popcll(__ballot(pass && (int)(u >> kShift1) > tb));
-                    if (above >= p.ksel + kSelGroup) {
-                        advance_boundary(hist, p.ksel, lane, tb, above);
-                        const uint32_t edge = (uint32_t)tb << kShift1;
-                        tau = edge > tau ? edge : tau;
-                        tau_f = code_floor_value(tau);
-                    }
-                } else if (cnt >= p.ksel) {
-                    tracking = true;
-                    int hb;
-                    find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
+        const uint32_t bits = __float_as_uint(sc);
+        const bool pass = sc >= tau_f && ok;
+        const uint64_t mask = __ballot(pass);
+        if (mask) {
+            const uint32_t u = ord_code(bits);
+            if (pass) {
+                buf[cnt + lane_rank(mask)] = make_uint2(bits, (uint32_t)key);
+                hist_add(hist, u >> kShift1);
+            }
+            cnt += __popcll(mask);
+            if (tracking) {
+                // keep tau near the edge of the bin holding the Ksel-th best;
+                // the boundary may lag by up to one group of entries
+                above += __popcll(__ballot(pass && (int)(u >> kShift1) > tb));
+                if (above >= p.ksel + kSelGroup) {
+                    advance_boundary(hist, p.ksel, lane, tb, above);
                     const uint32_t edge = (uint32_t)tb << kShift1;
                     tau = edge > tau ? edge : tau;
                     tau_f = code_floor_value(tau);
                 }
-                if (cnt > p.cap - kSelGroup) {  // overflow fallback
-                    wave_sync_mem();
-                    const Cut cut = choose_cut(buf, cnt, p.ksel, hist, true, approx_limit, lane);
-                    compact(buf, cnt, cut, hist, lane);
-                    tau = cut.tc + 1;
-                    tau_f = code_floor_value(tau);
-                    int hb;
-                    find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
-                }
+            } else if (cnt >= p.ksel) {
+                tracking = true;
+                int hb;
+                find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
+                const uint32_t edge = (uint32_t)tb << kShift1;
+                tau = edge > tau ? edge : tau;
+                tau_f = code_floor_value(tau);
             }
+            if (cnt > p.cap - kSelGroup) {  // overflow fallback
+                wave_sync_mem();
+                const Cut cut = choose_cut(buf, cnt, p.ksel, hist, true, approx_limit, lane);
+                compact(buf, cnt, cut, hist, lane);
+                tau = cut.tc + 1;
+                tau_f = code_floor_value(tau);
+                int hb;
+                find_boundary(hist, kBins1, p.ksel, lane, tb, above, hb);
+            }
+        }
     };
     auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
         if constexpr (DENSE) {
