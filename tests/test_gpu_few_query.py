@@ -147,3 +147,19 @@ def test_few_query_empty_and_single_key():
     inp = replace(gen.generate("c4_csa_256k", S=4, T=1), q_pos0=3).to(DEV)
     idx, vl, _ = run(inp, few_query_rows=64)
     assert vl.tolist() == [1, 1, 1, 1] and idx[:, 0].tolist() == [0, 0, 0, 0]
+
+
+def test_few_query_more_than_1024_candidate_segments():
+    """A row of 4.5M keys has more than 1,024 filter segments of 4,096 keys,
+    so the cut kernel gathers the candidates in several rounds; ties on
+    repeated keys make the rounds' boundaries matter."""
+    g = torch.Generator().manual_seed(9)
+    T, H, d = 4_500_000, 4, 32
+    base = torch.randn(4096, d, generator=g)
+    k = base[torch.randint(0, 4096, (T,), generator=g)].bfloat16()   # many equal scores
+    q = torch.randn(2, H, d, generator=g).bfloat16()
+    w = torch.randn(H, generator=g)
+    inp = replace(gen.custom(q=q, k=k, w=w, topk=300), q_pos0=T - 2).to(DEV)
+    dense, stream = _both_paths(inp)
+    _assert_identical(dense, stream)
+    assert (dense[1] == 300).all()
