@@ -34,6 +34,11 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", f) for f in
                ("score_select.hip", "mfma_ops.h", "select_common.h", "kernels.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_select_c4_csa_256k_pmc.md")
+# the one-row decode step of the 1M-token workload (few-query path)
+DECODE_SRCS = [os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", f) for f in
+               ("score_rows.hip", "select_dense.hip", "mfma_ops.h", "select_common.h",
+                "kernels.h")]
+DECODE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "few_query_decode_c5_csa_1m_pmc.md")
 
 
 def log(msg):
@@ -59,24 +64,25 @@ def visible_pairs(S, T, m, causal, q_pos0=0):
     return total
 
 
-def kernel_sha():
-    """sha256[:16] of the sources the streaming kernel is compiled from."""
+def kernel_sha(srcs=None):
+    """sha256[:16] of the sources a kernel is compiled from (default: the
+    streaming kernel's)."""
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in srcs or KERNEL_SRCS:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per score_select launch from the committed counter summary,
-    if it was taken on the current kernel source (else None)."""
-    if not os.path.exists(PMC_SUMMARY):
+def stored_traffic(summary=PMC_SUMMARY, srcs=None, key="traffic_bytes_per_launch"):
+    """HBM bytes from a committed counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    if not os.path.exists(summary):
         return None
-    text = open(PMC_SUMMARY).read()
+    text = open(summary).read()
     sha = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
-    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not val or sha.group(1) != kernel_sha():
+    val = re.search(key + r":\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sha(srcs):
         return None
     return float(val.group(1))
 
@@ -306,8 +312,11 @@ def main():
                      (inp.T * 4 + inp.S * inp.H * 4 if inp.dtype == "fp8" else 0) +
                      inp.S * (W + 1) * 4)
         gbs = alg_bytes / score_s / 1e9
+        dtraffic = None
+        if args.workload == "c5_csa_1m" and args.decode == 1 and not args.wdist:
+            dtraffic = stored_traffic(DECODE_PMC_SUMMARY, DECODE_SRCS, "traffic_bytes_per_step")
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                    "frac": gbs / HBM_PEAK_GBS, "traffic": dtraffic,
                     "kernel": "few-query step (dense scoring + block select)",
                     "bytes_per_launch": alg_bytes, "avg_launch_ms": score_s * 1e3,
                     "mfma_frac": achieved_tflops / peak}
