@@ -1,8 +1,9 @@
 // select_dense: exact top-k of a few queries' materialised scores.
 //
 // For a handful of query rows (decode, small batches against a long key
-// set) the scoring kernel runs in its dense mode and writes each row's
-// visible scores to the workspace (a [rows, T] array: kilobytes to tens of
+// set) the scoring kernel runs in its dense mode (one or two rows: the rows
+// kernel of score_rows.hip) and writes each row's visible scores to the
+// workspace (a [rows, T] array: kilobytes to tens of
 // megabytes here, never the prefill-sized tensor).  Three kernels then find
 // the same exact result as the streaming selection -- the Ksel best keys
 // under the total order (higher score first, equal scores to the lower key
@@ -234,8 +235,7 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
                 [&](auto &&f) {
                     for (int i = threadIdx.x; i < kCap; i += kDenseThreads) f(sample[i]);
                 },
-                c, hist, red, res, est, est_exact, est_eq);
-            if (est == kNoList) est = kNoList - 1;  // keep the marker unambiguous
+                c, hist, red, res, est, est_exact, est_eq);  // low bits 0: never kNoList
         }
     }
     if (threadIdx.x == 0) p.est[blockIdx.x] = est;
