@@ -101,10 +101,11 @@ def cpu_baseline(inp, budget_s, seed, docs=None):
         t0 = time.perf_counter()
         if docs:
             cq = np.asarray(docs["cu_q_host"])
+            p0 = docs.get("pos0_host", np.zeros(len(cq) - 1, np.int64))
             orc.select_rows_varlen(inp, cq, docs["cu_k_host"], rows=rows, nthreads=threads,
-                                   cu_tok=cq[:-1] if inp.expand else None)
+                                   pos0=p0, cu_tok=docs.get("cu_tok_host"))
             doc = np.searchsorted(cq, rows, side="right") - 1
-            vis = [min(docs["nkeys"][i], (int(r) - int(cq[i]) + 1) // inp.m)
+            vis = [min(docs["nkeys"][i], (int(p0[i]) + int(r) - int(cq[i]) + 1) // inp.m)
                    for r, i in zip(rows, doc)]
         else:
             orc.select_rows(inp, rows, nthreads=threads)
@@ -139,6 +140,11 @@ def main():
                     help="capture the step in HIP graphs once and time replays")
     ap.add_argument("--screen", action="store_true",
                     help="DoSA certificate screening on the streaming path (lossless)")
+    ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
+                    help="batched decode: B documents of the workload's full context packed "
+                         "together, one query row at the end of each (varlen entry point)")
+    ap.add_argument("--few-query-rows", type=int, default=None,
+                    help="override indexer_config.few_query_rows (negative: never)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="few-query shape: N query rows at the end of the workload's full "
                          "context (every key visible), timed through the few-query path")
@@ -159,7 +165,13 @@ def main():
     log(f"bench: library {dsai.library_path()}")
     t0 = time.perf_counter()
     over = {"wdist": args.wdist} if args.wdist else {}
-    if args.decode:
+    if args.decode_batch:
+        from dataclasses import replace
+        full_T = gen.CONFIGS[args.workload]["T"]
+        inp = gen.generate(args.workload, S=args.decode_batch, T=args.decode_batch * full_T,
+                           device=dev, **over)
+        inp = replace(inp, query_chunk=None)
+    elif args.decode:
         from dataclasses import replace
         full_T = gen.CONFIGS[args.workload]["T"]
         inp = gen.generate(args.workload, S=args.decode, T=full_T, device=dev, **over)
@@ -171,9 +183,11 @@ def main():
         f"topk={inp.topk} dtype={inp.dtype} chunk={inp.query_chunk} in "
         f"{time.perf_counter() - t0:.1f} s")
 
+    few = max(64, args.decode, args.decode_batch) if (args.decode or args.decode_batch) else 0
+    if args.few_query_rows is not None:
+        few = args.few_query_rows
     ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
-                      query_chunk=inp.query_chunk or 0,
-                      few_query_rows=max(64, args.decode) if args.decode else 0,
+                      query_chunk=inp.query_chunk or 0, few_query_rows=few,
                       screen=args.screen, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
     docs = None
@@ -189,7 +203,23 @@ def main():
             raise SystemExit("the workload has fewer keys than its documents' pools")
         t32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32, device=dev)
         docs = dict(cu_q=t32(cu_q), cu_k=t32(cu_k), cu_tok=t32(cu_q[:-1]) if inp.expand else None,
-                    lens=lens, nkeys=nkeys, cu_q_host=cu_q, cu_k_host=cu_k)
+                    lens=lens, nkeys=nkeys, cu_q_host=cu_q, cu_k_host=cu_k,
+                    cu_tok_host=cu_q[:-1] if inp.expand else None,
+                    pairs=sum(visible_pairs(n, k, inp.m, inp.causal)
+                              for n, k in zip(lens, nkeys)))
+    if args.decode_batch:
+        # document i: keys [i*T_doc, (i+1)*T_doc), one row at its last token
+        B, T_doc = args.decode_batch, inp.T // args.decode_batch
+        cu_q = np.arange(B + 1)
+        cu_k = np.arange(B + 1) * T_doc
+        pos0 = np.full(B, T_doc * inp.m - 1, np.int64)
+        cu_tok = np.arange(B) * T_doc * inp.m
+        t32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32, device=dev)
+        docs = dict(cu_q=t32(cu_q), cu_k=t32(cu_k), cu_tok=t32(cu_tok) if inp.expand else None,
+                    pos0=torch.as_tensor(pos0, device=dev), lens=[1] * B, nkeys=[T_doc] * B,
+                    cu_q_host=cu_q, cu_k_host=cu_k, pos0_host=pos0,
+                    cu_tok_host=cu_tok if inp.expand else None,
+                    pairs=B * (min(T_doc, T_doc * inp.m // inp.m) if inp.causal else T_doc))
     idx = torch.empty((inp.S, W), dtype=torch.int32, device=dev)
     vl = torch.empty((inp.S,), dtype=torch.int32, device=dev)
     wsb = ix.workspace_bytes_varlen if docs else ix.workspace_bytes
@@ -200,9 +230,9 @@ def main():
     def score():
         if docs:
             ix.score_topk_varlen(inp.q, inp.w, inp.k, docs["cu_q"], docs["cu_k"], m=inp.m,
-                                 topk=inp.topk, causal=inp.causal, cu_tok=docs["cu_tok"],
-                                 q_scale=inp.q_scale, k_scale=inp.k_scale, workspace=ws,
-                                 out=(idx, vl, None))
+                                 topk=inp.topk, causal=inp.causal, pos0=docs.get("pos0"),
+                                 cu_tok=docs["cu_tok"], q_scale=inp.q_scale,
+                                 k_scale=inp.k_scale, workspace=ws, out=(idx, vl, None))
         else:
             ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
                           q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
@@ -251,8 +281,7 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     if docs:
-        pairs = sum(visible_pairs(n, k, inp.m, inp.causal) for n, k in
-                    zip(docs["lens"], docs["nkeys"]))
+        pairs = docs["pairs"]
     else:
         pairs = visible_pairs(inp.S, inp.T, inp.m, inp.causal, inp.q_pos0)
     triples = pairs * inp.H
@@ -261,7 +290,8 @@ def main():
     score_s = float(np.mean(score_ms)) / 1e3
     achieved_tflops = flops / score_s / 1e12
     peak = PEAK_TFLOPS[inp.dtype]
-    traffic = stored_traffic() if not (args.decode or args.varlen or args.screen) else None
+    traffic = stored_traffic() if not (args.decode or args.decode_batch or args.varlen or
+                                       args.screen) else None
 
     st = dsai.overlap_summary(shared, vl)
     regions = None
@@ -295,16 +325,19 @@ def main():
     if args.decode:
         workload_name = f"{inp.name} decode: {inp.S} rows at positions " \
                         f"{inp.q_pos0}..{inp.q_pos0 + inp.S - 1}"
-    if docs:
+    if args.varlen:
         workload_name = f"{inp.name} packed as {args.varlen} documents of {docs['lens'][0]} " \
                         f"tokens (varlen)"
+    if args.decode_batch:
+        workload_name = f"{inp.name} batched decode: {args.decode_batch} documents of " \
+                        f"{inp.T // args.decode_batch} keys, one row at the end of each (varlen)"
     roofline = {"bound": "mfma", "achieved": achieved_tflops, "peak": peak,
                 "unit": "TFLOP/s", "frac": achieved_tflops / peak,
                 "traffic": None if traffic is None else traffic,
                 "kernel": "score_select", "flops_per_launch": flops / n_launch,
                 "avg_launch_ms": score_s * 1e3 / n_launch}
-    if args.decode:
-        # Few-query step (dense scoring + one selection block per row): bound
+    if args.decode or args.decode_batch:
+        # Few-query step (dense scoring + candidate filter + exact cut): bound
         # by reading the key set once from HBM.
         esz = {"bf16": 2, "fp8": 1, "f32": 4}[inp.dtype]
         W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
@@ -317,7 +350,7 @@ def main():
             dtraffic = stored_traffic(DECODE_PMC_SUMMARY, DECODE_SRCS, "traffic_bytes_per_step")
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": gbs / HBM_PEAK_GBS, "traffic": dtraffic,
-                    "kernel": "few-query step (dense scoring + block select)",
+                    "kernel": "few-query step (dense scoring, candidate filter, exact cut)",
                     "bytes_per_launch": alg_bytes, "avg_launch_ms": score_s * 1e3,
                     "mfma_frac": achieved_tflops / peak}
     result = {

@@ -253,10 +253,10 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     const int64_t pmax = causal && !docs.on ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
     const int64_t rows = rows_per_launch(cfg, S);
-    const bool dense = !docs.on && use_dense(cfg, S, T);
+    const bool dense = use_dense(cfg, S, T);
     const bool screen = !docs.on && !dense && use_screen(cfg, H);
-    const size_t need = docs.on ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
-                                : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
+    const size_t need = docs.on && !dense ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
+                                          : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
 
     DeviceGuard guard(h->device);
@@ -290,6 +290,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     p.pos0 = docs.pos0;
     p.cu_tok = docs.cu_tok;
     p.ndoc = docs.ndoc;
+    p.varlen = docs.on;
     const int nb = (H + 31) / 32;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dense) {
@@ -315,8 +316,9 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.split_keys = tiles_per * dsai::kKeysPerTile;
         p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
         bool supported = true;
-        hipError_t e = S <= kRowsKernelMax
-                           ? dsai::launch_score_rows(cfg.dtype, nb, d, p, st, &supported)
+        // packed documents: every row its own key window, one row per slab
+        hipError_t e = S <= kRowsKernelMax || docs.on
+                           ? dsai::launch_score_rows(cfg.dtype, nb, d, docs.on, p, st, &supported)
                            : dsai::launch_score_select(cfg.dtype, nb, d, true, false, false, p,
                                                        st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
@@ -379,7 +381,9 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
-    *bytes = (size_t)(rows_per_launch(h->cfg, S) * capacity(ksel, T) * (int64_t)sizeof(uint2));
+    *bytes = use_dense(h->cfg, S, T)
+                 ? (size_t)DenseLayout(S, T).bytes
+                 : (size_t)(rows_per_launch(h->cfg, S) * capacity(ksel, T) * (int64_t)sizeof(uint2));
     return IDX_OK;
 }
 

@@ -44,6 +44,7 @@ struct ScoreSelectParams {
     const int64_t *pos0;
     const int32_t *cu_tok;
     int ndoc;
+    int varlen;             // 1: rows are packed documents (the fields above)
     // Few-query selection scratch (dense mode): per-row threshold estimate,
     // per (row, segment of dense_segment_keys() keys) candidate counts and
     // candidates as (score bits, key) (nseg segments per row,
@@ -81,8 +82,9 @@ hipError_t launch_key_norms(int dtype, int d, const ScoreSelectParams &p, hipStr
 
 // Dense scores of one or two rows (p.scores, as the dense mode of
 // launch_score_select writes them, bit for bit), every CU streaming its own
-// slice of the keys.
-hipError_t launch_score_rows(int dtype, int nb, int d, const ScoreSelectParams &p,
+// slice of the keys; varlen: any number of packed-document rows, one per
+// slab, each row's scores over its own key window.
+hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, const ScoreSelectParams &p,
                              hipStream_t stream, bool *supported);
 
 // Exact top-k of each row's dense scores and its canonical output row:

@@ -1,4 +1,5 @@
-// score_rows: dense scoring of one or two query rows (decode) for gfx950.
+// score_rows: dense scoring of one or two query rows (decode) for gfx950,
+// and of packed-document rows (batched decode: each row its own keys).
 //
 // Writes, for every key j visible to row t,
 //     s_tj = sum_h w[t,h] * ReLU(q[t,h,:] . k[j,:])
@@ -31,9 +32,10 @@ constexpr int kRowsWaves = 4;
 constexpr int kRowsThreads = kRowsWaves * 64;
 constexpr int kTargetWaves = 1024;  // about one wave per SIMD; each streams several groups
 
-template <int DT, int NB, int D, int SQ>
-__global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectParams p, int gpw)
+template <int DT, int NB, int D, int SQ, bool VARLEN>
+__global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectParams p)
 {
+    static_assert(!VARLEN || SQ == 1, "packed documents: one row per slab");
     using O = Op<DT, D>;
     using A = typename O::A;
     constexpr int KS = O::KS, ES = O::ES, RAW = O::RAW;
@@ -41,17 +43,27 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = lane >> 5, l32 = lane & 31;
 
-    // rows of this slab and the keys they see
+    // rows of this slab and the keys they see: keys [klo, klo + Pq[i]) of
+    // the key array (klo = 0 but for packed documents, one row per slab)
     const int64_t r0 = (int64_t)blockIdx.y * SQ;
     int64_t Pq[SQ];
-    int64_t Pmax = 0;
+    int64_t Pmax = 0, klo = 0;
 #pragma unroll
     for (int i = 0; i < SQ; ++i) {
         const int64_t r = r0 + i;
-        Pq[i] = r < p.nrows ? visible_keys(p.q_pos0 + p.row0 + r, p.T, p.m, p.causal) : 0;
+        if constexpr (VARLEN) {
+            const DocWindow dw = r < p.nrows ? doc_window(p, p.row0 + r) : DocWindow{};
+            Pq[i] = dw.P;
+            klo = dw.klo;
+        } else {
+            Pq[i] = r < p.nrows ? visible_keys(p.q_pos0 + p.row0 + r, p.T, p.m, p.causal) : 0;
+        }
         Pmax = Pq[i] > Pmax ? Pq[i] : Pmax;
     }
+    // the slab's 64-key groups, split evenly over the slab's waves
     const int64_t ngroups = (Pmax + kSelGroup - 1) / kSelGroup;
+    const int64_t nwaves = (int64_t)gridDim.x * kRowsWaves;
+    const int64_t gpw = (ngroups + nwaves - 1) / nwaves;
     const int64_t g0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * gpw;
     if (g0 >= ngroups) return;
     const int64_t g1 = g0 + gpw < ngroups ? g0 + gpw : ngroups;
@@ -97,11 +109,11 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     auto load_group = [&](int64_t g, uint4 (&dst)[2][RAW], float &sc) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int64_t key = g * kSelGroup + 32 * c + l32;
+            const int64_t key = klo + g * kSelGroup + 32 * c + l32;
             raw_row<O, D>(kbytes + (key < p.T ? key : p.T - 1) * ROWB, hh, dst[c]);
         }
         if (DT == 2) {
-            const int64_t key = g * kSelGroup + lane;
+            const int64_t key = klo + g * kSelGroup + lane;
             sc = p.k_scale[key < p.T ? key : p.T - 1];
         }
     };
@@ -152,38 +164,40 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     }
 }
 
-template <int DT, int NB, int D, int SQ>
+template <int DT, int NB, int D, int SQ, bool VARLEN>
 hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
 {
-    // the last row sees the most keys
-    const int64_t pmax = visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
+    // the last row sees the most keys (packed documents: at most all of them)
+    const int64_t pmax =
+        VARLEN ? p.T : visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
     const int64_t ngroups = (pmax + kSelGroup - 1) / kSelGroup;
     const int64_t nslab = (p.nrows + SQ - 1) / SQ;
     if (ngroups <= 0 || nslab <= 0) return hipSuccess;
-    int64_t gpw = (ngroups * nslab + kTargetWaves - 1) / kTargetWaves;
-    gpw = gpw < 1 ? 1 : gpw;
-    const int64_t waves = (ngroups + gpw - 1) / gpw;
+    // about kTargetWaves waves in all, at most one per group of a slab
+    int64_t waves = (kTargetWaves + nslab - 1) / nslab;
+    waves = waves < ngroups ? waves : ngroups;
     const int64_t blocks = ((waves + kRowsWaves - 1) / kRowsWaves + 7) / 8 * 8;
-    hipLaunchKernelGGL((score_rows_kernel<DT, NB, D, SQ>), dim3((unsigned)blocks, (unsigned)nslab),
-                       dim3(kRowsThreads), 0, stream, p, (int)gpw);
+    hipLaunchKernelGGL((score_rows_kernel<DT, NB, D, SQ, VARLEN>),
+                       dim3((unsigned)blocks, (unsigned)nslab), dim3(kRowsThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DT, int NB, int D>
-hipError_t launch_sq(const ScoreSelectParams &p, hipStream_t stream)
+hipError_t launch_sq(const ScoreSelectParams &p, bool varlen, hipStream_t stream)
 {
-    return p.nrows == 1 ? launch_rows<DT, NB, D, 1>(p, stream)
-                        : launch_rows<DT, NB, D, 2>(p, stream);
+    if (varlen) return launch_rows<DT, NB, D, 1, true>(p, stream);
+    return p.nrows == 1 ? launch_rows<DT, NB, D, 1, false>(p, stream)
+                        : launch_rows<DT, NB, D, 2, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_rows(int dtype, int nb, int d, const ScoreSelectParams &p,
+hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, const ScoreSelectParams &p,
                              hipStream_t stream, bool *supported)
 {
     *supported = true;
 #define DSAI_CASE(DT, NB, D) \
-    if (dtype == DT && nb == NB && d == D) return launch_sq<DT, NB, D>(p, stream);
+    if (dtype == DT && nb == NB && d == D) return launch_sq<DT, NB, D>(p, varlen, stream);
     DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
     DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
     DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)

@@ -116,27 +116,11 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     int64_t kbeg, kend;  // keys this block walks
     if constexpr (VARLEN) {
         __shared__ int64_t wlo[kQueriesPerBlock], whi[kQueriesPerBlock];
-        int doc = -1;
-        if (active && p.ndoc > 0 && t >= p.cu_q[0] && t < p.cu_q[p.ndoc]) {
-            int lo = 0, hi = p.ndoc;  // largest doc with cu_q[doc] <= t
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (p.cu_q[mid] <= t) lo = mid;
-                else hi = mid;
-            }
-            doc = lo;
-        }
-        pos = -1;
-        Pq = 0;
-        if (doc >= 0) {
-            pos = (p.pos0 ? p.pos0[doc] : 0) + (t - p.cu_q[doc]);
-            const int64_t a = p.cu_k[doc], b = p.cu_k[doc + 1];
-            klo = a < 0 ? 0 : (a > p.T ? p.T : a);
-            const int64_t khi_doc = b < klo ? klo : (b > p.T ? p.T : b);
-            Pq = visible_keys(pos, khi_doc - klo, p.m, p.causal);
-            if (pos < 0) Pq = 0;
-            tok0 = p.cu_tok ? p.cu_tok[doc] : 0;
-        }
+        const DocWindow dw = active ? doc_window(p, t) : DocWindow{};
+        pos = dw.pos;
+        Pq = dw.P;
+        klo = dw.klo;
+        tok0 = dw.tok0;
         if (lane == 0) {
             wlo[wave] = Pq > 0 ? klo : INT64_MAX;
             whi[wave] = Pq > 0 ? klo + Pq : INT64_MIN;

@@ -65,6 +65,37 @@ __host__ __device__ __forceinline__ int64_t visible_keys(int64_t pos, int64_t T,
     return c < T ? c : T;
 }
 
+// Key window of call row t in packed documents: the row's document doc (the
+// largest with cu_q[doc] <= t; none for padding rows after cu_q[ndoc]), its
+// position pos = pos0[doc] + t - cu_q[doc] inside the document, its visible
+// keys [klo, klo + P) of the packed key array (the document's keys
+// cu_k[doc] .. cu_k[doc + 1], clamped to [0, T)), and tok0 = cu_tok[doc], the
+// packed token index of the document's position 0.  P = 0 for padding rows
+// and negative positions.
+struct DocWindow {
+    int64_t pos = -1, P = 0, klo = 0, tok0 = 0;
+};
+template <class Params>
+__device__ __forceinline__ DocWindow doc_window(const Params &p, int64_t t)
+{
+    DocWindow w;
+    if (p.ndoc <= 0 || t < p.cu_q[0] || t >= p.cu_q[p.ndoc]) return w;
+    int lo = 0, hi = p.ndoc;  // largest doc with cu_q[doc] <= t
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_q[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    const int doc = lo;
+    w.pos = (p.pos0 ? p.pos0[doc] : 0) + (t - p.cu_q[doc]);
+    const int64_t a = p.cu_k[doc], b = p.cu_k[doc + 1];
+    w.klo = a < 0 ? 0 : (a > p.T ? p.T : a);
+    const int64_t khi = b < w.klo ? w.klo : (b > p.T ? p.T : b);
+    w.P = w.pos < 0 ? 0 : visible_keys(w.pos, khi - w.klo, p.m, p.causal);
+    w.tok0 = p.cu_tok ? p.cu_tok[doc] : 0;
+    return w;
+}
+
 
 // ---------------------------------------------------------------------------
 // Selection helpers (one wave, one query).  Codes are cut in three radix

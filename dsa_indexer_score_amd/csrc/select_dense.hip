@@ -191,16 +191,28 @@ constexpr int kSampleBlock = 64;      // consecutive keys per sample block
 constexpr uint32_t kAllKeys = 0u;     // estimate: every key is a candidate
 constexpr uint32_t kNoList = 0xFFFFFFFFu;  // estimate: select from the full row
 
-struct RowView {  // one row of the dense scores
-    int64_t t, pos, P;
+// One row of the dense scores: score j is key klo + j; an output key j is
+// written as klo + j, or expanded as tok0 + j m + x (packed documents: the
+// row's document window and token offset; else klo = tok0 = 0).
+struct RowView {
+    int64_t t, pos, P, klo, tok0;
     int n;
     const uint32_t *sc;
     uint32_t need;
     __device__ RowView(const ScoreSelectParams &p, int64_t qrow)
     {
         t = p.row0 + qrow;
-        pos = p.q_pos0 + t;
-        P = visible_keys(pos, p.T, p.m, p.causal);
+        if (p.varlen) {
+            const DocWindow w = doc_window(p, t);
+            pos = w.pos;
+            P = w.P;
+            klo = w.klo;
+            tok0 = w.tok0;
+        } else {
+            pos = p.q_pos0 + t;
+            P = visible_keys(pos, p.T, p.m, p.causal);
+            klo = tok0 = 0;
+        }
         n = (int)P;
         sc = reinterpret_cast<const uint32_t *>(p.scores + qrow * p.sstride);
         need = (uint32_t)(n < p.ksel ? n : p.ksel);
@@ -292,6 +304,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
     const uint32_t *sc = rv.sc;
     const uint32_t need = rv.need;
     const int mexp = p.expand ? p.m : 1;
+    const int64_t obase = p.expand ? rv.tok0 : rv.klo;  // output of key j: obase + j mexp + x
     int32_t *orow = p.idx + t * (int64_t)p.W;
     float *srow = p.sel_score ? p.sel_score + t * (int64_t)p.W : nullptr;
 
@@ -407,7 +420,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
                 const uint32_t kb = gt_before + (eq_before < cc.need_eq ? eq_before : cc.need_eq);
                 const int key = ckey[i0 + i];
                 for (int x = 0; x < mexp; ++x) {
-                    orow[(int)kb * mexp + x] = key * mexp + x;
+                    orow[(int)kb * mexp + x] = (int32_t)(obase + (int64_t)key * mexp + x);
                     if (srow) srow[(int)kb * mexp + x] = __uint_as_float(bits);
                 }
             }
@@ -443,7 +456,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
                     const uint32_t kb =
                         gt_before + (eq_before < cc.need_eq ? eq_before : cc.need_eq);
                     for (int x = 0; x < mexp; ++x) {
-                        orow[(int)kb * mexp + x] = (j0 + i) * mexp + x;
+                        orow[(int)kb * mexp + x] = (int32_t)(obase + (int64_t)(j0 + i) * mexp + x);
                         if (srow) srow[(int)kb * mexp + x] = __uint_as_float(sl.bits[i]);
                     }
                 }
@@ -456,9 +469,10 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
     }
 
     const int body = (int)cc.kept() * mexp;
-    const int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - P * p.m) : 0;
+    int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - P * p.m) : 0;
+    tl = tl < 0 ? 0 : (tl > p.W - body ? p.W - body : tl);  // packed documents: keys missing
     for (int s = body + (int)threadIdx.x; s < p.W; s += kDenseThreads) {
-        orow[s] = s < body + tl ? (int32_t)(P * p.m + (s - body)) : -1;
+        orow[s] = s < body + tl ? (int32_t)(rv.tok0 + P * p.m + (s - body)) : -1;
         if (srow) srow[s] = 0.f;
     }
     if (threadIdx.x == 0) p.valid_len[t] = body + tl;

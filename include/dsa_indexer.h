@@ -178,9 +178,12 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
  * arrays are read on the device only, so their preconditions are not
  * checked on the host; offsets are clamped to [0, T], and a row whose
  * document lacks complete pools gets a tail clipped to the row width.  With
- * IDX_EXPAND the caller keeps every output index below 2^31.  This call
- * always uses the streaming path; workspace from
- * indexer_workspace_bytes_varlen.
+ * IDX_EXPAND the caller keeps every output index below 2^31.  With at most
+ * few_query_rows rows (batched decode: one row per sequence) and a dense
+ * workspace of S x T scores within 4 GiB, the rows take the few-query path
+ * (each row's own key window scored by all CUs, then the per-row exact
+ * cut); otherwise the streaming path.  Both give identical results.
+ * Workspace from indexer_workspace_bytes_varlen.
  */
 int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, const float *w,
                               int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
@@ -190,9 +193,10 @@ int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, 
                               float *sel_score, void *workspace, size_t workspace_bytes,
                               void *stream);
 
-/* Device workspace bytes for indexer_score_topk_varlen (candidate buffers
- * for one query chunk of up to min(S, query_chunk) rows, each bounded by T
- * keys).  Host-only. */
+/* Device workspace bytes for indexer_score_topk_varlen: the few-query
+ * layout of indexer_config.few_query_rows for S rows over T keys when that
+ * path is taken, else candidate buffers for one query chunk of up to
+ * min(S, query_chunk) rows, each bounded by T keys.  Host-only. */
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
                                    int topk, size_t *bytes);
 

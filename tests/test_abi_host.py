@@ -116,6 +116,23 @@ def test_workspace_bytes_of_the_few_query_path():
     lib.indexer_destroy(h)
 
 
+def test_workspace_bytes_varlen_follow_the_path():
+    """Packed documents: at or below few_query_rows the few-query layout,
+    above it (or with a negative setting) the streaming buffers."""
+    n = ctypes.c_size_t()
+    lib, h = _handle()
+    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == _dense_bytes(8, 4096)
+    assert lib.indexer_workspace_bytes_varlen(h, 100, 4096, 64, 128, 4, 2048,
+                                              ctypes.byref(n)) == 0
+    assert n.value == 100 * (4096 + 64) * 8
+    lib.indexer_destroy(h)
+    lib, h = _handle(few=-1)
+    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 8 * (4096 + 64) * 8
+    lib.indexer_destroy(h)
+
+
 def test_workspace_bytes_with_screening():
     """IDX_SCREEN adds, on the streaming path with 33 <= H <= 64, the
     certificates of one launch's rows (644 bytes a row in four 256-byte

@@ -32,10 +32,10 @@ def _layout(rng, lens, m, pos0=None):
     return cu_q, cu_k, pos0, cu_tok
 
 
-def _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True):
+def _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True, few=0):
     import dsa_indexer_score_amd as dsai
     ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
-                      query_chunk=inp.query_chunk or 0, device=DEV)
+                      query_chunk=inp.query_chunk or 0, few_query_rows=few, device=DEV)
     t = lambda a, dt: torch.as_tensor(np.asarray(a), dtype=dt, device=DEV)
     out = ix.score_topk_varlen(
         inp.q, inp.w, inp.k, t(cu_q, torch.int32), t(cu_k, torch.int32), m=inp.m, topk=inp.topk,
@@ -111,3 +111,86 @@ def test_varlen_float_batch_per_document(name):
         rep = check.compare(sub, np.arange(r1 - r0), loc.astype(np.int32), vl[r0:r1],
                             sc[r0:r1])
         assert rep["ok"], (i, rep["failures"][:3])
+
+
+def _decode_batch(rng, lens, m, dtype, H=8, d=64, pad=3):
+    """One query row per document, at the last position of each document's
+    context (batched decode), plus padding rows."""
+    lens = np.asarray(lens, np.int64)
+    nkeys = lens // m                                     # complete pools only
+    cu_k = np.concatenate([[0], np.cumsum(nkeys)]).astype(np.int32)
+    ndoc = len(lens)
+    cu_q = np.arange(ndoc + 1, dtype=np.int32)
+    pos0 = lens - 1                                       # the row is the last token
+    cu_tok = np.concatenate([[0], np.cumsum(lens)])[:-1].astype(np.int32)
+    S, T = ndoc + pad, int(cu_k[-1])
+    g = torch.Generator().manual_seed(int(rng.integers(1 << 30)))
+    if dtype == torch.float32:
+        q = torch.randint(-3, 4, (S, H, d), generator=g).float()
+        k = torch.randint(-3, 4, (T, d), generator=g).float()
+        w = torch.tensor(rng.choice([-1.0, -0.5, 0.5, 1.0], size=(S, H)), dtype=torch.float32)
+        qs = ks = None
+    else:
+        q = torch.randn(S, H, d, generator=g) / d ** 0.5
+        k = torch.randn(T, d, generator=g) / d ** 0.5
+        w = torch.randn(S, H, generator=g)
+        qs = ks = None
+        if dtype == torch.float8_e4m3fn:
+            qs = q.abs().amax(-1) / 448 + 1e-12
+            ks = k.abs().amax(-1) / 448 + 1e-12
+            q, k = q / qs[..., None], k / ks[:, None]
+        q, k = q.to(dtype), k.to(dtype)
+    return q, k, w, qs, ks, cu_q, cu_k, pos0, cu_tok
+
+
+@pytest.mark.parametrize("m,expand", [(4, True), (4, False), (1, False)])
+def test_batched_decode_few_query_path_is_exact(m, expand):
+    """One row per document at the end of its context (lengths around the
+    pool edges and long ones), padding rows: the few-query path equals the
+    streaming path bit for bit and the oracle exactly (integer inputs)."""
+    rng = np.random.default_rng(40 + m)
+    lens = [3, 4, 5, 7, 8, 9, 64, 65, 900, 5000, 20000, 37]
+    q, k, w, qs, ks, cu_q, cu_k, pos0, cu_tok = _decode_batch(rng, lens, m, torch.float32)
+    topk = 48 if expand else 12
+    inp = gen.custom(q=q, k=k, w=w, m=m, topk=topk, expand=expand, tail=expand).to(DEV)
+    dense = _run(inp, cu_q, cu_k, pos0, cu_tok, few=64)
+    stream = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
+    for a, b in zip(dense, stream):
+        assert torch.equal(a, b)
+    want = orc.select_rows_varlen(inp, cu_q, cu_k, pos0=pos0, cu_tok=cu_tok)
+    assert np.array_equal(dense[1].cpu().numpy(), want["valid_len"])
+    assert np.array_equal(dense[0].cpu().numpy(), want["idx"])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_batched_decode_float_matches_streaming(dtype):
+    rng = np.random.default_rng(7)
+    lens = [70000, 4096, 123457, 9, 30000, 65536]
+    q, k, w, qs, ks, cu_q, cu_k, pos0, cu_tok = _decode_batch(rng, lens, 4, dtype, H=64, d=128)
+    inp = gen.custom(q=q, k=k, w=w, m=4, topk=2048, expand=False, tail=False, q_scale=qs,
+                     k_scale=ks).to(DEV)
+    dense = _run(inp, cu_q, cu_k, pos0, cu_tok, few=64)
+    stream = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
+    for a, b in zip(dense, stream):
+        assert torch.equal(a, b)
+    log(f"  {dtype}: {len(lens)} decode rows over {int(cu_k[-1])} keys, valid_len "
+        f"{dense[1].tolist()}")
+
+
+def test_few_query_rows_of_several_documents():
+    """Few rows, several per document, later-chunk positions and padding:
+    few-query and streaming paths agree bit for bit."""
+    rng = np.random.default_rng(8)
+    lens = [5, 1, 20, 3]
+    cu_q, cu_k, pos0, cu_tok = _layout(rng, lens, 4, pos0=[0, 33, 100, 7])
+    S, T, H, d = int(cu_q[-1]) + 2, int(cu_k[-1]), 4, 32
+    q = torch.from_numpy(rng.integers(-3, 4, size=(S, H, d)).astype(np.float32))
+    k = torch.from_numpy(rng.integers(-3, 4, size=(T, d)).astype(np.float32))
+    w = torch.from_numpy(rng.choice([-1.0, 1.0], size=(S, H)).astype(np.float32))
+    inp = gen.custom(q=q, k=k, w=w, m=4, topk=16, expand=True, tail=True).to(DEV)
+    dense = _run(inp, cu_q, cu_k, pos0, cu_tok, few=64)
+    stream = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
+    for a, b in zip(dense, stream):
+        assert torch.equal(a, b)
+    want = orc.select_rows_varlen(inp, cu_q, cu_k, pos0=pos0, cu_tok=cu_tok)
+    assert np.array_equal(dense[0].cpu().numpy(), want["idx"])
