@@ -99,7 +99,17 @@ struct DenseLayout {
 bool use_dense(const indexer_config &cfg, int64_t S, int64_t T)
 {
     const int64_t lim = cfg.few_query_rows == 0 ? kFewRowsDefault : cfg.few_query_rows;
-    return lim > 0 && S <= lim && S <= 65535 && DenseLayout(S, T).bytes <= kDenseMaxBytes;
+    return lim > 0 && S <= lim && S <= 65535 && DenseLayout(1, T).bytes <= kDenseMaxBytes;
+}
+
+// Rows per few-query pass: all S while the workspace stays within 4 GiB,
+// else as many as fit (the rows are then taken in several passes).
+int64_t dense_rows(int64_t S, int64_t T)
+{
+    const int64_t per_row = DenseLayout(1, T).bytes;
+    int64_t r = std::max<int64_t>(1, std::min<int64_t>(S, kDenseMaxBytes / per_row));
+    while (r > 1 && DenseLayout(r, T).bytes > kDenseMaxBytes) --r;
+    return r;
 }
 
 // Screening (IDX_SCREEN) on the streaming path: needs two head blocks.
@@ -130,7 +140,7 @@ struct StreamLayout {
 int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int H, int64_t ksel,
                        int64_t pmax)
 {
-    if (use_dense(cfg, S, T)) return DenseLayout(S, T).bytes;
+    if (use_dense(cfg, S, T)) return DenseLayout(dense_rows(S, T), T).bytes;
     return StreamLayout(rows_per_launch(cfg, S), capacity(ksel, pmax), T, use_screen(cfg, H)).bytes;
 }
 
@@ -296,8 +306,10 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     if (dense) {
         // Few-query path: all CUs score the rows' key ranges into the dense
         // workspace, then the selection runs per row (estimate), per
-        // (row, key segment) (candidate filter) and per row (exact cut).
-        const DenseLayout L(S, T);
+        // (row, key segment) (candidate filter) and per row (exact cut); in
+        // passes of as many rows as the workspace holds.
+        const int64_t R = dense_rows(S, T);
+        const DenseLayout L(R, T);
         char *base = static_cast<char *>(workspace);
         p.ws = nullptr;
         p.scores = reinterpret_cast<float *>(base);
@@ -306,25 +318,30 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.seg_cnt = reinterpret_cast<int32_t *>(base + L.cnt);
         p.seg_buf = reinterpret_cast<uint2 *>(base + L.key);
         p.nseg = (int)L.nseg;
-        p.row0 = 0;
-        p.nrows = S;
-        const int64_t groups = (S + dsai::kQueriesPerBlock - 1) / dsai::kQueriesPerBlock;
-        const int64_t tiles = (std::max<int64_t>(pmax, 1) + dsai::kKeysPerTile - 1) /
-                              dsai::kKeysPerTile;
-        const int64_t want = std::max<int64_t>(1, (kFillBlocks + groups - 1) / groups);
-        const int64_t tiles_per = (tiles + std::min(want, tiles) - 1) / std::min(want, tiles);
-        p.split_keys = tiles_per * dsai::kKeysPerTile;
-        p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
-        bool supported = true;
-        // packed documents: every row its own key window, one row per slab
-        hipError_t e = S <= kRowsKernelMax || docs.on
-                           ? dsai::launch_score_rows(cfg.dtype, nb, d, docs.on, p, st, &supported)
-                           : dsai::launch_score_select(cfg.dtype, nb, d, true, false, false, p,
-                                                       st, &supported);
-        if (!supported) return IDX_EUNSUPPORTED;
-        if (e != hipSuccess) return fail_hip(e);
-        e = dsai::launch_select_dense(p, st);
-        if (e != hipSuccess) return fail_hip(e);
+        for (int64_t r0 = 0; r0 < S; r0 += R) {
+            p.row0 = r0;
+            p.nrows = std::min(R, S - r0);
+            const int64_t groups = (p.nrows + dsai::kQueriesPerBlock - 1) / dsai::kQueriesPerBlock;
+            const int64_t pm = causal && !docs.on
+                                   ? std::min<int64_t>(T, (q_pos0 + r0 + p.nrows) / m) : T;
+            const int64_t tiles = (std::max<int64_t>(pm, 1) + dsai::kKeysPerTile - 1) /
+                                  dsai::kKeysPerTile;
+            const int64_t want = std::max<int64_t>(1, (kFillBlocks + groups - 1) / groups);
+            const int64_t tiles_per = (tiles + std::min(want, tiles) - 1) / std::min(want, tiles);
+            p.split_keys = tiles_per * dsai::kKeysPerTile;
+            p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
+            bool supported = true;
+            // packed documents: every row its own key window, one row per slab
+            hipError_t e =
+                p.nrows <= kRowsKernelMax || docs.on
+                    ? dsai::launch_score_rows(cfg.dtype, nb, d, docs.on, p, st, &supported)
+                    : dsai::launch_score_select(cfg.dtype, nb, d, true, false, false, p, st,
+                                                &supported);
+            if (!supported) return IDX_EUNSUPPORTED;
+            if (e != hipSuccess) return fail_hip(e);
+            e = dsai::launch_select_dense(p, st);
+            if (e != hipSuccess) return fail_hip(e);
+        }
         return IDX_OK;
     }
     if (screen) {
@@ -381,9 +398,9 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
-    *bytes = use_dense(h->cfg, S, T)
-                 ? (size_t)DenseLayout(S, T).bytes
-                 : (size_t)(rows_per_launch(h->cfg, S) * capacity(ksel, T) * (int64_t)sizeof(uint2));
+    const int64_t stream_bytes = rows_per_launch(h->cfg, S) * capacity(ksel, T) * 8;
+    *bytes = (size_t)(use_dense(h->cfg, S, T) ? DenseLayout(dense_rows(S, T), T).bytes
+                                               : stream_bytes);
     return IDX_OK;
 }
 

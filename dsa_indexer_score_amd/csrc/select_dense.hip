@@ -348,7 +348,8 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
             for (int s0 = 0; s0 < nseg_row; s0 += kDenseThreads) {
                 const int sg = s0 + (int)threadIdx.x;
                 uint32_t off = off_first, tot = tot_first;
-                if (s0 > 0) off = block_excl_scan(sg < nseg_row ? (uint32_t)cnts[sg] : 0u, red, tot);
+                if (s0 > 0)
+                    off = block_excl_scan(sg < nseg_row ? (uint32_t)cnts[sg] : 0u, red, tot);
                 soff[threadIdx.x] = done + off;
                 __syncthreads();
                 // owner segment of each list slot of this round (LDS only) ...
@@ -486,8 +487,8 @@ hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream)
     hipLaunchKernelGGL(estimate_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)p.nseg, (unsigned)p.nrows), dim3(kFilterThreads),
-                       0, stream, p);
+    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)p.nseg, (unsigned)p.nrows),
+                       dim3(kFilterThreads), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(finish_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream, p);

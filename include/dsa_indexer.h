@@ -79,8 +79,10 @@ typedef struct {
      * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
      * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
      * G = ceil(max(T, 1) / 4096)) and the candidates as (score, key) pairs
-     * (S * G * 4096 * 8), about 12 bytes per (row, key); it is used only
-     * while it stays within 4 GiB. */
+     * (S * G * 4096 * 8), about 12 bytes per (row, key).  It is capped at
+     * 4 GiB: when the S rows need more, the rows are taken in passes of as
+     * many rows R as fit and the workspace is sized for R rows (the path is
+     * used while one row fits). */
     int64_t few_query_rows;
 } indexer_config;
 

@@ -93,8 +93,9 @@ def _dense_bytes(S, T):
 
 def test_workspace_bytes_of_the_few_query_path():
     """At or below few_query_rows (default 64) the workspace holds the rows'
-    dense scores and the selection's candidate scratch while that stays
-    within 4 GiB; a negative setting always streams."""
+    dense scores and the selection's candidate scratch, for as many rows as
+    fit in 4 GiB (the rest are taken in further passes); a negative setting
+    always streams."""
     n = ctypes.c_size_t()
     lib, h = _handle(chunk=16384)
     assert lib.indexer_workspace_bytes(h, 64, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
@@ -104,7 +105,7 @@ def test_workspace_bytes_of_the_few_query_path():
     assert lib.indexer_workspace_bytes(h, 65, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 65 * 20736 * 8            # above the default: streaming buffers
     assert lib.indexer_workspace_bytes(h, 64, 2 ** 25, 64, 128, 1, 2048, ctypes.byref(n)) == 0
-    assert n.value == 64 * 20736 * 8            # 8 GiB of dense scores: streams instead
+    assert n.value == _dense_bytes(10, 2 ** 25)  # 25 GiB for all rows: passes of 10 rows
     lib.indexer_destroy(h)
     lib, h = _handle(few=-1)
     assert lib.indexer_workspace_bytes(h, 1, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0

@@ -163,3 +163,28 @@ def test_few_query_more_than_1024_candidate_segments():
     dense, stream = _both_paths(inp)
     _assert_identical(dense, stream)
     assert (dense[1] == 300).all()
+
+
+def test_few_query_rows_in_passes():
+    """Eight decode rows over 48M keys need more than the 4 GiB the dense
+    workspace may take, so the rows go in passes of as many as fit (7 + 1);
+    each row equals the same row scored and cut on its own."""
+    import dsa_indexer_score_amd as dsai
+    g = torch.Generator().manual_seed(21)
+    S, T, H, d = 8, 48_000_000, 4, 32
+    base = (torch.randn(1 << 16, d, generator=g) / d ** 0.5).bfloat16()
+    k = base[torch.randint(0, 1 << 16, (T,), generator=g)].to(DEV)
+    q = (torch.randn(S, H, d, generator=g) / d ** 0.5).bfloat16().to(DEV)
+    w = torch.randn(S, H, generator=g).to(DEV)
+    kw = dict(m=1, topk=700, causal=True, few_query_rows=64, with_scores=True)
+    h = dsai.Indexer(torch.bfloat16, few_query_rows=64, device=DEV)
+    assert 6 * 12 * T < h.workspace_bytes(S, T, H, d, 1, 700) <= 1 << 32   # 7 rows a pass
+    idx, vl, sc = dsai.score_topk(q, w, k, q_pos0=T - S, **kw)
+    torch.cuda.synchronize()
+    for t in range(S):
+        i1, v1, s1 = dsai.score_topk(q[t:t + 1].contiguous(), w[t:t + 1].contiguous(), k,
+                                     q_pos0=T - S + t, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(i1[0], idx[t]) and torch.equal(v1[0], vl[t]), t
+        assert torch.equal(s1[0], sc[t]), t
+    assert (vl == 700).all()

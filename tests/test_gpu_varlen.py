@@ -194,3 +194,22 @@ def test_few_query_rows_of_several_documents():
         assert torch.equal(a, b)
     want = orc.select_rows_varlen(inp, cu_q, cu_k, pos0=pos0, cu_tok=cu_tok)
     assert np.array_equal(dense[0].cpu().numpy(), want["idx"])
+
+
+def test_batched_decode_in_passes():
+    """43 decode rows over 19.4M packed keys: the dense workspace for all
+    rows would pass 4 GiB, so the rows go in passes (18 + 18 + 7); the
+    result equals the streaming path bit for bit."""
+    rng = np.random.default_rng(12)
+    lens = rng.integers(1_000_000, 3_000_000, size=40)     # 19.4M complete pools
+    q, k, w, qs, ks, cu_q, cu_k, pos0, cu_tok = _decode_batch(rng, lens, 4, torch.bfloat16,
+                                                              H=4, d=32)
+    inp = gen.custom(q=q, k=k, w=w, m=4, topk=512, expand=True, tail=True).to(DEV)
+    import dsa_indexer_score_amd as dsai
+    ix = dsai.Indexer(torch.bfloat16, expand=True, tail=True, few_query_rows=64, device=DEV)
+    assert 17 * 12 * inp.T < ix.workspace_bytes_varlen(inp.S, inp.T, 4, 32, 4, 512) <= 1 << 32
+    dense = _run(inp, cu_q, cu_k, pos0, cu_tok, few=64)
+    stream = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
+    for a, b in zip(dense, stream):
+        assert torch.equal(a, b)
+    log(f"  {inp.S} rows over {inp.T} keys, valid_len {dense[1][:4].tolist()}...")
