@@ -308,8 +308,11 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         // workspace, then the selection runs per row (estimate), per
         // (row, key segment) (candidate filter) and per row (exact cut); in
         // passes of as many rows as the workspace holds.
+        // equal passes (each at most the R rows the workspace holds)
         const int64_t R = dense_rows(S, T);
         const DenseLayout L(R, T);
+        const int64_t npass = (S + R - 1) / R;
+        const int64_t Rp = npass > 0 ? (S + npass - 1) / npass : R;
         char *base = static_cast<char *>(workspace);
         p.ws = nullptr;
         p.scores = reinterpret_cast<float *>(base);
@@ -318,9 +321,9 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.seg_cnt = reinterpret_cast<int32_t *>(base + L.cnt);
         p.seg_buf = reinterpret_cast<uint2 *>(base + L.key);
         p.nseg = (int)L.nseg;
-        for (int64_t r0 = 0; r0 < S; r0 += R) {
+        for (int64_t r0 = 0; r0 < S; r0 += Rp) {
             p.row0 = r0;
-            p.nrows = std::min(R, S - r0);
+            p.nrows = std::min(Rp, S - r0);
             const int64_t groups = (p.nrows + dsai::kQueriesPerBlock - 1) / dsai::kQueriesPerBlock;
             const int64_t pm = causal && !docs.on
                                    ? std::min<int64_t>(T, (q_pos0 + r0 + p.nrows) / m) : T;

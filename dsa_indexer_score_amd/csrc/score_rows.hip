@@ -17,7 +17,8 @@
 // the rows' q operands in registers and owns a run of 64-key groups of one
 // row slab; it loads its keys' B operands straight from global memory (each
 // lane the contiguous half of one key row that its MFMA slots cover, so 32
-// keys arrive as whole rows), one group ahead, with no LDS and no barrier.
+// keys arrive as whole rows), one or two groups ahead, with no LDS and no
+// barrier.
 // All CUs stream disjoint slices of the key set, so one row is bound by
 // reading the keys from HBM.  Slabs of the same key range sit in blocks a
 // multiple of 8 apart, so they land on the same XCD and share its L2.
@@ -30,7 +31,10 @@ namespace {
 
 constexpr int kRowsWaves = 4;
 constexpr int kRowsThreads = kRowsWaves * 64;
-constexpr int kTargetWaves = 1024;  // about one wave per SIMD; each streams several groups
+// waves per launch, each streaming several groups: about one per SIMD, two
+// for packed documents (many rows, each a slab of its own)
+constexpr int kTargetWaves = 1024;
+constexpr int kTargetWavesDocs = 2048;
 
 template <int DT, int NB, int D, int SQ, bool VARLEN>
 __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectParams p)
@@ -104,8 +108,11 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     // A key at or past T is read at key T - 1 instead: column j of the
     // product depends on key j alone, and such keys' scores are never stored.
     const char *kbytes = static_cast<const char *>(p.k);
-    uint4 raw[2][RAW], nraw[2][RAW];
-    float ksc = 0.f, nksc = 0.f;
+    // groups loaded ahead of use: two where the register budget allows
+    // (fp8 at d = 128: 16 KB of keys per wave in flight), else one
+    constexpr int AHEAD = RAW <= 4 ? 2 : 1;
+    uint4 raw[AHEAD + 1][2][RAW];
+    float ksc[AHEAD + 1] = {};
     auto load_group = [&](int64_t g, uint4 (&dst)[2][RAW], float &sc) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -118,14 +125,16 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
         }
     };
 
-    load_group(g0, raw, ksc);
+#pragma unroll
+    for (int a = 0; a < AHEAD; ++a)
+        if (g0 + a < g1) load_group(g0 + a, raw[a], ksc[a]);
     for (int64_t g = g0; g < g1; ++g) {
-        if (g + 1 < g1) load_group(g + 1, nraw, nksc);
+        if (g + AHEAD < g1) load_group(g + AHEAD, raw[AHEAD], ksc[AHEAD]);
         float part[SQ][2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             A bfr[KS];
-            O::from_raw(raw[c], bfr);
+            O::from_raw(raw[0][c], bfr);
 #pragma unroll
             for (int i = 0; i < SQ; ++i) {
                 float e = 0.f;
@@ -151,15 +160,18 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
                                                              __float_as_uint(part[i][1]), false,
                                                              false);
             float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (DT == 2) s *= ksc;
+            if (DT == 2) s *= ksc[0];
             if (key < Pq[i]) p.scores[(r0 + i) * p.sstride + key] = s;
         }
         if (g + 1 < g1) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int a = 0; a < AHEAD; ++a) {
 #pragma unroll
-                for (int x = 0; x < RAW; ++x) raw[c][x] = nraw[c][x];
-            ksc = nksc;
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int x = 0; x < RAW; ++x) raw[a][c][x] = raw[a + 1][c][x];
+                ksc[a] = ksc[a + 1];
+            }
         }
     }
 }
@@ -174,7 +186,8 @@ hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
     const int64_t nslab = (p.nrows + SQ - 1) / SQ;
     if (ngroups <= 0 || nslab <= 0) return hipSuccess;
     // about kTargetWaves waves in all, at most one per group of a slab
-    int64_t waves = (kTargetWaves + nslab - 1) / nslab;
+    const int64_t target = VARLEN ? kTargetWavesDocs : kTargetWaves;
+    int64_t waves = (target + nslab - 1) / nslab;
     waves = waves < ngroups ? waves : ngroups;
     const int64_t blocks = ((waves + kRowsWaves - 1) / kRowsWaves + 7) / 8 * 8;
     hipLaunchKernelGGL((score_rows_kernel<DT, NB, D, SQ, VARLEN>),

@@ -43,6 +43,7 @@ constexpr int kPer = 16;                        // consecutive keys per thread p
 constexpr int kChunk = kDenseThreads * kPer;    // keys per chunk
 constexpr int kFilterThreads = 256;             // candidate filter block
 constexpr int kSeg = kFilterThreads * kPer;     // keys per filter segment
+constexpr int64_t kFilterBlocks = 4096;         // filter blocks per launch (about)
 
 // The KP consecutive scores of this thread's slice of chunk `base` (raw
 // bits); all loads are issued before any is used.
@@ -253,35 +254,38 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
     if (threadIdx.x == 0) p.est[blockIdx.x] = est;
 }
 
-// Candidates of one segment (kSeg keys) of one row: every visible key
-// whose code is >= the row's estimate, as (score bits, key) in key order,
-// into the segment's slot; the segment count is always written.
+// Candidates of one row, segment by segment (kSeg keys each): every visible
+// key whose code is >= the row's estimate, as (score bits, key) in key
+// order, into the segment's slot, and the segment's count.  A block takes
+// every gridDim.x-th segment of its row that holds visible keys, so the
+// grid does not grow with the rows' stride (packed documents: a row's
+// window is often a small part of all keys).  Without an estimate the cut
+// reads the full row and no count is needed.
 __global__ void __launch_bounds__(kFilterThreads) filter_kernel(ScoreSelectParams p)
 {
     __shared__ uint32_t red[kFilterThreads / 64];
-    const int seg = blockIdx.x;
     const RowView rv(p, blockIdx.y);
     const uint32_t est = p.est[blockIdx.y];
-    const int base = seg * kSeg;
-    const int64_t slot = (int64_t)blockIdx.y * p.nseg + seg;
-    if (est == kNoList || base >= rv.n) {
-        if (threadIdx.x == 0) p.seg_cnt[slot] = 0;
-        return;
+    if (est == kNoList) return;
+    for (int seg = blockIdx.x; (int64_t)seg * kSeg < rv.n; seg += gridDim.x) {
+        const int base = seg * kSeg;
+        const int64_t slot = (int64_t)blockIdx.y * p.nseg + seg;
+        Slice sl;
+        sl.load(rv.sc, base, rv.n);
+        const int j0 = base + (int)threadIdx.x * kPer;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            cnt += (j0 + i < rv.n && ord_code(sl.bits[i]) >= est) ? 1u : 0u;
+        uint32_t tot;
+        uint32_t o = block_excl_scan<kFilterThreads / 64>(cnt, red, tot);  // ends in a barrier
+        uint2 *dst = p.seg_buf + slot * (int64_t)kSeg;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (j0 + i < rv.n && ord_code(sl.bits[i]) >= est)
+                dst[o++] = make_uint2(sl.bits[i], (uint32_t)(j0 + i));
+        if (threadIdx.x == 0) p.seg_cnt[slot] = (int32_t)tot;
     }
-    Slice sl;
-    sl.load(rv.sc, base, rv.n);
-    const int j0 = base + (int)threadIdx.x * kPer;
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) cnt += (j0 + i < rv.n && ord_code(sl.bits[i]) >= est) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t o = block_excl_scan<kFilterThreads / 64>(cnt, red, tot);
-    uint2 *dst = p.seg_buf + slot * (int64_t)kSeg;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if (j0 + i < rv.n && ord_code(sl.bits[i]) >= est)
-            dst[o++] = make_uint2(sl.bits[i], (uint32_t)(j0 + i));
-    if (threadIdx.x == 0) p.seg_cnt[slot] = (int32_t)tot;
 }
 
 // Exact selection of one row and its canonical output row: from the
@@ -487,7 +491,10 @@ hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream)
     hipLaunchKernelGGL(estimate_kernel, dim3((unsigned)p.nrows), dim3(kDenseThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)p.nseg, (unsigned)p.nrows),
+    // about 16 filter blocks per CU, at most one per segment of the stride
+    const int64_t per_row = (kFilterBlocks + p.nrows - 1) / p.nrows;
+    const int64_t fx = per_row < p.nseg ? per_row : p.nseg;
+    hipLaunchKernelGGL(filter_kernel, dim3((unsigned)fx, (unsigned)p.nrows),
                        dim3(kFilterThreads), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

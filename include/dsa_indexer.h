@@ -80,9 +80,9 @@ typedef struct {
      * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
      * G = ceil(max(T, 1) / 4096)) and the candidates as (score, key) pairs
      * (S * G * 4096 * 8), about 12 bytes per (row, key).  It is capped at
-     * 4 GiB: when the S rows need more, the rows are taken in passes of as
-     * many rows R as fit and the workspace is sized for R rows (the path is
-     * used while one row fits). */
+     * 4 GiB: when the S rows need more, the workspace is sized for the R
+     * rows that fit and the rows are taken in ceil(S / R) equal passes (the
+     * path is used while one row fits). */
     int64_t few_query_rows;
 } indexer_config;
 

@@ -167,8 +167,8 @@ def test_few_query_more_than_1024_candidate_segments():
 
 def test_few_query_rows_in_passes():
     """Eight decode rows over 48M keys need more than the 4 GiB the dense
-    workspace may take, so the rows go in passes of as many as fit (7 + 1);
-    each row equals the same row scored and cut on its own."""
+    workspace may take, so the rows go in two equal passes (4 + 4; 7 would
+    fit); each row equals the same row scored and cut on its own."""
     import dsa_indexer_score_amd as dsai
     g = torch.Generator().manual_seed(21)
     S, T, H, d = 8, 48_000_000, 4, 32

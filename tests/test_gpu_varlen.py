@@ -198,8 +198,8 @@ def test_few_query_rows_of_several_documents():
 
 def test_batched_decode_in_passes():
     """43 decode rows over 19.4M packed keys: the dense workspace for all
-    rows would pass 4 GiB, so the rows go in passes (18 + 18 + 7); the
-    result equals the streaming path bit for bit."""
+    rows would pass 4 GiB, so the rows go in three equal passes (15 + 15 +
+    13; 18 would fit); the result equals the streaming path bit for bit."""
     rng = np.random.default_rng(12)
     lens = rng.integers(1_000_000, 3_000_000, size=40)     # 19.4M complete pools
     q, k, w, qs, ks, cu_q, cu_k, pos0, cu_tok = _decode_batch(rng, lens, 4, torch.bfloat16,
