@@ -222,9 +222,12 @@ def main():
                     pairs=B * (min(T_doc, T_doc * inp.m // inp.m) if inp.causal else T_doc))
     idx = torch.empty((inp.S, W), dtype=torch.int32, device=dev)
     vl = torch.empty((inp.S,), dtype=torch.int32, device=dev)
-    wsb = ix.workspace_bytes_varlen if docs else ix.workspace_bytes
-    ws = torch.empty((wsb(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk),),
-                     dtype=torch.uint8, device=dev)
+    # packed documents: the longest document's keys bound the dense rows
+    max_doc_keys = int(max(docs["nkeys"])) if docs else 0
+    nbytes = (ix.workspace_bytes_varlen(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk,
+                                        max_doc_keys) if docs else
+              ix.workspace_bytes(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk))
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def score():
@@ -232,7 +235,8 @@ def main():
             ix.score_topk_varlen(inp.q, inp.w, inp.k, docs["cu_q"], docs["cu_k"], m=inp.m,
                                  topk=inp.topk, causal=inp.causal, pos0=docs.get("pos0"),
                                  cu_tok=docs["cu_tok"], q_scale=inp.q_scale,
-                                 k_scale=inp.k_scale, workspace=ws, out=(idx, vl, None))
+                                 k_scale=inp.k_scale, max_doc_keys=max_doc_keys,
+                                 workspace=ws, out=(idx, vl, None))
         else:
             ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
                           q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,

@@ -138,21 +138,24 @@ class Indexer:
         return (idx, valid_len, sel) if with_scores else (idx, valid_len)
 
 
-    def workspace_bytes_varlen(self, S: int, T: int, H: int, d: int, m: int, topk: int) -> int:
+    def workspace_bytes_varlen(self, S: int, T: int, H: int, d: int, m: int, topk: int,
+                               max_doc_keys: int = 0) -> int:
         n = ctypes.c_size_t(0)
         _lib.check(self._lib.indexer_workspace_bytes_varlen(self._h, S, T, H, d, m, topk,
-                                                            ctypes.byref(n)),
+                                                            max_doc_keys, ctypes.byref(n)),
                    "indexer_workspace_bytes_varlen")
         return n.value
 
     def score_topk_varlen(self, q, w, k, cu_q, cu_k, *, m: int = 1, topk: int,
                           causal: bool = True, pos0=None, cu_tok=None, q_scale=None,
-                          k_scale=None, with_scores: bool = False,
+                          k_scale=None, max_doc_keys: int = 0, with_scores: bool = False,
                           workspace: Optional[torch.Tensor] = None, out=None):
         """Packed documents: rows [cu_q[i], cu_q[i+1]) see keys [cu_k[i], cu_k[i+1])
         (int32 device tensors of ndoc + 1 entries); pos0 (int64 [ndoc]) is each
         document's first-row position, cu_tok (int32 [ndoc], expand mode) its
-        token offset.  Returns (idx, valid_len[, sel_score])."""
+        token offset; max_doc_keys (host int, 0 = unknown) bounds every
+        document's key count and sizes the few-query path's dense rows.
+        Returns (idx, valid_len[, sel_score])."""
         if q.dim() != 3 or k.dim() != 2:
             raise ValueError("q must be [S, H, d] and k [T, d]")
         S, H, d = q.shape
@@ -187,13 +190,13 @@ class Indexer:
                 if with_scores else None
         else:
             idx, valid_len, sel = out
-        nbytes = self.workspace_bytes_varlen(S, T, H, d, m, topk)
+        nbytes = self.workspace_bytes_varlen(S, T, H, d, m, topk, max_doc_keys)
         if workspace is None:
             workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
         rc = self._lib.indexer_score_topk_varlen(
             self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
             d, m, topk, int(bool(causal)), _ptr(cu_q), _ptr(cu_k), _ptr(pos0), _ptr(cu_tok), ndoc,
-            _ptr(idx), _ptr(valid_len), _ptr(sel), _ptr(workspace),
+            max_doc_keys, _ptr(idx), _ptr(valid_len), _ptr(sel), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(self.device))
         _lib.check(rc, "indexer_score_topk_varlen")
         return (idx, valid_len, sel) if with_scores else (idx, valid_len)

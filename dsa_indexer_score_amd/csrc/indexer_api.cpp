@@ -221,7 +221,15 @@ struct Docs {  // packed-document layout (varlen); on = false: one document
     const int32_t *cu_q = nullptr, *cu_k = nullptr, *cu_tok = nullptr;
     const int64_t *pos0 = nullptr;
     int ndoc = 0;
+    int64_t row_keys = 0;  // keys per dense row of the few-query path
 };
+
+// Keys per dense row for packed documents: the caller's bound on a
+// document's keys (0: unknown), at most T.
+int64_t doc_row_keys(int64_t max_doc_keys, int64_t T)
+{
+    return max_doc_keys > 0 && max_doc_keys < T ? max_doc_keys : T;
+}
 
 int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const float *w,
                     int64_t w_stride_s, const void *k, const float *k_scale, int64_t S, int64_t T,
@@ -263,10 +271,13 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     const int64_t pmax = causal && !docs.on ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
     const int64_t rows = rows_per_launch(cfg, S);
-    const bool dense = use_dense(cfg, S, T);
+    const int64_t Tk = docs.on ? docs.row_keys : T;  // scores per dense row
+    const bool dense = use_dense(cfg, S, Tk);
     const bool screen = !docs.on && !dense && use_screen(cfg, H);
-    const size_t need = docs.on && !dense ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
-                                          : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
+    const size_t need =
+        dense     ? (size_t)DenseLayout(dense_rows(S, Tk), Tk).bytes
+        : docs.on ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
+                  : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
 
     DeviceGuard guard(h->device);
@@ -309,8 +320,8 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         // (row, key segment) (candidate filter) and per row (exact cut); in
         // passes of as many rows as the workspace holds.
         // equal passes (each at most the R rows the workspace holds)
-        const int64_t R = dense_rows(S, T);
-        const DenseLayout L(R, T);
+        const int64_t R = dense_rows(S, Tk);
+        const DenseLayout L(R, Tk);
         const int64_t npass = (S + R - 1) / R;
         const int64_t Rp = npass > 0 ? (S + npass - 1) / npass : R;
         char *base = static_cast<char *>(workspace);
@@ -395,15 +406,18 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
 }
 
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
-                                   int topk, size_t *bytes)
+                                   int topk, int64_t max_doc_keys, size_t *bytes)
 {
-    if (!h || !bytes || S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1) return IDX_EINVAL;
+    if (!h || !bytes || S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1 ||
+        max_doc_keys < 0)
+        return IDX_EINVAL;
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
     const int64_t stream_bytes = rows_per_launch(h->cfg, S) * capacity(ksel, T) * 8;
-    *bytes = (size_t)(use_dense(h->cfg, S, T) ? DenseLayout(dense_rows(S, T), T).bytes
-                                               : stream_bytes);
+    const int64_t Tk = doc_row_keys(max_doc_keys, T);
+    *bytes = (size_t)(use_dense(h->cfg, S, Tk) ? DenseLayout(dense_rows(S, Tk), Tk).bytes
+                                                : stream_bytes);
     return IDX_OK;
 }
 
@@ -411,10 +425,11 @@ int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, 
                               int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
                               int64_t T, int H, int d, int m, int topk, int causal,
                               const int32_t *cu_q, const int32_t *cu_k, const int64_t *pos0,
-                              const int32_t *cu_tok, int ndoc, int32_t *idx, int32_t *valid_len,
-                              float *sel_score, void *workspace, size_t workspace_bytes,
-                              void *stream)
+                              const int32_t *cu_tok, int ndoc, int64_t max_doc_keys,
+                              int32_t *idx, int32_t *valid_len, float *sel_score,
+                              void *workspace, size_t workspace_bytes, void *stream)
 {
+    if (max_doc_keys < 0) return IDX_EINVAL;
     Docs docs;
     docs.on = true;
     docs.cu_q = cu_q;
@@ -422,6 +437,7 @@ int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, 
     docs.pos0 = pos0;
     docs.cu_tok = cu_tok;
     docs.ndoc = ndoc;
+    docs.row_keys = doc_row_keys(max_doc_keys, T);
     return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
                            0, docs, idx, valid_len, sel_score, workspace, workspace_bytes, stream);
 }

@@ -56,8 +56,10 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     for (int i = 0; i < SQ; ++i) {
         const int64_t r = r0 + i;
         if constexpr (VARLEN) {
+            // a window longer than the dense row (the caller's bound on a
+            // document's keys) is cut to it: every store stays in the row
             const DocWindow dw = r < p.nrows ? doc_window(p, p.row0 + r) : DocWindow{};
-            Pq[i] = dw.P;
+            Pq[i] = dw.P < p.sstride ? dw.P : p.sstride;
             klo = dw.klo;
         } else {
             Pq[i] = r < p.nrows ? visible_keys(p.q_pos0 + p.row0 + r, p.T, p.m, p.causal) : 0;
@@ -179,9 +181,9 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
 template <int DT, int NB, int D, int SQ, bool VARLEN>
 hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
 {
-    // the last row sees the most keys (packed documents: at most all of them)
+    // the last row sees the most keys (packed documents: at most a dense row)
     const int64_t pmax =
-        VARLEN ? p.T : visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
+        VARLEN ? p.sstride : visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
     const int64_t ngroups = (pmax + kSelGroup - 1) / kSelGroup;
     const int64_t nslab = (p.nrows + SQ - 1) / SQ;
     if (ngroups <= 0 || nslab <= 0) return hipSuccess;

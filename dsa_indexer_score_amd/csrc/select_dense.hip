@@ -206,7 +206,7 @@ struct RowView {
         if (p.varlen) {
             const DocWindow w = doc_window(p, t);
             pos = w.pos;
-            P = w.P;
+            P = w.P < p.sstride ? w.P : p.sstride;  // at most the dense row
             klo = w.klo;
             tok0 = w.tok0;
         } else {

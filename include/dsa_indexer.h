@@ -170,6 +170,15 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
  *           sequence at the end of its context).
  *   cu_tok  device int32 [ndoc], required with IDX_EXPAND: packed-token
  *           index of document i's position 0.
+ *   max_doc_keys  host int64: an upper bound on every document's key count
+ *           cu_k[i+1] - cu_k[i] (as a maximum sequence length is passed to
+ *           varlen attention); 0 = unknown, taken as T; values above T are
+ *           taken as T; negative: IDX_EINVAL.  It sizes the few-query
+ *           path's dense rows (max_doc_keys scores per row instead of T),
+ *           so batched decode over many documents needs far less workspace
+ *           and fewer passes; the streaming path does not use it.  A
+ *           document with more keys breaks the precondition: its rows'
+ *           selection is then unspecified, but every access stays in bounds.
  *   Output entries: compressed keys as global key indices cu_k[i] + j;
  *   with IDX_EXPAND, token indices cu_tok[i] + position (pool j expands to
  *   positions j*m .. j*m+m-1; with IDX_TAIL the positions from P*m to p of
@@ -181,26 +190,28 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
  * checked on the host; offsets are clamped to [0, T], and a row whose
  * document lacks complete pools gets a tail clipped to the row width.  With
  * IDX_EXPAND the caller keeps every output index below 2^31.  With at most
- * few_query_rows rows (batched decode: one row per sequence) and a dense
- * workspace of S x T scores within 4 GiB, the rows take the few-query path
- * (each row's own key window scored by all CUs, then the per-row exact
- * cut); otherwise the streaming path.  Both give identical results.
- * Workspace from indexer_workspace_bytes_varlen.
+ * few_query_rows rows (batched decode: one row per sequence) the rows take
+ * the few-query path (each row's own key window scored by all CUs into a
+ * dense row of max_doc_keys scores, then the per-row exact cut; in equal
+ * passes when S rows need more than 4 GiB); otherwise the streaming path.
+ * Both give identical results.  Workspace from
+ * indexer_workspace_bytes_varlen with the same max_doc_keys.
  */
 int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, const float *w,
                               int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
                               int64_t T, int H, int d, int m, int topk, int causal,
                               const int32_t *cu_q, const int32_t *cu_k, const int64_t *pos0,
-                              const int32_t *cu_tok, int ndoc, int32_t *idx, int32_t *valid_len,
-                              float *sel_score, void *workspace, size_t workspace_bytes,
-                              void *stream);
+                              const int32_t *cu_tok, int ndoc, int64_t max_doc_keys,
+                              int32_t *idx, int32_t *valid_len, float *sel_score,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes for indexer_score_topk_varlen: the few-query
- * layout of indexer_config.few_query_rows for S rows over T keys when that
- * path is taken, else candidate buffers for one query chunk of up to
- * min(S, query_chunk) rows, each bounded by T keys.  Host-only. */
+ * layout of indexer_config.few_query_rows for S rows of max_doc_keys keys
+ * (0: T) when that path is taken, else candidate buffers for one query
+ * chunk of up to min(S, query_chunk) rows, each bounded by T keys.
+ * Host-only. */
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
-                                   int topk, size_t *bytes);
+                                   int topk, int64_t max_doc_keys, size_t *bytes);
 
 /*
  * Adjacent-pair overlap diagnostic ("Adjacent-Query KV-Index Overlap in

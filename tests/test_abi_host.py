@@ -119,17 +119,35 @@ def test_workspace_bytes_of_the_few_query_path():
 
 def test_workspace_bytes_varlen_follow_the_path():
     """Packed documents: at or below few_query_rows the few-query layout,
-    above it (or with a negative setting) the streaming buffers."""
+    with rows of max_doc_keys scores (0 or above T: T), above it (or with a
+    negative setting) the streaming buffers."""
     n = ctypes.c_size_t()
     lib, h = _handle()
-    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(8, 4096)
-    assert lib.indexer_workspace_bytes_varlen(h, 100, 4096, 64, 128, 4, 2048,
+    for mk in (0, 4096, 10 ** 9):
+        assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, mk,
+                                                  ctypes.byref(n)) == 0
+        assert n.value == _dense_bytes(8, 4096)
+    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, 1000,
                                               ctypes.byref(n)) == 0
-    assert n.value == 100 * (4096 + 64) * 8
+    assert n.value == _dense_bytes(8, 1000)
+    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, -1,
+                                              ctypes.byref(n)) == -1
+    assert lib.indexer_workspace_bytes_varlen(h, 100, 4096, 64, 128, 4, 2048, 1000,
+                                              ctypes.byref(n)) == 0
+    assert n.value == 100 * (4096 + 64) * 8    # streaming: sized by T
+    # 64 decode rows over 64 documents of 262,144 keys: one pass of 64 short
+    # rows with the bound, passes of 21 rows of all 2^24 keys without it
+    T = 64 * 262144
+    assert lib.indexer_workspace_bytes_varlen(h, 64, T, 64, 128, 4, 2048, 262144,
+                                              ctypes.byref(n)) == 0
+    assert n.value == _dense_bytes(64, 262144)
+    assert lib.indexer_workspace_bytes_varlen(h, 64, T, 64, 128, 4, 2048, 0,
+                                              ctypes.byref(n)) == 0
+    assert n.value == _dense_bytes(21, T)
     lib.indexer_destroy(h)
     lib, h = _handle(few=-1)
-    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, 0,
+                                              ctypes.byref(n)) == 0
     assert n.value == 8 * (4096 + 64) * 8
     lib.indexer_destroy(h)
 

@@ -32,7 +32,7 @@ def _layout(rng, lens, m, pos0=None):
     return cu_q, cu_k, pos0, cu_tok
 
 
-def _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True, few=0):
+def _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True, few=0, max_doc_keys=0):
     import dsa_indexer_score_amd as dsai
     ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
                       query_chunk=inp.query_chunk or 0, few_query_rows=few, device=DEV)
@@ -41,7 +41,7 @@ def _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True, few=0):
         inp.q, inp.w, inp.k, t(cu_q, torch.int32), t(cu_k, torch.int32), m=inp.m, topk=inp.topk,
         causal=inp.causal, pos0=t(pos0, torch.int64),
         cu_tok=t(cu_tok, torch.int32) if inp.expand else None, q_scale=inp.q_scale,
-        k_scale=inp.k_scale, with_scores=with_scores)
+        k_scale=inp.k_scale, max_doc_keys=max_doc_keys, with_scores=with_scores)
     torch.cuda.synchronize()
     return out
 
@@ -213,3 +213,28 @@ def test_batched_decode_in_passes():
     for a, b in zip(dense, stream):
         assert torch.equal(a, b)
     log(f"  {inp.S} rows over {inp.T} keys, valid_len {dense[1][:4].tolist()}...")
+
+
+@pytest.mark.parametrize("m,expand", [(4, True), (1, False)])
+def test_batched_decode_with_a_bound_on_document_keys(m, expand):
+    """max_doc_keys sizes the dense rows by the longest document instead of
+    all keys: 43 rows over about 20M packed keys then fit one pass; with the
+    exact bound, a looser one and none the result is the same, bit for bit,
+    and equals the streaming path."""
+    rng = np.random.default_rng(13)
+    lens = rng.integers(250_000, 750_000, size=40) * m     # about 20M complete pools
+    q, k, w, qs, ks, cu_q, cu_k, pos0, cu_tok = _decode_batch(rng, lens, m, torch.bfloat16,
+                                                              H=4, d=32)
+    inp = gen.custom(q=q, k=k, w=w, m=m, topk=512, expand=expand, tail=expand).to(DEV)
+    longest = int(np.diff(cu_k).max())
+    import dsa_indexer_score_amd as dsai
+    ix = dsai.Indexer(torch.bfloat16, expand=expand, tail=expand, few_query_rows=64, device=DEV)
+    nb = ix.workspace_bytes_varlen(inp.S, inp.T, 4, 32, m, 512, longest)
+    assert nb < 13 * inp.S * longest                      # one pass of short rows
+    ref = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
+    for bound in (longest, longest + 12345, 0):
+        got = _run(inp, cu_q, cu_k, pos0, cu_tok, few=64, max_doc_keys=bound)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), bound
+    log(f"  m={m}: {inp.S} rows, longest document {longest} keys of {inp.T}, "
+        f"workspace {nb / 2 ** 20:.0f} MiB with the bound")
