@@ -64,6 +64,21 @@ def visible_pairs(S, T, m, causal, q_pos0=0):
     return total
 
 
+def scored_pairs(S, T, m, causal, ksel, q_pos0=0):
+    """Visible pairs of the rows that see more than ksel keys.  Without
+    selected scores, a block whose rows all see at most ksel keys writes
+    them unscored, so those rows' pairs are not counted as work (a slight
+    undercount: a block mixing both kinds scores all its rows)."""
+    if T <= ksel:
+        return 0
+    if not causal:
+        return S * T
+    first = max(q_pos0, (ksel + 1) * m - 1)  # first position with P > ksel
+    if first >= q_pos0 + S:
+        return 0
+    return visible_pairs(q_pos0 + S - first, T, m, causal, first)
+
+
 def kernel_sha(srcs=None):
     """sha256[:16] of the sources a kernel is compiled from (default: the
     streaming kernel's)."""
@@ -190,6 +205,7 @@ def main():
                       query_chunk=inp.query_chunk or 0, few_query_rows=few,
                       screen=args.screen, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
+    ksel = inp.topk // inp.m if inp.expand else inp.topk
     docs = None
     if args.varlen:
         # N equal documents; document i owns rows [i*L, (i+1)*L) and its own
@@ -205,7 +221,7 @@ def main():
         docs = dict(cu_q=t32(cu_q), cu_k=t32(cu_k), cu_tok=t32(cu_q[:-1]) if inp.expand else None,
                     lens=lens, nkeys=nkeys, cu_q_host=cu_q, cu_k_host=cu_k,
                     cu_tok_host=cu_q[:-1] if inp.expand else None,
-                    pairs=sum(visible_pairs(n, k, inp.m, inp.causal)
+                    pairs=sum(scored_pairs(n, k, inp.m, inp.causal, ksel)
                               for n, k in zip(lens, nkeys)))
     if args.decode_batch:
         # document i: keys [i*T_doc, (i+1)*T_doc), one row at its last token
@@ -286,8 +302,10 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     if docs:
         pairs = docs["pairs"]
+    elif args.decode:
+        pairs = visible_pairs(inp.S, inp.T, inp.m, inp.causal, inp.q_pos0)  # dense: all scored
     else:
-        pairs = visible_pairs(inp.S, inp.T, inp.m, inp.causal, inp.q_pos0)
+        pairs = scored_pairs(inp.S, inp.T, inp.m, inp.causal, ksel, inp.q_pos0)
     triples = pairs * inp.H
     flops = 2 * inp.d * triples
     n_launch = math.ceil(inp.S / (inp.query_chunk or inp.S))

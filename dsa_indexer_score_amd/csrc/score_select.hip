@@ -66,6 +66,11 @@
 //    ("Adjacent-Query KV-Index Overlap in 256K DSA Training", section 3),
 //    pools expand to m positions and the incomplete tail follows
 //    (GLM-5.3-Flash Module 06 "DSA & KPool", section 2), then -1 padding.
+//  * A row that sees at most Ksel keys selects all of them whatever their
+//    scores (valid_len = min(Ksel, visible)); when no selected scores are
+//    asked for, a block whose rows all see at most Ksel keys loads and
+//    scores nothing and writes those keys directly (the first Ksel*m
+//    positions of a sequence, documents shorter than that).
 #include "kernels.h"
 #include "mfma_ops.h"
 #include "select_common.h"
@@ -114,6 +119,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // keys, its position inside that document.
     int64_t pos, Pq, klo = 0, tok0 = 0;
     int64_t kbeg, kend;  // keys this block walks
+    int64_t Pmax;        // most keys any row of the block sees
     if constexpr (VARLEN) {
         __shared__ int64_t wlo[kQueriesPerBlock], whi[kQueriesPerBlock];
         const DocWindow dw = active ? doc_window(p, t) : DocWindow{};
@@ -128,10 +134,13 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         __syncthreads();
         kbeg = INT64_MAX;
         kend = INT64_MIN;
+        Pmax = 0;
 #pragma unroll
         for (int i = 0; i < kQueriesPerBlock; ++i) {
             kbeg = wlo[i] < kbeg ? wlo[i] : kbeg;
             kend = whi[i] > kend ? whi[i] : kend;
+            const int64_t Pi = whi[i] > wlo[i] ? whi[i] - wlo[i] : 0;
+            Pmax = Pi > Pmax ? Pi : Pmax;
         }
         if (kend <= kbeg) kbeg = kend = 0;
     } else {
@@ -142,6 +151,37 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         const int64_t Pblk = visible_keys(p.q_pos0 + p.row0 + last, p.T, p.m, p.causal);
         kbeg = DENSE ? (int64_t)sp * p.split_keys : 0;
         kend = DENSE && kbeg + p.split_keys < Pblk ? kbeg + p.split_keys : Pblk;
+        Pmax = Pblk;
+    }
+    // The end of an output row after its `body` selected entries: the tail
+    // positions of the incomplete pool (clipped to the row for packed
+    // documents, whose pools the caller forms), then -1; and valid_len.
+    auto end_row = [&](int body, float *srow) {
+        int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - Pq * p.m) : 0;
+        if (VARLEN) tl = tl < 0 ? 0 : (tl > p.W - body ? p.W - body : tl);  // keys missing: clip
+        int32_t *orow = p.idx + t * (int64_t)p.W;
+        for (int s = body + lane; s < p.W; s += 64) {
+            const bool in_tail = s < body + tl;
+            orow[s] = in_tail ? (int32_t)(tok0 + Pq * p.m + (s - body)) : -1;
+            if (srow) srow[s] = 0.f;
+        }
+        if (lane == 0) p.valid_len[t] = body + tl;
+    };
+    // No row of the block sees more keys than it selects and no score is
+    // asked for: every visible key is selected whatever its score, so the
+    // block loads nothing, scores nothing and writes its rows' visible keys
+    // in key order (block-uniform, after the last barrier of such a block).
+    if (!DENSE && !p.sel_score && Pmax <= p.ksel) {
+        if (active) {
+            const int mexp = p.expand ? p.m : 1;
+            const int64_t obase = VARLEN && p.expand ? tok0 - klo * p.m : 0;
+            int32_t *orow = p.idx + t * (int64_t)p.W;
+            for (int64_t j = lane; j < Pq; j += 64)
+                for (int x = 0; x < mexp; ++x)
+                    orow[j * mexp + x] = (int32_t)(obase + (klo + j) * mexp + x);
+            end_row((int)Pq * mexp, nullptr);
+        }
+        return;
     }
     const int64_t khi = klo + Pq;
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + kKeysPerTile - 1) / kKeysPerTile) : 0;
@@ -570,15 +610,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         }
         wcnt += __popcll(km);
     });
-    const int body = wcnt * mexp;
-    int tl = (p.expand && p.tail && p.causal) ? (int)(pos + 1 - Pq * p.m) : 0;
-    if (VARLEN) tl = tl < 0 ? 0 : (tl > p.W - body ? p.W - body : tl);  // keys missing: clip
-    for (int s = body + lane; s < p.W; s += 64) {
-        const bool in_tail = s < body + tl;
-        orow[s] = in_tail ? (int32_t)(tok0 + Pq * p.m + (s - body)) : -1;
-        if (srow) srow[s] = 0.f;
-    }
-    if (lane == 0) p.valid_len[t] = body + tl;
+    end_row(wcnt * mexp, srow);
 }
 
 template <int DT, int NB, int D, bool DENSE, bool VARLEN, bool SCREEN>

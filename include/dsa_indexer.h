@@ -133,7 +133,9 @@ int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int
  *   valid_len  device, [S] int32 out: number of valid entries of each row =
  *              min(Ksel, P_t) * (m if expand) + tail, P_t visible keys.
  *   sel_score  device, [S, W] fp32 out or NULL: the fp32 score of the key
- *              behind each entry; 0 for tail and padding slots.
+ *              behind each entry; 0 for tail and padding slots.  With NULL,
+ *              rows that see at most Ksel keys (all of them selected) are
+ *              answered without scoring on the streaming path.
  *   workspace  device, >= indexer_workspace_bytes(...) bytes, 16-B aligned;
  *              contents on entry are ignored, on return undefined.
  *   stream     hipStream_t (void*), NULL = default stream.

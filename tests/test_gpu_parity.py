@@ -185,6 +185,27 @@ def test_topk_larger_than_visible_and_topk_one():
         device_invariants(inp, out[0], out[1])
 
 
+@pytest.mark.parametrize("expand,tail,causal,q_pos0,T", [
+    (False, False, True, 0, None),       # first 2048 pools' rows taken whole
+    (True, True, True, 6001, None),      # blocks straddle the Ksel edge
+    (False, False, False, 0, 2000),      # non-causal, every row sees T <= Ksel
+    (True, False, False, 0, 3000)])      # non-causal, T > Ksel: scored
+def test_rows_with_at_most_ksel_keys_need_no_scores(expand, tail, causal, q_pos0, T):
+    """A row that sees at most Ksel keys selects all of them, so without
+    sel_score a block of such rows writes them without scoring; the result
+    equals the scored path's bit for bit and passes the oracle's rule."""
+    base = gen.generate("c4_csa_256k", S=12000, T=T or 4600)
+    inp = gen.custom(q=base.q, k=base.k, w=base.w, m=4, topk=2048 * (4 if expand else 1),
+                     expand=expand, tail=tail, causal=causal, q_pos0=q_pos0).to(DEV)
+    idx, vl, sc = run(inp, with_scores=True)
+    idx2, vl2 = run(inp, with_scores=False)
+    assert torch.equal(idx, idx2) and torch.equal(vl, vl2)
+    device_invariants(inp, idx2, vl2)
+    rows = np.concatenate([np.arange(0, inp.S, 97), [inp.S - 1]])
+    rep = check.compare(inp, rows, idx2.cpu().numpy()[rows], vl2.cpu().numpy()[rows])
+    assert rep["ok"], rep["failures"][:3]
+
+
 def test_non_causal_and_ragged():
     base = gen.generate("c4_csa_256k", S=1001, T=777, topk=100)
     inp = gen.custom(q=base.q, k=base.k, w=base.w, m=4, topk=100, causal=False).to(DEV)

@@ -238,3 +238,26 @@ def test_batched_decode_with_a_bound_on_document_keys(m, expand):
             assert torch.equal(a, b), bound
     log(f"  m={m}: {inp.S} rows, longest document {longest} keys of {inp.T}, "
         f"workspace {nb / 2 ** 20:.0f} MiB with the bound")
+
+
+@pytest.mark.parametrize("m,expand", [(4, True), (1, False)])
+def test_short_documents_need_no_scores(m, expand):
+    """Documents whose rows see at most Ksel keys select every visible key:
+    without sel_score their blocks write them unscored.  Mixed with longer
+    documents and padding, the result equals the oracle exactly (integer
+    inputs) and the scored call bit for bit."""
+    rng = np.random.default_rng(70 + m)
+    lens = list(rng.choice([1, 3, 4, 5, 9, 64, 100, 129, 130, 300], size=50)) + [700, 2000]
+    cu_q, cu_k, pos0, cu_tok = _layout(rng, lens, m)
+    S, T, H, d = int(cu_q[-1]) + 3, int(cu_k[-1]), 4, 32
+    q = torch.from_numpy(rng.integers(-3, 4, size=(S, H, d)).astype(np.float32))
+    k = torch.from_numpy(rng.integers(-3, 4, size=(T, d)).astype(np.float32))
+    w = torch.from_numpy(rng.choice([-1.0, -0.5, 0.5, 1.0], size=(S, H)).astype(np.float32))
+    topk = 32 * m if expand else 32                       # Ksel = 32 keys
+    inp = gen.custom(q=q, k=k, w=w, m=m, topk=topk, expand=expand, tail=expand).to(DEV)
+    plain = _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=False, few=-1)
+    scored = _run(inp, cu_q, cu_k, pos0, cu_tok, with_scores=True, few=-1)
+    assert torch.equal(plain[0], scored[0]) and torch.equal(plain[1], scored[1])
+    want = orc.select_rows_varlen(inp, cu_q, cu_k, pos0=pos0, cu_tok=cu_tok)
+    assert np.array_equal(plain[1].cpu().numpy(), want["valid_len"])
+    assert np.array_equal(plain[0].cpu().numpy(), want["idx"])
