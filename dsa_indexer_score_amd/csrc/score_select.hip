@@ -35,7 +35,8 @@
 //    w'[t,h] = w[t,h] * q_scale[t,h] multiplies the head sum, k_scale[j]
 //    multiplies the finished score.
 //  * The two waves that share a SIMD (w and w + 4) select at opposite ends of
-//    a tile, so one wave's branchy selection overlaps the other's MFMAs.
+//    a tile, so one wave's branchy selection overlaps the other's MFMAs; the
+//    wave in its MFMA phase runs at raised issue priority (s_setprio).
 //  * Optional screening (SCREEN instance; DoSA summary, "Method steps"):
 //    head block 0 holds a per-row certificate's kept heads and bounds every
 //    key; only keys whose bound reaches the running threshold get block 1,
@@ -512,6 +513,9 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             float part[NCB];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) part[cb] = 0.f;
+            // The wave in its MFMA phase issues first on its SIMD; the other
+            // wave's selection fills the issue slots its MFMAs leave.
+            __builtin_amdgcn_s_setprio(1);
             A bfr[KS];
             O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
             f32x16 accp;
@@ -544,6 +548,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                 if (s > 0) part[pcb] = e;
                 if (s < NS) accp = acc;
             }
+            __builtin_amdgcn_s_setprio(0);
             float sg[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
