@@ -9,7 +9,9 @@
 // tests the bit of every entry of row A, then zeroes the words it used.
 // Every LDS access is independent of the others, so the wave is bound by
 // loading the two rows, not by the latency of a search; rows of up to 2304
-// entries are loaded once into registers (one memory round trip per pair).
+// entries are loaded once into registers (one memory round trip per pair),
+// and window offsets are 32-bit (indices lie in [0, 2^31)), which keeps the
+// wave at about 90 registers so five waves share each SIMD.
 // Ranges wider than the bitmap are covered in consecutive windows.
 // With few pairs (decode: a handful of rows spread over the whole context)
 // one wave per pair would leave the chip idle and walk many small windows,
@@ -97,7 +99,7 @@ __global__ void __launch_bounds__(kWaves * 64) pair_overlap_kernel(const int32_t
     if (va > 0 && vb > 0) {
         const int64_t lo = a[0] < b[0] ? a[0] : b[0];
         const int64_t hi = a[va - 1] > b[vb - 1] ? a[va - 1] : b[vb - 1];
-        clear_words(bm, kWindow, lane);
+        clear_words(bm, hi - lo + 1 < kWindow ? hi - lo + 1 : kWindow, lane);
         wave_sync_lds();
         if (va <= 64 * kRegPerLane && vb <= 64 * kRegPerLane) {
             // both rows in registers: one round trip to memory per pair
@@ -109,17 +111,20 @@ __global__ void __launch_bounds__(kWaves * 64) pair_overlap_kernel(const int32_t
                 rb[i] = e < vb ? b[e] : 0;
             }
             for (int64_t w0 = lo; w0 <= hi; w0 += kWindow) {
+                // entries and w0 lie in [0, 2^31): 32-bit offsets, and an
+                // entry below the window wraps to >= 2^31
+                const int32_t w0i = (int32_t)w0;
 #pragma unroll
                 for (int i = 0; i < kRegPerLane; ++i) {
-                    const int64_t r = (int64_t)rb[i] - w0;
-                    if (i * 64 + lane < vb && r >= 0 && r < kWindow)
+                    const uint32_t r = (uint32_t)(rb[i] - w0i);
+                    if (i * 64 + lane < vb && r < (uint32_t)kWindow)
                         atomicOr(&bm[r >> 5], 1u << (r & 31));
                 }
                 wave_sync_lds();
 #pragma unroll
                 for (int i = 0; i < kRegPerLane; ++i) {
-                    const int64_t r = (int64_t)ra[i] - w0;
-                    if (i * 64 + lane < va && r >= 0 && r < kWindow)
+                    const uint32_t r = (uint32_t)(ra[i] - w0i);
+                    if (i * 64 + lane < va && r < (uint32_t)kWindow)
                         c += (bm[r >> 5] >> (r & 31)) & 1u;
                 }
                 wave_sync_lds();
