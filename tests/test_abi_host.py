@@ -239,6 +239,36 @@ def test_score_topk_validation_paths():
     lib.indexer_destroy(h)
 
 
+def _call_varlen(lib, h, **kw):
+    a = dict(q=FAKE, q_scale=None, w=FAKE, w_stride=0, k=FAKE, k_scale=None, S=16, T=16, H=64,
+             d=128, m=1, topk=4, causal=1, cu_q=FAKE, cu_k=FAKE, pos0=None, cu_tok=None, ndoc=2,
+             max_doc_keys=0, idx=FAKE, vl=FAKE, sel=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.indexer_score_topk_varlen(
+        h, a["q"], a["q_scale"], a["w"], a["w_stride"], a["k"], a["k_scale"], a["S"], a["T"],
+        a["H"], a["d"], a["m"], a["topk"], a["causal"], a["cu_q"], a["cu_k"], a["pos0"],
+        a["cu_tok"], a["ndoc"], a["max_doc_keys"], a["idx"], a["vl"], a["sel"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+def test_score_topk_varlen_validation_paths():
+    """Every case is rejected on the host, before any launch."""
+    lib, h = _handle()
+    E, WS = _lib.IDX_EINVAL, _lib.IDX_EWORKSPACE
+    assert _call_varlen(lib, h, S=0) == 0                 # empty problem: nothing to do
+    assert _call_varlen(lib, h, max_doc_keys=-1) == E
+    assert _call_varlen(lib, h, ndoc=-1) == E
+    assert _call_varlen(lib, h, cu_q=None) == E
+    assert _call_varlen(lib, h, cu_k=None) == E
+    assert _call_varlen(lib, h, ws_bytes=64) == WS
+    assert _call_varlen(lib, None) == E
+    lib.indexer_destroy(h)
+    lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL)
+    assert _call_varlen(lib, h, m=4, topk=8) == E         # expansion needs cu_tok
+    assert _call_varlen(lib, h, m=4, topk=8, cu_tok=FAKE, causal=0) == E  # tail needs causal
+    lib.indexer_destroy(h)
+
+
 def test_pair_overlap_host_paths():
     lib = _lib.load()
     assert lib.indexer_pair_overlap(None, None, 1, 4, None, None) == 0   # no pair
