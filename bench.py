@@ -357,7 +357,9 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved_tflops / peak,
                 "traffic": None if traffic is None else traffic,
                 "kernel": "score_select", "flops_per_launch": flops / n_launch,
-                "avg_launch_ms": score_s * 1e3 / n_launch}
+                "avg_launch_ms": score_s * 1e3 / n_launch,
+                # the MFMA the contraction runs on (e4m3 codes widen exactly to bf16)
+                "mfma_dtype": {"bf16": "bf16", "fp8": "bf16", "f32": "f32"}[inp.dtype]}
     if args.decode or args.decode_batch:
         # Few-query step (dense scoring + candidate filter + exact cut): bound
         # by reading the key set once from HBM.
