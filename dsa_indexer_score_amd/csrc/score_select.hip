@@ -492,6 +492,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const bool lagged = !DENSE && !SCREEN && wave >= kQueriesPerBlock / 2;
     float pend[NG];
     int64_t pend_j0 = -1;
+    // B operand reads: the XOR swizzle of a lane's rows (32 cb + l32) is
+    // l32 & SWZ for every column block, so the byte offsets of its KS chunks
+    // are fixed for the whole launch; a column block adds a constant.
+    constexpr bool kBOff = DT != 0 && SWZ < 32;
+    uint32_t boff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        boff[ks] = (uint32_t)((l32 * NCH + ((hh * KS + ks) ^ (l32 & SWZ))) * 16);
 
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
@@ -517,7 +525,15 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             // wave's selection fills the issue slots its MFMAs leave.
             __builtin_amdgcn_s_setprio(1);
             A bfr[KS];
-            O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
+            const char *tbytes = reinterpret_cast<const char *>(ktile[cur]);
+            if constexpr (kBOff) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    bfr[ks] = __builtin_bit_cast(
+                        A, *reinterpret_cast<const uint4 *>(tbytes + boff[ks]));
+            } else {
+                O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
+            }
             f32x16 accp;
             constexpr int EPK = (16 + KS - 1) / KS;  // epilogue elements per MFMA slot
 #pragma unroll
@@ -533,8 +549,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                 for (int ks = 0; ks < KS; ++ks) {
                     if (s < NS) acc = O::mma(qa[b][ks], bfr[ks], acc);
                     if (loads) {
-                        const int r = (cb + 1) * 32 + l32;
-                        O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
+                        if constexpr (kBOff) {
+                            bfr[ks] = __builtin_bit_cast(
+                                A, *reinterpret_cast<const uint4 *>(
+                                       tbytes + (cb + 1) * 32 * NCH * 16 + boff[ks]));
+                        } else {
+                            const int r = (cb + 1) * 32 + l32;
+                            O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
+                        }
                     }
                     if (s > 0) {
 #pragma unroll
