@@ -285,6 +285,15 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     }
     __syncthreads();
 
+    // B operand reads: the XOR swizzle of a lane's rows (32 cb + l32) is
+    // l32 & SWZ for every column block, so the byte offsets of its KS chunks
+    // are fixed for the whole launch; a column block adds a constant.
+    constexpr bool kBOff = DT != 0 && SWZ < 32;
+    uint32_t boff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        boff[ks] = (uint32_t)((l32 * NCH + ((hh * KS + ks) ^ (l32 & SWZ))) * 16);
+
     // Selection of one tile's scores (NG groups of 64 keys, one key per lane).
     constexpr int NCB = kKeysPerTile / 32;  // 32-key column blocks per tile
     constexpr int NG = NCB / 2;             // 64-key selection groups per tile
@@ -362,7 +371,15 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         constexpr int EPK = (16 + KS - 1) / KS;
         float part[NCB], ub[NCB];
         A bfr[KS];
-        O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
+        const char *tbytes = reinterpret_cast<const char *>(ktile[cur]);
+        if constexpr (kBOff) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                bfr[ks] = __builtin_bit_cast(
+                    A, *reinterpret_cast<const uint4 *>(tbytes + boff[ks]));
+        } else {
+            O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
+        }
         f32x16 accp;
 #pragma unroll
         for (int s = 0; s <= NCB; ++s) {  // MFMAs of column block s, epilogue of s - 1
@@ -375,8 +392,14 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             for (int ks = 0; ks < KS; ++ks) {
                 if (s < NCB) acc = O::mma(qa[0][ks], bfr[ks], acc);
                 if (loads) {
-                    const int r = (s + 1) * 32 + l32;
-                    O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
+                    if constexpr (kBOff) {
+                        bfr[ks] = __builtin_bit_cast(
+                            A, *reinterpret_cast<const uint4 *>(
+                                   tbytes + (s + 1) * 32 * NCH * 16 + boff[ks]));
+                    } else {
+                        const int r = (s + 1) * 32 + l32;
+                        O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
+                    }
                 }
                 if (s > 0) {
 #pragma unroll
@@ -492,14 +515,6 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const bool lagged = !DENSE && !SCREEN && wave >= kQueriesPerBlock / 2;
     float pend[NG];
     int64_t pend_j0 = -1;
-    // B operand reads: the XOR swizzle of a lane's rows (32 cb + l32) is
-    // l32 & SWZ for every column block, so the byte offsets of its KS chunks
-    // are fixed for the whole launch; a column block adds a constant.
-    constexpr bool kBOff = DT != 0 && SWZ < 32;
-    uint32_t boff[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        boff[ks] = (uint32_t)((l32 * NCH + ((hh * KS + ks) ^ (l32 & SWZ))) * 16);
 
     for (int it = 0; it < ntiles; ++it) {
         const int cur = it & 1;
