@@ -245,16 +245,34 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const char *kbytes = static_cast<const char *>(p.k);
     uint4 stage[CPT];
     float ksc = 0.f, kn = 0.f;
+    // bf16: a tile wholly below T is loaded unchecked off a uniform base with
+    // per-thread offsets fixed for the launch (measured no better for fp8)
+    constexpr bool kFastLoad = DT == 1;
+    uint32_t goff[kFastLoad ? CPT : 1];
+#pragma unroll
+    for (int c = 0; c < (kFastLoad ? CPT : 1); ++c) {
+        const int id = threadIdx.x + c * kThreads;
+        goff[c] = (uint32_t)((id / GCH) * ROWB + (id % GCH) * 16);
+    }
     auto load_tile = [&](int it) {
         const int64_t j0 = kbeg + (int64_t)it * kKeysPerTile;
+        if (kFastLoad && j0 + kKeysPerTile <= p.T) {
+            const char *tb = kbytes + j0 * ROWB;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int id = threadIdx.x + c * kThreads;
-            stage[c] = make_uint4(0, 0, 0, 0);
-            if (id < GTILE_CH) {
-                const int64_t key = j0 + id / GCH;
-                if (key < p.T)
-                    stage[c] = reinterpret_cast<const uint4 *>(kbytes + key * ROWB)[id % GCH];
+            for (int c = 0; c < CPT; ++c) {
+                const int id = threadIdx.x + c * kThreads;
+                if (id < GTILE_CH) stage[c] = *reinterpret_cast<const uint4 *>(tb + goff[c]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const int id = threadIdx.x + c * kThreads;
+                stage[c] = make_uint4(0, 0, 0, 0);
+                if (id < GTILE_CH) {
+                    const int64_t key = j0 + id / GCH;
+                    if (key < p.T)
+                        stage[c] = reinterpret_cast<const uint4 *>(kbytes + key * ROWB)[id % GCH];
+                }
             }
         }
         if (DT == 2 && threadIdx.x < kKeysPerTile) {
