@@ -78,6 +78,11 @@ def test_full_size_sampled_rows(name):
     log(f"  rows {rep['rows']}, index-mismatch rows {rep['index_mismatch_rows']}, "
         f"max score rel err {rep['max_score_rel_err']:.2e}")
     assert rep["ok"], rep["failures"]
+    # the benchmark's call asks for no scores (rows that see at most Ksel
+    # keys are then written unscored): the same rows, bit for bit
+    del sc
+    idx2, vl2 = run(inp, with_scores=False)
+    assert torch.equal(vl, vl2) and torch.equal(idx, idx2)
 
 
 # ---------------------------------------------------------------- edge cases

@@ -188,3 +188,19 @@ def test_screened_chunked_launches_and_modes():
         rep = check.compare(inp, rows, idx.cpu().numpy()[rows], vl.cpu().numpy()[rows],
                             sc.cpu().numpy()[rows])
         assert rep["ok"], (causal, rep["failures"][:3])
+
+
+def test_screened_full_size_sampled_rows():
+    """The 256K workload at full size in its benchmark launch configuration
+    (16 query chunks), screened: sampled rows against the oracle's rule,
+    every row against the device invariants."""
+    from gpu_util import device_invariants, rows_to_host
+    inp = gen.generate("c4_csa_256k", device=DEV)
+    idx, vl, sc = run(inp, screen=True)
+    device_invariants(inp, idx, vl)
+    rows = check.sample_rows(inp.S, m=inp.m, ksel=inp.topk, chunk=inp.query_chunk,
+                             seed=inp.seed, n_uniform=96)
+    hi, hv, hs = rows_to_host(rows, idx, vl, sc)
+    rep = check.compare(inp, rows, hi, hv, hs)
+    log(f"  rows {rep['rows']}, index-mismatch rows {rep['index_mismatch_rows']}")
+    assert rep["ok"], rep["failures"][:3]
