@@ -74,7 +74,7 @@ typedef struct {
      * the workspace by all CUs, candidates at or above a per-row threshold
      * estimate are filtered out by all CUs, and each row is then cut exactly
      * by one block; otherwise rows are scored and selected in one streaming
-     * pass per query chunk.  0 = default (64); negative = never.  Both paths
+     * pass per query chunk.  0 = default (1024); negative = never.  Both paths
      * give identical results.  The dense workspace holds, each part starting
      * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
      * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,

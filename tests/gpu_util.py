@@ -19,6 +19,9 @@ def run(inp, *, with_scores=True, query_chunk=None, **overrides):
               q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
               query_chunk=inp.query_chunk if query_chunk is None else query_chunk,
               with_scores=with_scores)
+    # these tests target the streaming path unless they name the few-query
+    # path (which has tests of its own; the sweeps also run the default)
+    kw["few_query_rows"] = -1
     kw.update(overrides)
     out = dsai.score_topk(inp.q, inp.w, inp.k, **kw)
     torch.cuda.synchronize()

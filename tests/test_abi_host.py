@@ -69,7 +69,8 @@ def test_create_rejects_bad_configs():
 
 
 def test_workspace_bytes_scale_with_chunk_and_selection():
-    lib, h = _handle(chunk=16384)
+    """Streaming path: candidate buffers for one query chunk."""
+    lib, h = _handle(chunk=16384, few=-1)
     n = ctypes.c_size_t()
     assert lib.indexer_workspace_bytes(h, 262144, 65536, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 16384 * 20736 * 8         # 10 x 2048 + 256 candidate slots of 8 bytes
@@ -92,7 +93,7 @@ def _dense_bytes(S, T):
 
 
 def test_workspace_bytes_of_the_few_query_path():
-    """At or below few_query_rows (default 64) the workspace holds the rows'
+    """At or below few_query_rows (default 1024) the workspace holds the rows'
     dense scores and the selection's candidate scratch, for as many rows as
     fit in 4 GiB (the rest are taken in further passes); a negative setting
     always streams."""
@@ -102,8 +103,10 @@ def test_workspace_bytes_of_the_few_query_path():
     assert n.value == _dense_bytes(64, 262144) == 64 * 262144 * 12 + 256 + 64 * 64 * 4
     assert lib.indexer_workspace_bytes(h, 1, 1001, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == _dense_bytes(1, 1001) == 4096 + 256 + 256 + 4096 * 8
-    assert lib.indexer_workspace_bytes(h, 65, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == 65 * 20736 * 8            # above the default: streaming buffers
+    assert lib.indexer_workspace_bytes(h, 1025, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 1025 * 20736 * 8          # above the default: streaming buffers
+    assert lib.indexer_workspace_bytes(h, 1024, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == _dense_bytes(1024, 262144)   # 3.2 GB: one pass
     assert lib.indexer_workspace_bytes(h, 64, 2 ** 25, 64, 128, 1, 2048, ctypes.byref(n)) == 0
     assert n.value == _dense_bytes(10, 2 ** 25)  # 25 GiB for all rows: passes of 10 rows
     lib.indexer_destroy(h)
@@ -132,9 +135,9 @@ def test_workspace_bytes_varlen_follow_the_path():
     assert n.value == _dense_bytes(8, 1000)
     assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, -1,
                                               ctypes.byref(n)) == -1
-    assert lib.indexer_workspace_bytes_varlen(h, 100, 4096, 64, 128, 4, 2048, 1000,
+    assert lib.indexer_workspace_bytes_varlen(h, 1025, 4096, 64, 128, 4, 2048, 1000,
                                               ctypes.byref(n)) == 0
-    assert n.value == 100 * (4096 + 64) * 8    # streaming: sized by T
+    assert n.value == 1025 * (4096 + 64) * 8   # streaming: sized by T
     # 64 decode rows over 64 documents of 262,144 keys: one pass of 64 short
     # rows with the bound, passes of 21 rows of all 2^24 keys without it
     T = 64 * 262144
@@ -158,7 +161,7 @@ def test_workspace_bytes_with_screening():
     aligned parts) and 4 bytes per key; H <= 32 cannot screen."""
     up = lambda x, a: -(-x // a) * a
     n = ctypes.c_size_t()
-    lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL | _lib.IDX_SCREEN)
+    lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL | _lib.IDX_SCREEN, few=-1)
     S, T, cap = 100, 5000, up(5000, 64) + 64          # cap: every visible key fits
     base = S * cap * 8
     want = up(base, 256) + 2 * up(S * 256, 256) + up(S * 128, 256) + up(S * 4, 256) + T * 4
