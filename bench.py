@@ -241,7 +241,7 @@ def main():
     # packed documents: the longest document's keys bound the dense rows
     max_doc_keys = int(max(docs["nkeys"])) if docs else 0
     nbytes = (ix.workspace_bytes_varlen(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk,
-                                        max_doc_keys) if docs else
+                                        len(docs["nkeys"]), max_doc_keys) if docs else
               ix.workspace_bytes(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk))
     ws = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)

@@ -139,9 +139,9 @@ class Indexer:
 
 
     def workspace_bytes_varlen(self, S: int, T: int, H: int, d: int, m: int, topk: int,
-                               max_doc_keys: int = 0) -> int:
+                               ndoc: int, max_doc_keys: int = 0) -> int:
         n = ctypes.c_size_t(0)
-        _lib.check(self._lib.indexer_workspace_bytes_varlen(self._h, S, T, H, d, m, topk,
+        _lib.check(self._lib.indexer_workspace_bytes_varlen(self._h, S, T, H, d, m, topk, ndoc,
                                                             max_doc_keys, ctypes.byref(n)),
                    "indexer_workspace_bytes_varlen")
         return n.value
@@ -190,7 +190,7 @@ class Indexer:
                 if with_scores else None
         else:
             idx, valid_len, sel = out
-        nbytes = self.workspace_bytes_varlen(S, T, H, d, m, topk, max_doc_keys)
+        nbytes = self.workspace_bytes_varlen(S, T, H, d, m, topk, ndoc, max_doc_keys)
         if workspace is None:
             workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
         rc = self._lib.indexer_score_topk_varlen(

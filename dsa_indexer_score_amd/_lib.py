@@ -37,7 +37,7 @@ SIGNATURES = {
                                 _I64, _P, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk_varlen": (_I, [_P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I, _I, _I, _I,
                                        _I, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _P, _SZ, _P]),
-    "indexer_workspace_bytes_varlen": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I64,
+    "indexer_workspace_bytes_varlen": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I, _I64,
                                             ctypes.POINTER(_SZ)]),
     "indexer_pair_overlap": (_I, [_P, _P, _I64, _I, _P, _P]),
     "indexer_pair_regions": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),

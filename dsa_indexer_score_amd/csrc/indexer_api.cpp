@@ -75,6 +75,11 @@ int64_t rows_per_launch(const indexer_config &cfg, int64_t S)
 // keys, the few-query path is faster up to 1,024 rows (1.4x-8.7x) and the
 // streaming path from 1,536 on (by 8-25 %).
 constexpr int64_t kFewRowsDefault = 1024;
+// Packed documents with several rows each score each row's keys on its own
+// on the few-query path, while the streaming path shares a staged key tile
+// among a block's 8 rows: there the default stays at 64 rows unless there
+// are at most two rows per document (batched decode).
+constexpr int64_t kFewRowsDocsDefault = 64;
 constexpr int64_t kDenseMaxBytes = int64_t(1) << 32;
 constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
 constexpr int64_t kRowsKernelMax = 2;  // rows scored with q in registers, keys from HBM
@@ -99,11 +104,13 @@ struct DenseLayout {
     }
 };
 
-// Few-query path: the S rows' visible scores (and the selection's scratch)
-// fit a dense workspace.
-bool use_dense(const indexer_config &cfg, int64_t S, int64_t T)
+// Few-query path: at most the configured number of rows (ndoc < 0: a plain
+// call, else the packed documents' count), and one row's visible scores
+// (and the selection's scratch) fit a dense workspace.
+bool use_dense(const indexer_config &cfg, int64_t S, int64_t T, int64_t ndoc = -1)
 {
-    const int64_t lim = cfg.few_query_rows == 0 ? kFewRowsDefault : cfg.few_query_rows;
+    int64_t lim = cfg.few_query_rows;
+    if (lim == 0) lim = ndoc < 0 || S <= 2 * ndoc ? kFewRowsDefault : kFewRowsDocsDefault;
     return lim > 0 && S <= lim && S <= 65535 && DenseLayout(1, T).bytes <= kDenseMaxBytes;
 }
 
@@ -277,7 +284,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     const int64_t cap = capacity(ksel, pmax);
     const int64_t rows = rows_per_launch(cfg, S);
     const int64_t Tk = docs.on ? docs.row_keys : T;  // scores per dense row
-    const bool dense = use_dense(cfg, S, Tk);
+    const bool dense = use_dense(cfg, S, Tk, docs.on ? docs.ndoc : -1);
     const bool screen = !docs.on && !dense && use_screen(cfg, H);
     const size_t need =
         dense     ? (size_t)DenseLayout(dense_rows(S, Tk), Tk).bytes
@@ -411,9 +418,9 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
 }
 
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
-                                   int topk, int64_t max_doc_keys, size_t *bytes)
+                                   int topk, int ndoc, int64_t max_doc_keys, size_t *bytes)
 {
-    if (!h || !bytes || S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1 ||
+    if (!h || !bytes || S < 0 || T < 0 || H < 1 || d < 1 || m < 1 || topk < 1 || ndoc < 0 ||
         max_doc_keys < 0)
         return IDX_EINVAL;
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
@@ -421,8 +428,8 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
     const int64_t stream_bytes = rows_per_launch(h->cfg, S) * capacity(ksel, T) * 8;
     const int64_t Tk = doc_row_keys(max_doc_keys, T);
-    *bytes = (size_t)(use_dense(h->cfg, S, Tk) ? DenseLayout(dense_rows(S, Tk), Tk).bytes
-                                                : stream_bytes);
+    *bytes = (size_t)(use_dense(h->cfg, S, Tk, ndoc) ? DenseLayout(dense_rows(S, Tk), Tk).bytes
+                                                      : stream_bytes);
     return IDX_OK;
 }
 

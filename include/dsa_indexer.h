@@ -74,7 +74,10 @@ typedef struct {
      * the workspace by all CUs, candidates at or above a per-row threshold
      * estimate are filtered out by all CUs, and each row is then cut exactly
      * by one block; otherwise rows are scored and selected in one streaming
-     * pass per query chunk.  0 = default (1024); negative = never.  Both paths
+     * pass per query chunk.  0 = default: 1024, or 64 for packed documents
+     * with more than two rows per document (indexer_score_topk_varlen: S >
+     * 2 ndoc), whose rows share key tiles on the streaming path; negative =
+     * never.  Both paths
      * give identical results.  The dense workspace holds, each part starting
      * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
      * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
@@ -196,8 +199,9 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
  * the few-query path (each row's own key window scored by all CUs into a
  * dense row of max_doc_keys scores, then the per-row exact cut; in equal
  * passes when S rows need more than 4 GiB); otherwise the streaming path.
- * Both give identical results.  Workspace from
- * indexer_workspace_bytes_varlen with the same max_doc_keys.
+ * With the default few_query_rows that means up to 1024 rows when S <= 2
+ * ndoc, else up to 64.  Both give identical results.  Workspace from
+ * indexer_workspace_bytes_varlen with the same S, T, ndoc and max_doc_keys.
  */
 int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, const float *w,
                               int64_t w_stride_s, const void *k, const float *k_scale, int64_t S,
@@ -207,13 +211,13 @@ int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, 
                               int32_t *idx, int32_t *valid_len, float *sel_score,
                               void *workspace, size_t workspace_bytes, void *stream);
 
-/* Device workspace bytes for indexer_score_topk_varlen: the few-query
- * layout of indexer_config.few_query_rows for S rows of max_doc_keys keys
- * (0: T) when that path is taken, else candidate buffers for one query
- * chunk of up to min(S, query_chunk) rows, each bounded by T keys.
- * Host-only. */
+/* Device workspace bytes for indexer_score_topk_varlen with the same S, T,
+ * ndoc and max_doc_keys: the few-query layout of indexer_config.
+ * few_query_rows for S rows of max_doc_keys keys (0: T) when that path is
+ * taken, else candidate buffers for one query chunk of up to min(S,
+ * query_chunk) rows, each bounded by T keys.  Host-only. */
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
-                                   int topk, int64_t max_doc_keys, size_t *bytes);
+                                   int topk, int ndoc, int64_t max_doc_keys, size_t *bytes);
 
 /*
  * Adjacent-pair overlap diagnostic ("Adjacent-Query KV-Index Overlap in

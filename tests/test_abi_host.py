@@ -123,34 +123,37 @@ def test_workspace_bytes_of_the_few_query_path():
 def test_workspace_bytes_varlen_follow_the_path():
     """Packed documents: at or below few_query_rows the few-query layout,
     with rows of max_doc_keys scores (0 or above T: T), above it (or with a
-    negative setting) the streaming buffers."""
+    negative setting) the streaming buffers.  The default is 1024 rows with
+    at most two rows per document (batched decode), else 64."""
     n = ctypes.c_size_t()
+    wb = lambda h, S, T, ndoc, mk: lib.indexer_workspace_bytes_varlen(h, S, T, 64, 128, 4, 2048,
+                                                                      ndoc, mk, ctypes.byref(n))
     lib, h = _handle()
     for mk in (0, 4096, 10 ** 9):
-        assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, mk,
-                                                  ctypes.byref(n)) == 0
+        assert wb(h, 8, 4096, 8, mk) == 0
         assert n.value == _dense_bytes(8, 4096)
-    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, 1000,
-                                              ctypes.byref(n)) == 0
+    assert wb(h, 8, 4096, 8, 1000) == 0
     assert n.value == _dense_bytes(8, 1000)
-    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, -1,
-                                              ctypes.byref(n)) == -1
-    assert lib.indexer_workspace_bytes_varlen(h, 1025, 4096, 64, 128, 4, 2048, 1000,
-                                              ctypes.byref(n)) == 0
+    assert wb(h, 8, 4096, 8, -1) == _lib.IDX_EINVAL
+    assert wb(h, 8, 4096, -1, 0) == _lib.IDX_EINVAL
+    assert wb(h, 1025, 4096, 1025, 1000) == 0
     assert n.value == 1025 * (4096 + 64) * 8   # streaming: sized by T
+    assert wb(h, 1024, 4096, 512, 1000) == 0   # two rows per document: few-query
+    assert n.value == _dense_bytes(1024, 1000)
+    assert wb(h, 1024, 4096, 511, 1000) == 0   # more: streaming above 64 rows
+    assert n.value == 1024 * (4096 + 64) * 8
+    assert wb(h, 64, 4096, 1, 1000) == 0       # at most 64 rows: few-query
+    assert n.value == _dense_bytes(64, 1000)
     # 64 decode rows over 64 documents of 262,144 keys: one pass of 64 short
     # rows with the bound, passes of 21 rows of all 2^24 keys without it
     T = 64 * 262144
-    assert lib.indexer_workspace_bytes_varlen(h, 64, T, 64, 128, 4, 2048, 262144,
-                                              ctypes.byref(n)) == 0
+    assert wb(h, 64, T, 64, 262144) == 0
     assert n.value == _dense_bytes(64, 262144)
-    assert lib.indexer_workspace_bytes_varlen(h, 64, T, 64, 128, 4, 2048, 0,
-                                              ctypes.byref(n)) == 0
+    assert wb(h, 64, T, 64, 0) == 0
     assert n.value == _dense_bytes(21, T)
     lib.indexer_destroy(h)
     lib, h = _handle(few=-1)
-    assert lib.indexer_workspace_bytes_varlen(h, 8, 4096, 64, 128, 4, 2048, 0,
-                                              ctypes.byref(n)) == 0
+    assert wb(h, 8, 4096, 8, 0) == 0
     assert n.value == 8 * (4096 + 64) * 8
     lib.indexer_destroy(h)
 

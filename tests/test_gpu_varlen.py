@@ -207,7 +207,8 @@ def test_batched_decode_in_passes():
     inp = gen.custom(q=q, k=k, w=w, m=4, topk=512, expand=True, tail=True).to(DEV)
     import dsa_indexer_score_amd as dsai
     ix = dsai.Indexer(torch.bfloat16, expand=True, tail=True, few_query_rows=64, device=DEV)
-    assert 17 * 12 * inp.T < ix.workspace_bytes_varlen(inp.S, inp.T, 4, 32, 4, 512) <= 1 << 32
+    assert 17 * 12 * inp.T < ix.workspace_bytes_varlen(inp.S, inp.T, 4, 32, 4, 512,
+                                                       len(lens)) <= 1 << 32
     dense = _run(inp, cu_q, cu_k, pos0, cu_tok, few=64)
     stream = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
     for a, b in zip(dense, stream):
@@ -229,7 +230,7 @@ def test_batched_decode_with_a_bound_on_document_keys(m, expand):
     longest = int(np.diff(cu_k).max())
     import dsa_indexer_score_amd as dsai
     ix = dsai.Indexer(torch.bfloat16, expand=expand, tail=expand, few_query_rows=64, device=DEV)
-    nb = ix.workspace_bytes_varlen(inp.S, inp.T, 4, 32, m, 512, longest)
+    nb = ix.workspace_bytes_varlen(inp.S, inp.T, 4, 32, m, 512, len(lens), longest)
     assert nb < 13 * inp.S * longest                      # one pass of short rows
     ref = _run(inp, cu_q, cu_k, pos0, cu_tok, few=-1)
     for bound in (longest, longest + 12345, 0):
