@@ -50,10 +50,11 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 class Indexer:
-    """A library handle: element dtype, output mode, query chunk size, the
-    row count at or below which the few-query path runs (0: the library's
-    default, negative: never) and DoSA certificate screening of the
-    streaming path (screen=True; used when 33 <= H <= 64)."""
+    """A library handle: element dtype, output mode, rows per streaming
+    launch (0: as many as 4 GiB of candidate buffers hold), the row count at
+    or below which the few-query path runs (0: the library's default,
+    negative: never) and DoSA certificate screening of the streaming path
+    (screen=True; used when 33 <= H <= 64)."""
 
     def __init__(self, dtype: torch.dtype, *, expand: bool = False, tail: bool = False,
                  query_chunk: int = 0, few_query_rows: int = 0, screen: bool = False,

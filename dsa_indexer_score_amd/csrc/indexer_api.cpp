@@ -64,9 +64,17 @@ int64_t capacity(int64_t ksel, int64_t pmax)
     return std::min(cap, all);
 }
 
-int64_t rows_per_launch(const indexer_config &cfg, int64_t S)
+// Rows per streaming launch: query_chunk, or by default as many rows as
+// 4 GiB of candidate buffers hold at the capacity T allows (so the size does
+// not depend on the call's positions), and at least 2,048 (256 blocks).
+// Results do not depend on the chunking.
+constexpr int64_t kStreamAutoBytes = int64_t(1) << 32;
+int64_t rows_per_launch(const indexer_config &cfg, int64_t S, int64_t cap_max)
 {
-    return (cfg.query_chunk > 0 && cfg.query_chunk < S) ? cfg.query_chunk : S;
+    if (cfg.query_chunk > 0) return cfg.query_chunk < S ? cfg.query_chunk : S;
+    int64_t r = kStreamAutoBytes / (cap_max * (int64_t)sizeof(uint2));
+    r = std::max<int64_t>(r / dsai::kQueriesPerBlock * dsai::kQueriesPerBlock, 2048);
+    return std::min(r, S);
 }
 
 // Rows at or below which the few-query path is taken by default: the
@@ -153,7 +161,8 @@ int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int H, i
                        int64_t pmax)
 {
     if (use_dense(cfg, S, T)) return DenseLayout(dense_rows(S, T), T).bytes;
-    return StreamLayout(rows_per_launch(cfg, S), capacity(ksel, pmax), T, use_screen(cfg, H)).bytes;
+    return StreamLayout(rows_per_launch(cfg, S, capacity(ksel, T)), capacity(ksel, pmax), T,
+                        use_screen(cfg, H)).bytes;
 }
 
 struct DeviceGuard {
@@ -282,7 +291,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     // ---- workspace
     const int64_t pmax = causal && !docs.on ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
-    const int64_t rows = rows_per_launch(cfg, S);
+    const int64_t rows = rows_per_launch(cfg, S, capacity(ksel, T));
     const int64_t Tk = docs.on ? docs.row_keys : T;  // scores per dense row
     const bool dense = use_dense(cfg, S, Tk, docs.on ? docs.ndoc : -1);
     const bool screen = !docs.on && !dense && use_screen(cfg, H);
@@ -426,7 +435,8 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
     if ((h->cfg.flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
     const int64_t ksel = ksel_of(topk, m, h->cfg.flags);
     if (ksel > kMaxSel) return IDX_EUNSUPPORTED;
-    const int64_t stream_bytes = rows_per_launch(h->cfg, S) * capacity(ksel, T) * 8;
+    const int64_t stream_bytes = rows_per_launch(h->cfg, S, capacity(ksel, T)) *
+                                 capacity(ksel, T) * 8;
     const int64_t Tk = doc_row_keys(max_doc_keys, T);
     *bytes = (size_t)(use_dense(h->cfg, S, Tk, ndoc) ? DenseLayout(dense_rows(S, Tk), Tk).bytes
                                                       : stream_bytes);

@@ -68,7 +68,9 @@ enum {
 typedef struct {
     int dtype;           /* enum idx_dtype                                     */
     int flags;           /* IDX_EXPAND | IDX_TAIL | IDX_SCREEN                 */
-    int64_t query_chunk; /* queries per launch (bounds the workspace); 0 = all */
+    int64_t query_chunk; /* queries per streaming launch (bounds the workspace);
+                          * 0 = as many as 4 GiB of candidate buffers hold
+                          * (at least 2048); results do not depend on it    */
     /* Few-query path (decode, small batches against a long key set): when
      * S <= few_query_rows, every visible score of the S rows is written to
      * the workspace by all CUs, candidates at or above a per-row threshold
@@ -215,7 +217,8 @@ int indexer_score_topk_varlen(indexer_t h, const void *q, const float *q_scale, 
  * ndoc and max_doc_keys: the few-query layout of indexer_config.
  * few_query_rows for S rows of max_doc_keys keys (0: T) when that path is
  * taken, else candidate buffers for one query chunk of up to min(S,
- * query_chunk) rows, each bounded by T keys.  Host-only. */
+ * query_chunk) rows (0: as for indexer_score_topk), each bounded by T keys.
+ * Host-only. */
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
                                    int topk, int ndoc, int64_t max_doc_keys, size_t *bytes);
 

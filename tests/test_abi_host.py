@@ -83,6 +83,22 @@ def test_workspace_bytes_scale_with_chunk_and_selection():
     lib.indexer_destroy(h)
 
 
+def test_workspace_bytes_automatic_query_chunk():
+    """query_chunk = 0 on the streaming path: as many rows as 4 GiB of
+    candidate buffers hold at the capacity T allows (a multiple of 8, at
+    least 2,048), never more than S."""
+    lib, h = _handle(few=-1)
+    n = ctypes.c_size_t()
+    cap = 10 * 2048 + 256                                  # 20,736 slots of 8 bytes
+    rows = (2 ** 32 // (cap * 8)) // 8 * 8                 # 25,888
+    assert lib.indexer_workspace_bytes(h, 2 ** 20, 262144, 64, 128, 4, 2048,
+                                       ctypes.byref(n)) == 0
+    assert n.value == rows * cap * 8 <= 2 ** 32
+    assert lib.indexer_workspace_bytes(h, 5000, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
+    assert n.value == 5000 * cap * 8
+    lib.indexer_destroy(h)
+
+
 def _dense_bytes(S, T):
     """The documented few-query layout: scores, estimates, candidate counts
     and (score, key) candidates, each part 256-byte aligned."""

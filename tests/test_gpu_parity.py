@@ -85,6 +85,16 @@ def test_full_size_sampled_rows(name):
     assert torch.equal(vl, vl2) and torch.equal(idx, idx2)
 
 
+def test_automatic_query_chunk_is_bit_identical():
+    """query_chunk = 0 takes as many rows per launch as 4 GiB of candidate
+    buffers hold (25,888 at the 256K workload): the same rows as the
+    benchmark's 16,384-row chunks, bit for bit."""
+    inp = gen.generate("c4_csa_256k", device=DEV)
+    a = run(inp, with_scores=False)
+    b = run(inp, with_scores=False, query_chunk=0)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[0], b[0])
+
+
 # ---------------------------------------------------------------- edge cases
 def _exact_rows(inp, out):
     ref = orc.select_rows(inp, np.arange(inp.S))
