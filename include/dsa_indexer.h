@@ -79,8 +79,9 @@ typedef struct {
      * pass per query chunk.  0 = default: 1024, or 64 for packed documents
      * with more than two rows per document (indexer_score_topk_varlen: S >
      * 2 ndoc), whose rows share key tiles on the streaming path; negative =
-     * never.  Both paths
-     * give identical results.  The dense workspace holds, each part starting
+     * never.  Both paths give identical results.  For packed documents the
+     * rows hold max_doc_keys scores instead of T (see the varlen call).  The
+     * dense workspace holds, each part starting
      * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
      * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
      * G = ceil(max(T, 1) / 4096)) and the candidates as (score, key) pairs
