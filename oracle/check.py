@@ -65,7 +65,7 @@ def _keys_of_row(row, v, P, m, expand):
 def compare(inp, rows, idx, valid_len, sel_score=None, *, exact=None, rtol=None, ref=None,
             nthreads=0):
     """Check result rows (numpy arrays for the given call rows) against the
-    oracle.  Returns a report dict; report['ok'] is the verdict and
+    oracle.  Returns a report dict; report['ok'] is the outcome and
     report['failures'] lists the first problems found."""
     rows = np.asarray(rows, np.int64)
     idx = np.asarray(idx)
