@@ -28,6 +28,7 @@ constexpr int kWords = 2048;                 // 8 KB of bitmap per wave
 constexpr int64_t kWindow = (int64_t)kWords * 32;
 constexpr int kRegPerLane = 36;              // rows up to 2304 entries stay in registers
 constexpr int kUnroll = 8;                   // row entries in flight per lane (long rows)
+constexpr int kRegionsUnroll = 32;           // region split: a 2048-entry row in one batch
 constexpr int kWideThreads = 1024;           // few pairs: one block per pair ...
 constexpr int kWideWords = 32768;            // ... with 128 KB of bitmap
 constexpr int64_t kWideWindow = (int64_t)kWideWords * 32;
@@ -45,19 +46,19 @@ __device__ __forceinline__ void clear_words(uint32_t *bm, int64_t nbits, int lan
     for (int i = lane; i < nw; i += 64) bm[i] = 0;
 }
 
-// f(x) for every entry x of row[0, n), kUnroll loads issued before use.
-template <class F>
+// f(x) for every entry x of row[0, n), U loads issued before use.
+template <int U = kUnroll, class F>
 __device__ __forceinline__ void for_each_index(const int32_t *row, int n, int lane, F &&f)
 {
-    for (int base = 0; base < n; base += 64 * kUnroll) {
-        int32_t v[kUnroll];
+    for (int base = 0; base < n; base += 64 * U) {
+        int32_t v[U];
 #pragma unroll
-        for (int i = 0; i < kUnroll; ++i) {
+        for (int i = 0; i < U; ++i) {
             const int e = base + i * 64 + lane;
             v[i] = e < n ? row[e] : 0;
         }
 #pragma unroll
-        for (int i = 0; i < kUnroll; ++i)
+        for (int i = 0; i < U; ++i)
             if (base + i * 64 + lane < n) f(v[i]);
     }
 }
@@ -65,18 +66,18 @@ __device__ __forceinline__ void for_each_index(const int32_t *row, int n, int la
 // f(valid, x) for every lane of every batch, in row order (entry base +
 // 64 i + lane), kUnroll loads in flight; lanes past the row get valid = false
 // so wave-uniform state in f stays uniform.
-template <class F>
+template <int U = kUnroll, class F>
 __device__ __forceinline__ void for_each_index_ordered(const int32_t *row, int n, int lane, F &&f)
 {
-    for (int base = 0; base < n; base += 64 * kUnroll) {
-        int32_t v[kUnroll];
+    for (int base = 0; base < n; base += 64 * U) {
+        int32_t v[U];
 #pragma unroll
-        for (int i = 0; i < kUnroll; ++i) {
+        for (int i = 0; i < U; ++i) {
             const int e = base + i * 64 + lane;
             v[i] = e < n ? row[e] : 0;
         }
 #pragma unroll
-        for (int i = 0; i < kUnroll; ++i) f(base + i * 64 + lane < n, v[i]);
+        for (int i = 0; i < U; ++i) f(base + i * 64 + lane < n, v[i]);
     }
 }
 
@@ -240,11 +241,11 @@ __global__ void __launch_bounds__(kWaves * 64) pair_regions_kernel(
             const int64_t nbits = hi - w0 + 1 < kWindow ? hi - w0 + 1 : kWindow;
             auto in_win = [&](int32_t x) { return (int64_t)x >= w0 && (int64_t)x - w0 < kWindow; };
             // row B's bits; row A's entries -> shared or left-only
-            for_each_index(b, vb, lane, [&](int32_t x) {
+            for_each_index<kRegionsUnroll>(b, vb, lane, [&](int32_t x) {
                 if (in_win(x)) atomicOr(&bm[(x - w0) >> 5], 1u << ((x - w0) & 31));
             });
             wave_sync_lds();
-            for_each_index_ordered(a, va, lane, [&](bool valid, int32_t x) {
+            for_each_index_ordered<kRegionsUnroll>(a, va, lane, [&](bool valid, int32_t x) {
                 const bool in = valid && in_win(x);
                 const bool hit = in && ((bm[(x - w0) >> 5] >> ((x - w0) & 31)) & 1u);
                 put(osh, nsh, hit, x);
@@ -254,11 +255,11 @@ __global__ void __launch_bounds__(kWaves * 64) pair_regions_kernel(
             clear_words(bm, nbits, lane);
             wave_sync_lds();
             // row A's bits; row B's entries -> right-only
-            for_each_index(a, va, lane, [&](int32_t x) {
+            for_each_index<kRegionsUnroll>(a, va, lane, [&](int32_t x) {
                 if (in_win(x)) atomicOr(&bm[(x - w0) >> 5], 1u << ((x - w0) & 31));
             });
             wave_sync_lds();
-            for_each_index_ordered(b, vb, lane, [&](bool valid, int32_t x) {
+            for_each_index_ordered<kRegionsUnroll>(b, vb, lane, [&](bool valid, int32_t x) {
                 const bool in = valid && in_win(x);
                 const bool hit = in && ((bm[(x - w0) >> 5] >> ((x - w0) & 31)) & 1u);
                 put(orr, nr, in && !hit, x);
