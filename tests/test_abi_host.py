@@ -136,6 +136,29 @@ def test_workspace_bytes_of_the_few_query_path():
     lib.indexer_destroy(h)
 
 
+def test_few_query_passes_property():
+    """For any S and T the few-query workspace holds R rows: the most that
+    fit in 4 GiB (at least one, at most S); past one row's fit the call
+    streams instead."""
+    import random
+    rng = random.Random(3)
+    lib, h = _handle(few=60000)
+    n = ctypes.c_size_t()
+    for _ in range(300):
+        S, T = rng.randint(1, 3000), rng.choice([rng.randint(1, 5000), rng.randint(1, 1 << 28)])
+        assert lib.indexer_workspace_bytes(h, S, T, 8, 64, 1, 64, ctypes.byref(n)) == 0
+        if _dense_bytes(1, T) > 1 << 32:
+            assert n.value < _dense_bytes(1, T)                # streaming buffers
+            continue
+        lo, hi = 1, S
+        while lo < hi:                                         # largest r with r rows fitting
+            mid = (lo + hi + 1) // 2
+            lo, hi = (mid, hi) if _dense_bytes(mid, T) <= 1 << 32 else (lo, mid - 1)
+        R = lo
+        assert n.value == _dense_bytes(R, T) <= 1 << 32, (S, T)
+    lib.indexer_destroy(h)
+
+
 def test_workspace_bytes_varlen_follow_the_path():
     """Packed documents: at or below few_query_rows the few-query layout,
     with rows of max_doc_keys scores (0 or above T: T), above it (or with a
