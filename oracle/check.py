@@ -15,6 +15,17 @@ n = d + H + 4 (the dot, the head sum and the final products), and keys may
 trade places when their oracle scores lie within twice the largest such
 bound of the k-th score.
 
+Row structure, checked on every row in both modes before any comparison
+(GLM-5.3-Flash Module 06 "DSA & KPool", sections 2-3; "Adjacent-Query
+KV-Index Overlap in 256K DSA Training", section 3):
+  * valid_len equals the visibility formula; slots from valid_len on are -1;
+  * the first valid_len entries are non-negative and strictly ascending, so
+    no index repeats;
+  * every entry is visible to the row (key < P, or position <= p);
+  * in expand mode the entries below P*m form whole pools -- m consecutive
+    positions starting at a multiple of m -- and the entries from P*m on are
+    exactly the tail positions P*m .. p (none without the tail flag).
+
 Rules for the float problems:
   * valid_len and the tail positions must match exactly;
   * with tau the oracle's k-th score and eps = 1e-3 * max |s*| over the
@@ -49,6 +60,41 @@ def sample_rows(S, *, m=1, ksel=2048, chunk=None, seed=0, n_uniform=256, causal=
     rng = np.random.default_rng(seed)
     rows.update(rng.integers(0, S, size=min(n_uniform, S)).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < S), dtype=np.int64)
+
+
+def row_structure(row, v, p, *, T, m, topk, causal, expand, tail):
+    """Problems with one output row (row = its W slots, v = its valid_len,
+    p = its absolute position), as a list of strings (empty = well formed)."""
+    row = np.asarray(row, np.int64)
+    fails = []
+    ev = orc.expected_valid_len(p, T, m, topk, causal, expand, tail)
+    if v != ev:
+        fails.append(f"valid_len {v} != {ev}")
+    if v < 0 or v > row.size:
+        return fails + [f"valid_len {v} outside the row"]
+    if np.any(row[v:] != -1):
+        fails.append("padding is not -1")
+    sel = row[:v]
+    if np.any(sel < 0):
+        fails.append("negative index")
+    if np.any(np.diff(sel) <= 0):
+        fails.append("entries not strictly ascending (repeated or out of order)")
+    P = orc.visible_keys(p, T, m, causal)
+    if not expand:
+        if sel.size and sel.max() >= P:
+            fails.append(f"key {int(sel.max())} not visible (P = {P})")
+        return fails
+    body, tl = sel[sel < P * m], sel[sel >= P * m]
+    want_tail = np.arange(P * m, p + 1) if (tail and causal) else np.empty(0, np.int64)
+    if not np.array_equal(tl, want_tail):
+        fails.append("tail is not exactly the positions P*m .. p")
+    if body.size % m:
+        fails.append("partial pool")
+    else:
+        pools = body.reshape(-1, m)
+        if np.any(pools != pools[:, :1] + np.arange(m)) or np.any(pools[:, 0] % m):
+            fails.append("pool not whole or not aligned")
+    return fails
 
 
 def _keys_of_row(row, v, P, m, expand):
@@ -88,6 +134,11 @@ def compare(inp, rows, idx, valid_len, sel_score=None, *, exact=None, rtol=None,
     need_rows, need_keys, pending = [], [], []
     for r, t in enumerate(rows):
         v = int(valid_len[r])
+        bad = row_structure(idx[r], v, int(t) + inp.q_pos0, T=inp.T, m=m, topk=inp.topk,
+                            causal=inp.causal, expand=expand, tail=inp.tail)
+        if bad:
+            fails.extend(f"row {t}: {b}" for b in bad)
+            continue
         if v != ref["valid_len"][r]:
             fails.append(f"row {t}: valid_len {v} != {ref['valid_len'][r]}")
             continue

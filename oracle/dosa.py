@@ -24,6 +24,13 @@ need not be computed.  The construction, step by step:
      (subadditivity: [a_A . k]_+ <= sum_{h in A} |w_h| [q_h . k]_+); the other
      omitted negative heads are dropped (they only lower the score).
      U_i = sum_{kept h} w~_h [q_h . k_i]_+ + E ||k_i|| - [a_A . k_i]_+.
+  4. joint residual bound ("Technical novelty"): with u_h = w_h d_h over the
+     omitted positive heads, sum_h [u_h . k]_+ <= E_joint ||k|| where
+     E_joint = (||sum_h u_h|| + sqrt(sum_{h,l} |u_h . u_l|)) / 2, because
+     [x]_+ = (x + |x|) / 2, sum_h u_h . k <= ||sum_h u_h|| ||k|| and
+     sum_h |u_h . k| = (sum_h sign_h u_h) . k, whose squared norm factor is
+     at most sum_{h,l} |u_h . u_l|.  E_joint <= E (triangle inequality), so
+     it replaces E in U_i.
 
 Choices the page leaves open, and the reading taken: the anchor of an
 omitted positive head is the kept positive head maximising
@@ -32,9 +39,8 @@ positive head is kept the omitted positive heads are bounded by
 w_h ||q_h|| ||k|| alone; the seed set is supplied by the caller, and with
 an empty seed set every activation frequency p_h is taken as 1/2 (the
 negative-head priority is then |w_h| ||q_h|| / 2) and no omitted negative
-head counts as majority-active (the aggregate a_A is zero).  The joint
-residual bound (a tightening of E) is not used: the plain allowance is
-already a valid certificate.
+head counts as majority-active (the aggregate a_A is zero).  u_h carries the
+head weight (w_h > 0), so E_joint is in the units of the score.
 """
 from __future__ import annotations
 
@@ -51,8 +57,9 @@ def seed_threshold(scores_seed: np.ndarray, K: int) -> float:
 
 def certificate(q: np.ndarray, w: np.ndarray, seed_keys: np.ndarray, r: int):
     """Certificate of one query: q [H, d], w [H] (fp64), seed_keys [n, d].
-    Returns dict(kept, w_fold, E, aA) with U(k) = sum_kept w_fold [q k]_+ +
-    E ||k|| - [aA k]_+."""
+    Returns dict(kept, w_fold, E, E_joint, aA, A, p) with U(k) = sum_kept
+    w_fold [q k]_+ + E_joint ||k|| - [aA k]_+ (E in place of E_joint gives
+    the looser per-head allowance)."""
     q = np.asarray(q, np.float64)
     w = np.asarray(w, np.float64)
     H = q.shape[0]
@@ -71,26 +78,33 @@ def certificate(q: np.ndarray, w: np.ndarray, seed_keys: np.ndarray, r: int):
     w_fold = {h: float(w[h]) for h in kept}
     kept_pos = [h for h in kept if w[h] > 0]
     E = 0.0
+    U_res = []                      # weighted residuals u_h = w_h d_h
     for h in (h for h in pos if h not in kept):
         if kept_pos:
             j = max(kept_pos, key=lambda j: max(q[h] @ q[j], 0.0) / norms[j])
             beta = max(q[h] @ q[j], 0.0) / (q[j] @ q[j])
             w_fold[j] += w[h] * beta
-            E += w[h] * np.linalg.norm(q[h] - beta * q[j])
+            d_h = q[h] - beta * q[j]
         else:
-            E += w[h] * norms[h]
+            d_h = q[h]
+        E += w[h] * np.linalg.norm(d_h)
+        U_res.append(w[h] * d_h)
+    U_res = np.array(U_res).reshape(-1, q.shape[1])
+    E_joint = 0.5 * (np.linalg.norm(U_res.sum(axis=0)) + np.sqrt(np.abs(U_res @ U_res.T).sum()))
     # the majority-active set needs activation evidence: empty without seeds
     A = [h for h in neg if h not in kept and p[h] >= 0.5] if X.shape[1] else []
     aA = np.zeros(q.shape[1])
     for h in A:
         aA += abs(w[h]) * q[h]
-    return dict(kept=kept, w_fold=np.array([w_fold[h] for h in kept]), E=float(E), aA=aA,
-                q_kept=q[kept])
+    return dict(kept=kept, w_fold=np.array([w_fold[h] for h in kept]), E=float(E),
+                E_joint=float(E_joint), aA=aA, A=A, p=p, q_kept=q[kept])
 
 
-def upper_bounds(cert: dict, keys: np.ndarray) -> np.ndarray:
-    """U_i for every key row of keys [n, d] (fp64)."""
+def upper_bounds(cert: dict, keys: np.ndarray, joint: bool = True) -> np.ndarray:
+    """U_i for every key row of keys [n, d] (fp64); joint=False uses the
+    per-head allowance E instead of E_joint."""
     keys = np.asarray(keys, np.float64)
     Xk = cert["q_kept"] @ keys.T
-    return (cert["w_fold"] @ np.maximum(Xk, 0.0) + cert["E"] * np.linalg.norm(keys, axis=1)
+    E = cert["E_joint"] if joint else cert["E"]
+    return (cert["w_fold"] @ np.maximum(Xk, 0.0) + E * np.linalg.norm(keys, axis=1)
             - np.maximum(keys @ cert["aA"], 0.0))

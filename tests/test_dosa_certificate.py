@@ -12,6 +12,9 @@ import pytest
 from oracle import dosa
 from workloads import gen
 
+# every pin below takes the certificate module as an argument, so that
+# test_dosa_mutants.py can run the same pins against planted mistakes
+
 
 def _scores(q, w, keys):
     return w @ np.maximum(q @ keys.T, 0.0)
@@ -116,3 +119,116 @@ def test_survival_on_the_synthetic_workload():
     print("survival (certificate vs seed tau, exact score vs seed tau, certificate vs final "
           "K-th score):", np.round(surv, 3).tolist())
     assert surv[:, 0].min() > 0.5      # the screen rejects little on these inputs
+
+
+# Seeds of the hand-derived cases below (d = 4): the signs of k_y, k_z and
+# k_w over the 8 seed keys fix the activation frequencies
+# p_1 = 4/8 (head 1 reads k_y), p_2 = 7/8 (head 2 reads k_z), p_3 = 4/8
+# (head 3 reads k_w) and p_4 = 1/8 (head 4 reads -k_z).
+_SEEDS = np.array([[0, y, z, u] for y, z, u in zip([1, 1, 1, 1, -1, -1, -1, -1],
+                                                   [1, 1, 1, 1, 1, 1, 1, -1],
+                                                   [1, -1, 1, -1, 1, -1, 1, -1])], float)
+_Q4 = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 2, 0], [0, 0, 0, 1], [0, 0, -1, 0]], float)
+_W4 = np.array([1.0, -1.0, -1.0, -0.25, -0.1])
+
+
+def pin_activation_frequency_ranks_negative_heads(mod=dosa):
+    """Budget r = 2: head 0 (the only positive head) plus one negative head.
+    By |w_h| ||q_h|| alone head 2 (1 x 2) beats head 1 (1 x 1), but the
+    page's priority weighs in min(p_h, 1 - p_h): head 1 gets 1 x 1 x 1/2 =
+    0.5, head 2 gets 1 x 2 x 1/8 = 0.25, head 3 0.25 x 1 x 1/2 = 0.125,
+    head 4 0.1 x 1 x 1/8 = 0.0125 -- so heads 0 and 1 are kept."""
+    cert = mod.certificate(_Q4, _W4, _SEEDS, r=2)
+    # k_x = 0 on every seed: head 0 never fires
+    np.testing.assert_allclose(cert["p"], [0.0, 0.5, 7 / 8, 0.5, 1 / 8])
+    assert sorted(cert["kept"]) == [0, 1]
+
+
+def pin_majority_active_aggregate_by_hand(mod=dosa):
+    """Same row: the omitted negative heads are 2 (p = 7/8), 3 (p = 1/2, on
+    the boundary, included since A takes p_h >= 1/2) and 4 (p = 1/8, left
+    out), so a_A = 1 x (0,0,2,0) + 0.25 x (0,0,0,1) = (0,0,2,0.25).  For the
+    key (1,0,1,4): kept part 1 x [1]_+ + (-1) x [0]_+ = 1, aggregate
+    [2 + 1]_+ = 3, U = 1 - 3 = -2, which is the exact score
+    1 - 0 - 1 x 2 - 0.25 x 4 - 0.1 x [-1]_+ = -2.  For (1,0,-1,-4) the
+    aggregate is [-3]_+ = 0 and U = 1 against the score 1 - 0.1 x 1 = 0.9.
+    Without the aggregate U would be 1 for both; with head 4 in A it would
+    be -1.9 for the first key."""
+    cert = mod.certificate(_Q4, _W4, _SEEDS, r=2)
+    assert sorted(cert["A"]) == [2, 3]
+    np.testing.assert_allclose(cert["aA"], [0, 0, 2, 0.25])
+    keys = np.array([[1, 0, 1, 4], [1, 0, -1, -4]], float)
+    np.testing.assert_allclose(mod.upper_bounds(cert, keys), [-2.0, 1.0], atol=1e-12)
+    np.testing.assert_allclose(_scores(_Q4, _W4, keys), [-2.0, 0.9], atol=1e-12)
+
+
+def _joint_case(q_omit, w_omit):
+    """Head 0 = (3,0,0) kept (largest w ||q||, budget 1), the given omitted
+    positive heads orthogonal to it (beta = 0, residual = the head)."""
+    q = np.vstack([[3.0, 0, 0], q_omit])
+    w = np.concatenate([[1.0], w_omit])
+    return q, w
+
+
+def pin_joint_residual_closed_forms(mod=dosa):
+    """u_h = w_h q_h here.  Orthogonal residuals u = (0,1,0), (0,0,0.5):
+    ||sum u|| = sqrt(1.25) and sum |u_h . u_l| = 1.25, so E_joint =
+    sqrt(1.25) = sqrt(5)/2 against E = 1.5.  Parallel u = (0,1,0), (0,1,0):
+    E_joint = (2 + sqrt(4)) / 2 = 2 = E.  Opposite u = (0,1,0), (0,-1,0):
+    E_joint = (0 + sqrt(4)) / 2 = 1 against E = 2, and it is attained:
+    [k_y]_+ + [-k_y]_+ = |k_y| = 1 x ||k|| at k = (0,1,0)."""
+    q, w = _joint_case([[0, 1, 0], [0, 0, 1]], [1.0, 0.5])
+    c = mod.certificate(q, w, np.zeros((0, 3)), r=1)
+    assert c["E"] == pytest.approx(1.5) and c["E_joint"] == pytest.approx(np.sqrt(5) / 2)
+    q, w = _joint_case([[0, 1, 0], [0, 2, 0]], [1.0, 0.5])
+    c = mod.certificate(q, w, np.zeros((0, 3)), r=1)
+    assert c["E"] == pytest.approx(2.0) and c["E_joint"] == pytest.approx(2.0)
+    q, w = _joint_case([[0, 1, 0], [0, -1, 0]], [1.0, 1.0])
+    c = mod.certificate(q, w, np.zeros((0, 3)), r=1)
+    assert c["E"] == pytest.approx(2.0) and c["E_joint"] == pytest.approx(1.0)
+    k = np.array([[0.0, 1.0, 0.0]])
+    assert mod.upper_bounds(c, k)[0] == pytest.approx(_scores(q, w, k)[0])   # tight
+
+
+def pin_projection_clips_negative_correlation(mod=dosa):
+    """Kept head 0 = (1,0) (w = 2), omitted positive head 1 = (-1,1) (w = 1):
+    q_1 . q_0 = -1, so beta = [-1]_+ / 1 = 0, no fold, residual = q_1 and
+    E = E_joint = sqrt(2).  At k = (-1,1) the score is 2 x 0 + 1 x [2]_+ = 2
+    and U = 0 + sqrt(2) x sqrt(2) = 2 (tight); an unclipped beta = -1 would
+    fold w_0 to 1 and claim U = sqrt(2) < 2."""
+    q = np.array([[1.0, 0.0], [-1.0, 1.0]])
+    w = np.array([2.0, 1.0])
+    c = mod.certificate(q, w, np.zeros((0, 2)), r=1)
+    assert c["kept"] == [0] and c["w_fold"][0] == pytest.approx(2.0)
+    assert c["E_joint"] == pytest.approx(np.sqrt(2))
+    k = np.array([[-1.0, 1.0]])
+    assert mod.upper_bounds(c, k)[0] == pytest.approx(2.0)
+
+
+def pin_bounds_hold_on_random_rows(mod=dosa):
+    """U >= s with the joint and with the per-head allowance, on random rows
+    with and without seeds (a_A in play), shared and independent heads."""
+    rng = np.random.default_rng(21)
+    for case in range(80):
+        H, d = int(rng.integers(2, 40)), int(rng.integers(2, 24))
+        shared = 0.9 if case % 2 else 0.0
+        q = shared * rng.standard_normal(d) + np.sqrt(1 - shared ** 2) * \
+            rng.standard_normal((H, d))
+        w = rng.standard_normal(H)
+        keys = rng.standard_normal((200, d))
+        c = mod.certificate(q, w, keys[:int(rng.integers(0, 64))], int(rng.integers(0, H + 1)))
+        s = _scores(q, w, keys)
+        assert c["E_joint"] <= c["E"] * (1 + 1e-12) + 1e-12
+        for joint in (True, False):
+            U = mod.upper_bounds(c, keys, joint=joint)
+            assert np.all(U >= s - 1e-9 * (1 + np.abs(s))), (case, joint)
+
+
+DOSA_PINS = [pin_activation_frequency_ranks_negative_heads, pin_majority_active_aggregate_by_hand,
+             pin_joint_residual_closed_forms, pin_projection_clips_negative_correlation,
+             pin_bounds_hold_on_random_rows]
+
+
+@pytest.mark.parametrize("pin", DOSA_PINS, ids=lambda f: f.__name__)
+def test_dosa_pin(pin):
+    pin()
