@@ -108,8 +108,11 @@ def cpu_baseline(inp, budget_s, seed, docs=None):
     With docs (packed documents) the oracle runs per document."""
     from oracle import oracle as orc
     rng = np.random.default_rng(seed)
+    # every core this process may run on, up to the host's CPU share for one
+    # GPU (OMP_NUM_THREADS where the host sets it, else 16)
     cores = len(os.sched_getaffinity(0))
-    threads = min(cores, 16)
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(cores, share))
     done_rows, done_triples, spent = 0, 0, 0.0
     while spent < budget_s:
         rows = np.sort(rng.integers(0, inp.S, size=4 * threads))
@@ -130,8 +133,10 @@ def cpu_baseline(inp, budget_s, seed, docs=None):
         done_rows += rows.size
         done_triples += sum(vis) * inp.H
     return dict(value=done_triples / spent, unit="triples/s", cores=threads, kind="oracle",
+                host_cores=cores, threads=threads,
                 sample=f"{done_rows} seeded uniform rows of the {inp.name} workload "
-                       f"({done_triples} triples, {spent:.1f} s, fp64, {threads} threads)")
+                       f"({done_triples} triples, {spent:.1f} s, fp64, {threads} threads on "
+                       f"{cores} available cores)")
 
 
 def main():

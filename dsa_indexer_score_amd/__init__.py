@@ -84,17 +84,8 @@ class Indexer:
             self._lib.indexer_destroy(h)
             self._h = None
 
-    def workspace_bytes(self, S: int, T: int, H: int, d: int, m: int, topk: int) -> int:
-        n = ctypes.c_size_t(0)
-        _lib.check(self._lib.indexer_workspace_bytes(self._h, S, T, H, d, m, topk, ctypes.byref(n)),
-                   "indexer_workspace_bytes")
-        return n.value
-
-    def score_topk(self, q, w, k, *, m: int = 1, topk: int, causal: bool = True,
-                   q_scale=None, k_scale=None, q_pos0: int = 0, with_scores: bool = False,
-                   workspace: Optional[torch.Tensor] = None, out=None):
-        """q [S,H,d], w [S,H] or [H] (fp32), k [T,d] -> (idx [S,W] int32,
-        valid_len [S] int32[, sel_score [S,W] fp32]) on q's device."""
+    def _inputs(self, q, w, k, q_scale, k_scale):
+        """Check q, w, k and the fp8 scales; returns (S, H, d, T, w_stride)."""
         if q.dim() != 3 or k.dim() != 2:
             raise ValueError("q must be [S, H, d] and k [T, d]")
         S, H, d = q.shape
@@ -120,17 +111,59 @@ class Indexer:
             if tuple(q_scale.shape) != (S, H) or tuple(k_scale.shape) != (T,) or \
                     q_scale.dtype != torch.float32 or k_scale.dtype != torch.float32:
                 raise ValueError("q_scale must be float32 [S,H], k_scale float32 [T]")
-        W = output_width(topk, m, self.expand, self.tail)
+        elif q_scale is not None or k_scale is not None:
+            raise ValueError("q_scale / k_scale are for fp8 only")
+        return S, H, d, T, w_stride
+
+    def _outputs(self, S, W, with_scores, out):
+        """Allocate (idx, valid_len, sel) or check the caller's: contiguous,
+        on this device, int32 [S, W] / int32 [S] / float32 [S, W] or None."""
         if out is None:
             idx = torch.empty((S, W), dtype=torch.int32, device=self.device)
             valid_len = torch.empty((S,), dtype=torch.int32, device=self.device)
             sel = torch.empty((S, W), dtype=torch.float32, device=self.device) \
                 if with_scores else None
-        else:
-            idx, valid_len, sel = out
-        nbytes = self.workspace_bytes(S, T, H, d, m, topk)
+            return idx, valid_len, sel
+        idx, valid_len, sel = out
+        for name, t, dt, shape in (("idx", idx, torch.int32, (S, W)),
+                                   ("valid_len", valid_len, torch.int32, (S,)),
+                                   ("sel_score", sel, torch.float32, (S, W))):
+            if t is None and name == "sel_score":
+                continue
+            if t is None or t.dtype != dt or tuple(t.shape) != shape or \
+                    t.device != self.device or not t.is_contiguous():
+                raise ValueError(f"out {name} must be a contiguous {dt} tensor of shape "
+                                 f"{shape} on {self.device}")
+        if with_scores and sel is None:
+            raise ValueError("with_scores needs a sel_score tensor in out")
+        return idx, valid_len, sel
+
+    def _workspace(self, nbytes, workspace):
         if workspace is None:
-            workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
+            return torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1 or \
+                not workspace.is_contiguous() or workspace.device != self.device or \
+                workspace.numel() < nbytes:
+            raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} "
+                             f"bytes on {self.device}")
+        return workspace
+
+    def workspace_bytes(self, S: int, T: int, H: int, d: int, m: int, topk: int) -> int:
+        n = ctypes.c_size_t(0)
+        _lib.check(self._lib.indexer_workspace_bytes(self._h, S, T, H, d, m, topk, ctypes.byref(n)),
+                   "indexer_workspace_bytes")
+        return n.value
+
+    def score_topk(self, q, w, k, *, m: int = 1, topk: int, causal: bool = True,
+                   q_scale=None, k_scale=None, q_pos0: int = 0, with_scores: bool = False,
+                   workspace: Optional[torch.Tensor] = None, out=None):
+        """q [S,H,d], w [S,H] or [H] (fp32), k [T,d] -> (idx [S,W] int32,
+        valid_len [S] int32[, sel_score [S,W] fp32]) on q's device.  out =
+        (idx, valid_len, sel_score or None) writes into the caller's tensors."""
+        S, H, d, T, w_stride = self._inputs(q, w, k, q_scale, k_scale)
+        W = output_width(topk, m, self.expand, self.tail)
+        idx, valid_len, sel = self._outputs(S, W, with_scores, out)
+        workspace = self._workspace(self.workspace_bytes(S, T, H, d, m, topk), workspace)
         rc = self._lib.indexer_score_topk(
             self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
             d, m, topk, int(bool(causal)), int(q_pos0), _ptr(idx), _ptr(valid_len), _ptr(sel),
@@ -157,12 +190,7 @@ class Indexer:
         token offset; max_doc_keys (host int, 0 = unknown) bounds every
         document's key count and sizes the few-query path's dense rows.
         Returns (idx, valid_len[, sel_score])."""
-        if q.dim() != 3 or k.dim() != 2:
-            raise ValueError("q must be [S, H, d] and k [T, d]")
-        S, H, d = q.shape
-        T = k.shape[0]
-        if q.dtype != self.dtype or k.dtype != self.dtype or w.dtype != torch.float32:
-            raise TypeError(f"q and k must be {self.dtype}, w float32")
+        S, H, d, T, w_stride = self._inputs(q, w, k, q_scale, k_scale)
         ndoc = cu_q.numel() - 1
         if ndoc < 0 or cu_k.numel() != ndoc + 1:
             raise ValueError("cu_q and cu_k must both have ndoc + 1 entries")
@@ -174,26 +202,10 @@ class Indexer:
                 raise ValueError(f"{name} must be a contiguous {dt} tensor on {self.device}")
             if name in ("pos0", "cu_tok") and t.numel() != ndoc:
                 raise ValueError(f"{name} must have ndoc entries")
-        for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
-            if t is not None and (t.device != self.device or not t.is_contiguous()):
-                raise ValueError(f"{name} must be contiguous on {self.device}")
-        if w.dim() == 1 and w.shape[0] == H:
-            w_stride = 0
-        elif w.dim() == 2 and tuple(w.shape) == (S, H):
-            w_stride = H
-        else:
-            raise ValueError("w must be [H] or [S, H]")
         W = output_width(topk, m, self.expand, self.tail)
-        if out is None:
-            idx = torch.empty((S, W), dtype=torch.int32, device=self.device)
-            valid_len = torch.empty((S,), dtype=torch.int32, device=self.device)
-            sel = torch.empty((S, W), dtype=torch.float32, device=self.device) \
-                if with_scores else None
-        else:
-            idx, valid_len, sel = out
-        nbytes = self.workspace_bytes_varlen(S, T, H, d, m, topk, ndoc, max_doc_keys)
-        if workspace is None:
-            workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=self.device)
+        idx, valid_len, sel = self._outputs(S, W, with_scores, out)
+        workspace = self._workspace(
+            self.workspace_bytes_varlen(S, T, H, d, m, topk, ndoc, max_doc_keys), workspace)
         rc = self._lib.indexer_score_topk_varlen(
             self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
             d, m, topk, int(bool(causal)), _ptr(cu_q), _ptr(cu_k), _ptr(pos0), _ptr(cu_tok), ndoc,

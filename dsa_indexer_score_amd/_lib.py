@@ -45,6 +45,7 @@ SIGNATURES = {
     "indexer_screen_certificates": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _P, _P,
                                          _P]),
     "indexer_strerror": (ctypes.c_char_p, [_I]),
+    "indexer_source_hash": (ctypes.c_char_p, []),
 }
 
 _lib = None
@@ -53,17 +54,25 @@ _lock = threading.Lock()
 
 def load():
     """Load the HIP library; build it first if it has never been built.
-    Raises if it cannot be built or loaded: there is no fallback path."""
+    Raises if it cannot be built or loaded, or if it was built from other
+    sources than the ones beside it (a stale build): there is no fallback
+    path."""
     global _lib
     with _lock:
         if _lib is None:
+            from . import build
             if not os.path.exists(LIB_PATH):
-                from . import build
                 build.build()
             lib = ctypes.CDLL(LIB_PATH)
             for name, (res, args) in SIGNATURES.items():
                 fn = getattr(lib, name)
                 fn.restype, fn.argtypes = res, args
+            built, want = lib.indexer_source_hash().decode(), build.source_hash()
+            if built != want:
+                raise RuntimeError(
+                    f"{LIB_PATH} was built from other sources (hash {built}) than those in "
+                    f"{build.CSRC} (hash {want}); rebuild it with "
+                    f"'python -m dsa_indexer_score_amd.build'")
             _lib = lib
     return _lib
 

@@ -1,6 +1,7 @@
 """Build libdsa_indexer.so (HIP for gfx950) in-tree with hipcc."""
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -28,6 +29,22 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-I", INCLUDE, "-I", CSRC]
 
 
+def source_hash() -> str:
+    """Hash of everything the library is compiled from: the kernel and host
+    sources, the public header and the compile flags.  Built into the
+    library (indexer_source_hash) so that a library built from other
+    sources is refused at load time."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
+    for path in [os.path.join(CSRC, f) for f in files] + [os.path.join(INCLUDE, "dsa_indexer.h")]:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    flags = [f for f in HIP_FLAGS if f not in (INCLUDE, CSRC)]      # paths differ between trees
+    h.update(repr((flags, sorted(FILE_FLAGS.items()))).encode())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -38,12 +55,14 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
+    tag = source_hash()
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
+            cmd.insert(-4, f'-DDSAI_SOURCE_HASH="{tag}"')
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

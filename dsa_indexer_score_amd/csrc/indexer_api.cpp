@@ -536,6 +536,11 @@ int indexer_overlap_summary(const int32_t *shared, const int32_t *valid_len, int
     return IDX_OK;
 }
 
+#ifndef DSAI_SOURCE_HASH
+#define DSAI_SOURCE_HASH "unknown"
+#endif
+const char *indexer_source_hash(void) { return DSAI_SOURCE_HASH; }
+
 const char *indexer_strerror(int code)
 {
     const char *base = "unknown status";

@@ -1,5 +1,5 @@
-// Per-wave streaming top-k machinery shared by the scoring kernel and the
-// split-merge kernel: order-preserving score codes, the packed LDS
+// Per-wave streaming top-k machinery shared by the streaming scoring kernel
+// and the few-query selection kernels: order-preserving score codes, the packed LDS
 // histogram, boundary searches, batched passes over a candidate list, exact
 // radix cuts under the tie rule, and in-place compaction.
 //

@@ -228,7 +228,8 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
  * 256K DSA Training", sections 1 and 3): for each non-overlapping pair
  * (rows 2i, 2i+1), i < S/2, shared[i] = |A_2i ∩ A_2i+1| where A_t is
  * idx[t, 0:valid_len[t]] (ascending, as indexer_score_topk writes it);
- * exact intersection by binary search, no all-pairs comparison.
+ * exact intersection (a bitmap over the pair's index range in LDS), no
+ * all-pairs comparison.
  *   idx [S, W] int32, valid_len [S] int32: device, in.
  *   shared [S/2] int32: device, out.  An odd last row is unpaired.
  */
@@ -305,6 +306,12 @@ int indexer_screen_certificates(indexer_t h, const void *q, const float *q_scale
 /* Static text for a status code, followed (for IDX_EHIP) by the calling
  * thread's last HIP error.  Never NULL. */
 const char *indexer_strerror(int code);
+
+/* Identification of the build: a short hash of the sources and compile
+ * flags the library was built from ("unknown" if the build did not set it),
+ * so a loader can refuse a library that no longer matches its sources.
+ * Static string, never NULL. */
+const char *indexer_source_hash(void);
 
 #ifdef __cplusplus
 }

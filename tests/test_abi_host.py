@@ -345,3 +345,11 @@ def test_strerror_is_never_null():
     lib = _lib.load()
     for code in (0, -1, -2, -3, -4, -99):
         assert lib.indexer_strerror(code)
+
+
+def test_library_was_built_from_these_sources():
+    """The loader refuses a library whose embedded source hash differs from
+    the sources beside it; the library under test matches them."""
+    from dsa_indexer_score_amd import build
+    lib = _lib.load()
+    assert lib.indexer_source_hash().decode() == build.source_hash()
