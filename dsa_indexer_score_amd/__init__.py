@@ -172,6 +172,22 @@ class Indexer:
         return (idx, valid_len, sel) if with_scores else (idx, valid_len)
 
 
+    def score_topk_noalloc(self, q, w, k, *, m: int = 1, topk: int, causal: bool = True,
+                           q_scale=None, k_scale=None, q_pos0: int = 0,
+                           with_scores: bool = False, out=None):
+        """score_topk through indexer_score_topk_noalloc: no workspace, the
+        library's static scratch instead (same results).  With out given,
+        nothing is allocated here either."""
+        S, H, d, T, w_stride = self._inputs(q, w, k, q_scale, k_scale)
+        W = output_width(topk, m, self.expand, self.tail)
+        idx, valid_len, sel = self._outputs(S, W, with_scores, out)
+        rc = self._lib.indexer_score_topk_noalloc(
+            self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
+            d, m, topk, int(bool(causal)), int(q_pos0), _ptr(idx), _ptr(valid_len), _ptr(sel),
+            _stream(self.device))
+        _lib.check(rc, "indexer_score_topk_noalloc")
+        return (idx, valid_len, sel) if with_scores else (idx, valid_len)
+
     def workspace_bytes_varlen(self, S: int, T: int, H: int, d: int, m: int, topk: int,
                                ndoc: int, max_doc_keys: int = 0) -> int:
         n = ctypes.c_size_t(0)

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
 SOURCES = ["score_select.hip", "score_rows.hip", "screen_cert.hip", "select_dense.hip",
-           "pair_overlap.hip", "indexer_api.cpp"]
+           "pair_overlap.hip", "noalloc.hip", "indexer_api.cpp"]
 
 # Per-file extra flags.  The scoring kernel assumes finite inputs (a documented
 # precondition), so IEEE NaN quieting is switched off there: ReLU then lowers

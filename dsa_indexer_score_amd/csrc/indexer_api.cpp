@@ -24,6 +24,7 @@ struct indexer_s {
 namespace {
 
 thread_local std::string g_hip_error;
+thread_local std::string g_detail;  // why the last IDX_EWORKSPACE was returned, if known
 thread_local std::string g_msg;
 
 int fail_hip(hipError_t e)
@@ -252,11 +253,28 @@ int64_t doc_row_keys(int64_t max_doc_keys, int64_t T)
     return max_doc_keys > 0 && max_doc_keys < T ? max_doc_keys : T;
 }
 
+// Largest rows r (a multiple of the block's 8 queries unless r = S < 8) whose
+// layout bytes(r) fit in `avail`; 0 when not even the smallest fits.
+template <class F> int64_t rows_that_fit(int64_t S, int64_t avail, F bytes)
+{
+    const int64_t q = dsai::kQueriesPerBlock;
+    int64_t lo = 0, hi = S;  // bytes(lo) fits (or lo = 0), find the largest
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (bytes(mid) <= avail) lo = mid; else hi = mid - 1;
+    }
+    return lo >= q || lo == S ? (lo == S ? lo : lo / q * q) : 0;
+}
+
+// fit_bytes > 0: the workspace is a fixed buffer of that many bytes (the
+// no-allocation entry point); the launches are sized to fit it -- the
+// few-query path in passes of the rows it holds, else streaming launches of
+// the rows it holds -- and a problem that fits neither way is refused.
 int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const float *w,
                     int64_t w_stride_s, const void *k, const float *k_scale, int64_t S, int64_t T,
                     int H, int d, int m, int topk, int causal, int64_t q_pos0, const Docs &docs,
                     int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
-                    size_t workspace_bytes, void *stream)
+                    size_t workspace_bytes, void *stream, int64_t fit_bytes = 0)
 {
     if (!h) return IDX_EINVAL;
     const indexer_config &cfg = h->cfg;
@@ -291,14 +309,37 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     // ---- workspace
     const int64_t pmax = causal && !docs.on ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
-    const int64_t rows = rows_per_launch(cfg, S, capacity(ksel, T));
+    int64_t rows = rows_per_launch(cfg, S, capacity(ksel, T));
     const int64_t Tk = docs.on ? docs.row_keys : T;  // scores per dense row
-    const bool dense = use_dense(cfg, S, Tk, docs.on ? docs.ndoc : -1);
-    const bool screen = !docs.on && !dense && use_screen(cfg, H);
-    const size_t need =
-        dense     ? (size_t)DenseLayout(dense_rows(S, Tk), Tk).bytes
+    bool dense = use_dense(cfg, S, Tk, docs.on ? docs.ndoc : -1);
+    int64_t dense_R = dense ? dense_rows(S, Tk) : 0;  // rows per few-query pass
+    bool screen = !docs.on && !dense && use_screen(cfg, H);
+    size_t need =
+        dense     ? (size_t)DenseLayout(dense_R, Tk).bytes
         : docs.on ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
                   : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
+    if (fit_bytes > 0) {
+        if (dense) {
+            dense_R = std::min(dense_R, rows_that_fit(S, fit_bytes, [&](int64_t r) {
+                                   return DenseLayout(r, Tk).bytes;
+                               }));
+            if (dense_R < 1) dense_R = 0, dense = false;
+        }
+        screen = !docs.on && !dense && use_screen(cfg, H);
+        if (!dense) {
+            const bool scr = screen;
+            rows = std::min(rows, rows_that_fit(S, fit_bytes, [&](int64_t r) {
+                                return StreamLayout(r, cap, T, scr).bytes;
+                            }));
+            if (rows < 1) {
+                g_detail = "the problem needs more scratch than the library's static " +
+                           std::to_string(fit_bytes >> 20) + " MiB hold";
+                return IDX_EWORKSPACE;
+            }
+        }
+        need = dense ? (size_t)DenseLayout(dense_R, Tk).bytes
+                     : (size_t)StreamLayout(rows, cap, T, screen).bytes;
+    }
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
 
     DeviceGuard guard(h->device);
@@ -341,7 +382,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         // (row, key segment) (candidate filter) and per row (exact cut); in
         // passes of as many rows as the workspace holds.
         // equal passes (each at most the R rows the workspace holds)
-        const int64_t R = dense_rows(S, Tk);
+        const int64_t R = dense_R;
         const DenseLayout L(R, Tk);
         const int64_t npass = (S + R - 1) / R;
         const int64_t Rp = npass > 0 ? (S + npass - 1) / npass : R;
@@ -424,6 +465,33 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
                            q_pos0, Docs{}, idx, valid_len, sel_score, workspace, workspace_bytes,
                            stream);
+}
+
+int indexer_score_topk_noalloc(indexer_t h, const void *q, const float *q_scale, const float *w,
+                               int64_t w_stride_s, const void *k, const float *k_scale,
+                               int64_t S, int64_t T, int H, int d, int m, int topk, int causal,
+                               int64_t q_pos0, int32_t *idx, int32_t *valid_len,
+                               float *sel_score, void *stream)
+{
+    if (!h) return IDX_EINVAL;
+    g_detail.clear();
+    // Sizes that cannot fit are refused on the host before any HIP call: a
+    // dry run of the sizing against a null workspace of the scratch's size
+    // returns IDX_EWORKSPACE for "does not fit" and the validation codes for
+    // bad arguments; only IDX_EWORKSPACE from a null workspace means "fits".
+    const int64_t cap_bytes = (int64_t)dsai::noalloc_scratch_bytes();
+    int rc = score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk,
+                             causal, q_pos0, Docs{}, idx, valid_len, sel_score, nullptr,
+                             (size_t)cap_bytes, stream, cap_bytes);
+    if (rc != IDX_EWORKSPACE || !g_detail.empty()) return rc;  // invalid, S = 0, or too large
+    DeviceGuard guard(h->device);
+    if (guard.err != hipSuccess) return fail_hip(guard.err);
+    void *scratch = nullptr;
+    const hipError_t e = dsai::noalloc_scratch(h->device, &scratch);
+    if (e != hipSuccess) return fail_hip(e);
+    return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
+                           q_pos0, Docs{}, idx, valid_len, sel_score, scratch, (size_t)cap_bytes,
+                           stream, cap_bytes);
 }
 
 int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int d, int m,
@@ -553,6 +621,10 @@ const char *indexer_strerror(int code)
     }
     if (code == IDX_EHIP && !g_hip_error.empty()) {
         g_msg = std::string(base) + ": " + g_hip_error;
+        return g_msg.c_str();
+    }
+    if (code == IDX_EWORKSPACE && !g_detail.empty()) {
+        g_msg = std::string(base) + ": " + g_detail;
         return g_msg.c_str();
     }
     return base;

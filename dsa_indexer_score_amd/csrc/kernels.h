@@ -93,6 +93,12 @@ hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, const ScoreS
 hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream);
 int dense_segment_keys();
 
+// Scratch of the no-allocation entry point: a static device array of
+// noalloc_scratch_bytes() bytes per GPU; noalloc_scratch gives its device
+// address on `device`, which must be the current device.
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(int device, void **ptr);
+
 hipError_t launch_pair_overlap(const int32_t *idx, const int32_t *valid_len, int64_t npairs,
                                int W, int32_t *shared, hipStream_t stream);
 

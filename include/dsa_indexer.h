@@ -159,6 +159,28 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
                        size_t workspace_bytes, void *stream);
 
 /*
+ * indexer_score_topk without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Scratch space comes from a static
+ * device array of the library, 256 MiB on every GPU the library runs on,
+ * held until the process ends.  Arguments, results and errors are those of
+ * indexer_score_topk (same kernels, bit-identical results); the launches
+ * are sized to fit the array: the few-query path in passes of the rows it
+ * holds when one row fits, else streaming launches of at most the rows it
+ * holds (and at most query_chunk).  A problem that fits neither way (only
+ * possible with IDX_SCREEN and more than about 66 million keys) returns
+ * IDX_EWORKSPACE before any HIP call, and indexer_strerror names the limit.
+ * No call allocates or frees memory.  Every call on one GPU uses that GPU's
+ * array, so calls that may overlap on one GPU (several streams, or threads
+ * without ordering) race and must be serialised by the caller.
+ */
+int indexer_score_topk_noalloc(indexer_t h, const void *q, const float *q_scale, const float *w,
+                               int64_t w_stride_s, const void *k, const float *k_scale,
+                               int64_t S, int64_t T, int H, int d, int m, int topk, int causal,
+                               int64_t q_pos0, int32_t *idx, int32_t *valid_len,
+                               float *sel_score, void *stream);
+
+/*
  * Packed documents ("varlen"; GLM-5.3-Flash Module 06 "DSA & KPool", section
  * 3: a pool may not span a document boundary, and one document's tokens may
  * not influence another document's selection).  The same operation as

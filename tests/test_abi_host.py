@@ -353,3 +353,28 @@ def test_library_was_built_from_these_sources():
     from dsa_indexer_score_amd import build
     lib = _lib.load()
     assert lib.indexer_source_hash().decode() == build.source_hash()
+
+
+def test_noalloc_refuses_what_its_scratch_cannot_hold():
+    """The no-allocation entry sizes its launches to its static scratch; a
+    screened problem whose key norms alone pass it is refused with
+    IDX_EWORKSPACE before any device call (host arithmetic only), and the
+    message names the limit."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check; uses placeholder device addresses")
+    lib = _lib.load()
+    cfg = _lib.IndexerConfig(_lib.IDX_BF16, _lib.IDX_SCREEN, 0, 0)
+    h = ctypes.c_void_p()
+    assert lib.indexer_create(ctypes.byref(cfg), 0, ctypes.byref(h)) == 0
+    fake = ctypes.c_void_p(1 << 20)             # aligned, never dereferenced
+    T = 70_000_000                              # 4 T bytes of key norms > 256 MiB
+    rc = lib.indexer_score_topk_noalloc(h, fake, None, fake, 0, fake, None, 4096, T, 64, 128, 1,
+                                        2048, 0, 0, fake, fake, None, None)
+    assert rc == _lib.IDX_EWORKSPACE
+    assert "256 MiB" in lib.indexer_strerror(rc).decode()
+    # invalid arguments are reported as such, not as a workspace problem
+    rc = lib.indexer_score_topk_noalloc(h, fake, None, fake, 0, fake, None, 4096, T, 64, 128, 1,
+                                        2048, 2, 0, fake, fake, None, None)
+    assert rc == _lib.IDX_EINVAL
+    lib.indexer_destroy(h)
