@@ -29,15 +29,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "indexer (q,k,head) triples/s + queries/s at S=256K,H=64; % MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 2500.0, "f32": 157.3}  # fp8 codes run on the bf16 MFMA
+# dense MFMA peaks of the instruction the contraction runs on: e4m3 codes
+# widened to bf16 run on the bf16 MFMA, with --fp8-mfma on the fp8 MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRCS = [os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", f) for f in
                ("score_select.hip", "mfma_ops.h", "select_common.h", "kernels.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_select_c4_csa_256k_pmc.md")
 # the one-row decode step of the 1M-token workload (few-query path)
 DECODE_SRCS = [os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", f) for f in
-               ("score_rows.hip", "select_dense.hip", "mfma_ops.h", "select_common.h",
-                "kernels.h")]
+               ("score_rows.hip", "select_few.hip", "score_select.hip", "mfma_ops.h",
+                "select_common.h", "kernels.h")]
 DECODE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "few_query_decode_c5_csa_1m_pmc.md")
 
 
@@ -139,6 +141,67 @@ def cpu_baseline(inp, budget_s, seed, docs=None):
                        f"{cores} available cores)")
 
 
+def host_streamed(args, inp, ix, W, dev):
+    """The workload with q (and its scales) in pinned host memory: each query
+    chunk is uploaded, scored at its absolute position (q_pos0), and its
+    index rows downloaded into pinned host memory, one chunk after another
+    on one stream.  Device memory then holds the keys, one chunk of q and of
+    idx, and one chunk's workspace; the peak is reported beside the step
+    time, which includes the PCIe transfers (so it is never the headline)."""
+    import torch
+    S, chunk = inp.S, inp.query_chunk or inp.S
+    q_h = torch.empty(inp.q.shape, dtype=inp.q.dtype, pin_memory=True)
+    for r0 in range(0, S, 1 << 16):
+        q_h[r0:r0 + (1 << 16)].copy_(inp.q[r0:r0 + (1 << 16)])
+    qs_h = None if inp.q_scale is None else inp.q_scale.to("cpu").pin_memory()
+    idx_h = torch.empty((S, W), dtype=torch.int32, pin_memory=True)
+    vl_h = torch.empty((S,), dtype=torch.int32, pin_memory=True)
+    w = inp.w if inp.w.dim() == 1 else None
+    if w is None:
+        raise SystemExit("--host-streamed takes a broadcast w[H]")
+    inp.q = inp.q_scale = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    H, d = q_h.shape[1], q_h.shape[2]
+    q_d = torch.empty((chunk, H, d), dtype=q_h.dtype, device=dev)
+    qs_d = None if qs_h is None else torch.empty((chunk, H), dtype=torch.float32, device=dev)
+    idx_d = torch.empty((chunk, W), dtype=torch.int32, device=dev)
+    vl_d = torch.empty((chunk,), dtype=torch.int32, device=dev)
+    ws = torch.empty((ix.workspace_bytes(chunk, inp.T, H, d, inp.m, inp.topk),), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        for r0 in range(0, S, chunk):
+            n = min(chunk, S - r0)
+            q_d[:n].copy_(q_h[r0:r0 + n], non_blocking=True)
+            if qs_d is not None:
+                qs_d[:n].copy_(qs_h[r0:r0 + n], non_blocking=True)
+            ix.score_topk(q_d[:n], w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
+                          q_scale=None if qs_d is None else qs_d[:n], k_scale=inp.k_scale,
+                          q_pos0=r0, workspace=ws, out=(idx_d[:n], vl_d[:n], None))
+            idx_h[r0:r0 + n].copy_(idx_d[:n], non_blocking=True)
+            vl_h[r0:r0 + n].copy_(vl_d[:n], non_blocking=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    peak = torch.cuda.max_memory_allocated(dev)
+    print(json.dumps({
+        "metric": "host-streamed indexer step: peak device bytes and PCIe-inclusive time",
+        "workload": inp.name, "S": S, "T": inp.T, "query_chunk": chunk, "steps": args.steps,
+        "ms_per_step": ms, "peak_hbm_bytes_allocated": int(peak),
+        "queries_per_s": S / (ms / 1e3),
+        "transfers_per_step_bytes": int(q_h.numel() * q_h.element_size() +
+                                        (0 if qs_h is None else qs_h.numel() * 4) +
+                                        idx_h.numel() * 4 + vl_h.numel() * 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +228,17 @@ def main():
                          "together, one query row at the end of each (varlen entry point)")
     ap.add_argument("--few-query-rows", type=int, default=None,
                     help="override indexer_config.few_query_rows (negative: never)")
+    ap.add_argument("--S", type=int, default=0, metavar="ROWS",
+                    help="prefill sweep: the workload scaled to ROWS queries (keys follow)")
+    ap.add_argument("--topk", type=int, default=0, help="override the workload's top-k")
+    ap.add_argument("--chunk", type=int, default=0, help="override the query chunk")
+    ap.add_argument("--context", type=int, default=0, metavar="TOKENS",
+                    help="--decode: a context of TOKENS tokens instead of the workload's")
+    ap.add_argument("--host-streamed", action="store_true",
+                    help="q in pinned host memory, uploaded per query chunk; idx chunks "
+                         "downloaded: reports peak device bytes and the PCIe-inclusive time")
+    ap.add_argument("--fp8-mfma", action="store_true",
+                    help="e4m3 workloads: contract the codes on the fp8 MFMA (IDX_FP8_MFMA)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="few-query shape: N query rows at the end of the workload's full "
                          "context (every key visible), timed through the few-query path")
@@ -193,11 +267,16 @@ def main():
         inp = replace(inp, query_chunk=None)
     elif args.decode:
         from dataclasses import replace
-        full_T = gen.CONFIGS[args.workload]["T"]
+        m = gen.CONFIGS[args.workload]["m"]
+        full_T = args.context // m if args.context else gen.CONFIGS[args.workload]["T"]
         inp = gen.generate(args.workload, S=args.decode, T=full_T, device=dev, **over)
         inp = replace(inp, q_pos0=full_T * inp.m - args.decode, query_chunk=None)
     else:
-        inp = gen.generate(args.workload, device=dev, **over)
+        inp = gen.generate(args.workload, S=args.S or None, topk=args.topk or None,
+                           device=dev, **over)
+    if args.chunk:
+        from dataclasses import replace
+        inp = replace(inp, query_chunk=args.chunk)
     torch.cuda.synchronize()
     log(f"bench: generated {args.workload} S={inp.S} T={inp.T} H={inp.H} d={inp.d} m={inp.m} "
         f"topk={inp.topk} dtype={inp.dtype} chunk={inp.query_chunk} in "
@@ -208,7 +287,7 @@ def main():
         few = args.few_query_rows
     ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail,
                       query_chunk=inp.query_chunk or 0, few_query_rows=few,
-                      screen=args.screen, device=dev)
+                      screen=args.screen, fp8_mfma=args.fp8_mfma, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
     ksel = inp.topk // inp.m if inp.expand else inp.topk
     docs = None
@@ -241,6 +320,9 @@ def main():
                     cu_q_host=cu_q, cu_k_host=cu_k, pos0_host=pos0,
                     cu_tok_host=cu_tok if inp.expand else None,
                     pairs=B * (min(T_doc, T_doc * inp.m // inp.m) if inp.causal else T_doc))
+    if args.host_streamed:
+        host_streamed(args, inp, ix, W, dev)
+        return
     idx = torch.empty((inp.S, W), dtype=torch.int32, device=dev)
     vl = torch.empty((inp.S,), dtype=torch.int32, device=dev)
     # packed documents: the longest document's keys bound the dense rows
@@ -316,7 +398,11 @@ def main():
     n_launch = math.ceil(inp.S / (inp.query_chunk or inp.S))
     score_s = float(np.mean(score_ms)) / 1e3
     achieved_tflops = flops / score_s / 1e12
-    peak = PEAK_TFLOPS[inp.dtype]
+    # the instruction the contraction runs on, and its dense peak
+    mfma_dtype = {"bf16": "bf16", "f32": "f32",
+                  "fp8": "fp8" if args.fp8_mfma and inp.d in (64, 128) and not args.screen
+                  else "bf16"}[inp.dtype]
+    peak = PEAK_TFLOPS[mfma_dtype]
     traffic = stored_traffic() if not (args.decode or args.decode_batch or args.varlen or
                                        args.screen) else None
 
@@ -363,11 +449,14 @@ def main():
                 "traffic": None if traffic is None else traffic,
                 "kernel": "score_select", "flops_per_launch": flops / n_launch,
                 "avg_launch_ms": score_s * 1e3 / n_launch,
-                # the MFMA the contraction runs on (e4m3 codes widen exactly to bf16)
-                "mfma_dtype": {"bf16": "bf16", "fp8": "bf16", "f32": "f32"}[inp.dtype]}
+                "mfma_dtype": mfma_dtype}
+    if inp.dtype == "fp8":
+        # the fp8 workloads' target is the fp8 dense peak, whatever MFMA runs
+        roofline["frac_of_fp8_peak"] = achieved_tflops / PEAK_TFLOPS["fp8"]
     if args.decode or args.decode_batch:
-        # Few-query step (dense scoring + candidate filter + exact cut): bound
-        # by reading the key set once from HBM.
+        # Few-query step (sampled estimate, scoring with sparse write-back,
+        # exact cut, repair launch): bound by reading the key set once from
+        # HBM.
         esz = {"bf16": 2, "fp8": 1, "f32": 4}[inp.dtype]
         W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
         alg_bytes = (inp.T * inp.d * esz + inp.S * inp.H * inp.d * esz + inp.w.numel() * 4 +
@@ -379,7 +468,8 @@ def main():
             dtraffic = stored_traffic(DECODE_PMC_SUMMARY, DECODE_SRCS, "traffic_bytes_per_step")
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": gbs / HBM_PEAK_GBS, "traffic": dtraffic,
-                    "kernel": "few-query step (dense scoring, candidate filter, exact cut)",
+                    "kernel": "few-query step (sample, estimate, filtered scoring, cut, "
+                              "repair)",
                     "bytes_per_launch": alg_bytes, "avg_launch_ms": score_s * 1e3,
                     "mfma_frac": achieved_tflops / peak}
     result = {
@@ -399,6 +489,7 @@ def main():
                    "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
                    inp.query_chunk, "launches_per_step": n_launch, "screen": bool(args.screen),
                    "wdist": inp.meta.get("wdist"), "graph": bool(args.graph),
+                   "fp8_mfma": bool(args.fp8_mfma),
                    "parallelism": "none (1 GPU)"},
         "queries_per_s": inp.S / (ms_per_step / 1e3),
         "mfma_frac": achieved_tflops / peak,

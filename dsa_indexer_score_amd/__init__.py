@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import IDX_BF16, IDX_EXPAND, IDX_F32, IDX_FP8_E4M3, IDX_SCREEN, IDX_TAIL  # noqa: F401
+from ._lib import (IDX_BF16, IDX_EXPAND, IDX_F32, IDX_FP8_E4M3, IDX_FP8_MFMA,  # noqa: F401
+                   IDX_SCREEN, IDX_TAIL)
 
 __all__ = ["Indexer", "score_topk", "output_width", "pair_overlap", "overlap_summary",
            "library_path"]
@@ -29,9 +30,9 @@ def library_path() -> str:
     return _lib.LIB_PATH
 
 
-def _flags(expand: bool, tail: bool, screen: bool = False) -> int:
+def _flags(expand: bool, tail: bool, screen: bool = False, fp8_mfma: bool = False) -> int:
     return (IDX_EXPAND if expand else 0) | (IDX_TAIL if tail else 0) | \
-        (IDX_SCREEN if screen else 0)
+        (IDX_SCREEN if screen else 0) | (IDX_FP8_MFMA if fp8_mfma else 0)
 
 
 def output_width(topk: int, m: int = 1, expand: bool = False, tail: bool = False) -> int:
@@ -53,12 +54,13 @@ class Indexer:
     """A library handle: element dtype, output mode, rows per streaming
     launch (0: as many as 4 GiB of candidate buffers hold), the row count at
     or below which the few-query path runs (0: the library's default,
-    negative: never) and DoSA certificate screening of the streaming path
-    (screen=True; used when 33 <= H <= 64)."""
+    negative: never), DoSA certificate screening of the streaming path
+    (screen=True; used when 33 <= H <= 64) and, for e4m3 inputs, the
+    contraction on the fp8 MFMA (fp8_mfma=True; d = 64 or 128, unscreened)."""
 
     def __init__(self, dtype: torch.dtype, *, expand: bool = False, tail: bool = False,
                  query_chunk: int = 0, few_query_rows: int = 0, screen: bool = False,
-                 device=None):
+                 fp8_mfma: bool = False, device=None):
         if dtype not in _DTYPE_CODE:
             raise TypeError(f"unsupported dtype {dtype}")
         dev = torch.device("cuda") if device is None else torch.device(device)
@@ -69,7 +71,8 @@ class Indexer:
         self.query_chunk = int(query_chunk or 0)
         self.few_query_rows = int(few_query_rows or 0)
         self.screen = bool(screen)
-        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail, screen),
+        self.fp8_mfma = bool(fp8_mfma)
+        cfg = _lib.IndexerConfig(_DTYPE_CODE[dtype], _flags(expand, tail, screen, fp8_mfma),
                                  self.query_chunk, self.few_query_rows)
         h = ctypes.c_void_p()
         lib = _lib.load()
@@ -234,24 +237,25 @@ class Indexer:
 _HANDLES = {}
 
 
-def _handle(dtype, expand, tail, query_chunk, few_query_rows, device, screen=False) -> Indexer:
+def _handle(dtype, expand, tail, query_chunk, few_query_rows, device, screen=False,
+            fp8_mfma=False) -> Indexer:
     key = (dtype, bool(expand), bool(tail), int(query_chunk or 0), int(few_query_rows or 0),
-           bool(screen), str(torch.device(device)))
+           bool(screen), bool(fp8_mfma), str(torch.device(device)))
     h = _HANDLES.get(key)
     if h is None:
         h = _HANDLES[key] = Indexer(dtype, expand=expand, tail=tail, query_chunk=query_chunk,
                                     few_query_rows=few_query_rows, screen=screen,
-                                    device=device)
+                                    fp8_mfma=fp8_mfma, device=device)
     return h
 
 
 def score_topk(q, w, k, *, m: int = 1, topk: int, causal: bool = True, expand: bool = False,
                tail: bool = False, q_scale=None, k_scale=None, q_pos0: int = 0,
                query_chunk: int = 0, few_query_rows: int = 0, screen: bool = False,
-               with_scores: bool = False, workspace=None):
+               fp8_mfma: bool = False, with_scores: bool = False, workspace=None):
     """One indexer step; see Indexer.score_topk."""
     return _handle(q.dtype, expand, tail, query_chunk, few_query_rows, q.device,
-                   screen).score_topk(
+                   screen, fp8_mfma).score_topk(
         q, w, k, m=m, topk=topk, causal=causal, q_scale=q_scale, k_scale=k_scale,
         q_pos0=q_pos0, with_scores=with_scores, workspace=workspace)
 

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa_indexer.so")
 
 IDX_F32, IDX_BF16, IDX_FP8_E4M3 = 0, 1, 2
-IDX_EXPAND, IDX_TAIL, IDX_SCREEN = 1, 2, 4
+IDX_EXPAND, IDX_TAIL, IDX_SCREEN, IDX_FP8_MFMA = 1, 2, 4, 8
 IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_EWORKSPACE, IDX_EHIP = 0, -1, -2, -3, -4
 
 

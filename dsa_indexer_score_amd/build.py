@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdsa_indexer.so")
-SOURCES = ["score_select.hip", "score_rows.hip", "screen_cert.hip", "select_dense.hip",
+SOURCES = ["score_select.hip", "score_rows.hip", "screen_cert.hip", "select_few.hip",
            "pair_overlap.hip", "noalloc.hip", "indexer_api.cpp"]
 
 # Per-file extra flags.  The scoring kernel assumes finite inputs (a documented

@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/dsa_indexer.h: argument checks,
 // output-width and workspace arithmetic, the query-chunk loop and launches.
 // Nothing here computes scores or selections; every step of the indexer runs
-// in the HIP kernels (score_select.hip, score_rows.hip, select_dense.hip,
+// in the HIP kernels (score_select.hip, score_rows.hip, select_few.hip,
 // pair_overlap.hip).
 #include <hip/hip_runtime.h>
 
@@ -33,6 +33,7 @@ int fail_hip(hipError_t e)
     return IDX_EHIP;
 }
 
+constexpr int kAllFlags = IDX_EXPAND | IDX_TAIL | IDX_SCREEN | IDX_FP8_MFMA;
 constexpr int64_t kMaxSel = 16000;  // 16-bit histogram counters bound the buffer at 65535
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -89,48 +90,52 @@ constexpr int64_t kFewRowsDefault = 1024;
 // among a block's 8 rows: there the default stays at 64 rows unless there
 // are at most two rows per document (batched decode).
 constexpr int64_t kFewRowsDocsDefault = 64;
-constexpr int64_t kDenseMaxBytes = int64_t(1) << 32;
+constexpr int64_t kFewMaxBytes = int64_t(1) << 32;
 constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
 constexpr int64_t kRowsKernelMax = 2;  // rows scored with q in registers, keys from HBM
 
-int64_t dense_stride(int64_t T) { return round_up(std::max<int64_t>(T, 1), 4); }
-
-// Few-query workspace: the rows' dense scores [S, stride] (f32), the
-// per-row threshold estimates [S] (u32), the candidate counts [S, nseg]
-// (i32) and the candidates [S, nseg, segment] of (score bits, key), each
-// 256-byte aligned.
-struct DenseLayout {
-    int64_t stride, nseg, est, cnt, key, bytes;
-    DenseLayout(int64_t S, int64_t T)
+// Few-query workspace for R rows of at most Tk keys each: the rows' key
+// samples [R, kSampleKeys] (f32), threshold estimates [R] (u32), candidate
+// sub-list counts [R, kFewSub] (u32), repair marks [R] (i32), the directory
+// of candidate batches [R, nbatch] of (offset, count), and the candidate
+// sub-lists [R, cap] of (score bits, key), each 256-byte aligned.  cap also holds the
+// streaming kernel's candidates when a row goes to the repair launch.  No
+// part holds a score per key: the directory has one entry per kFewBatch
+// keys, everything else is per row.
+struct FewLayout {
+    int64_t nbatch, cap, est, cnt, stat, dir, cand, bytes;
+    FewLayout(int64_t R, int64_t Tk, int64_t ksel)
     {
-        const int64_t seg = dsai::dense_segment_keys();
-        stride = dense_stride(T);
-        nseg = (std::max<int64_t>(T, 1) + seg - 1) / seg;
-        est = round_up(S * stride * 4, 256);
-        cnt = est + round_up(S * 4, 256);
-        key = cnt + round_up(S * nseg * 4, 256);
-        bytes = key + S * nseg * seg * 8;
+        nbatch = (std::max<int64_t>(Tk, 1) + dsai::kFewBatch - 1) / dsai::kFewBatch;
+        cap = std::max<int64_t>(dsai::kFewSub * dsai::kFewSubCap, capacity(ksel, Tk));
+        est = round_up(R * dsai::kSampleKeys * 4, 256);
+        cnt = est + round_up(R * 4, 256);
+        stat = cnt + round_up(R * dsai::kFewSub * 4, 256);
+        dir = stat + round_up(R * 4, 256);
+        cand = dir + round_up(R * nbatch * 8, 256);
+        bytes = cand + R * cap * 8;
     }
 };
 
 // Few-query path: at most the configured number of rows (ndoc < 0: a plain
-// call, else the packed documents' count), and one row's visible scores
-// (and the selection's scratch) fit a dense workspace.
-bool use_dense(const indexer_config &cfg, int64_t S, int64_t T, int64_t ndoc = -1)
+// call, else the packed documents' count), and one row's layout fits.
+bool use_few(const indexer_config &cfg, int64_t S, int64_t T, int64_t ksel, int64_t ndoc = -1)
 {
     int64_t lim = cfg.few_query_rows;
     if (lim == 0) lim = ndoc < 0 || S <= 2 * ndoc ? kFewRowsDefault : kFewRowsDocsDefault;
-    return lim > 0 && S <= lim && S <= 65535 && DenseLayout(1, T).bytes <= kDenseMaxBytes;
+    return lim > 0 && S <= lim && S <= 65535 && FewLayout(1, T, ksel).bytes <= kFewMaxBytes;
 }
 
 // Rows per few-query pass: all S while the workspace stays within 4 GiB,
 // else as many as fit (the rows are then taken in several passes).
-int64_t dense_rows(int64_t S, int64_t T)
+int64_t few_rows(int64_t S, int64_t T, int64_t ksel)
 {
-    const int64_t per_row = DenseLayout(1, T).bytes;
-    int64_t r = std::max<int64_t>(1, std::min<int64_t>(S, kDenseMaxBytes / per_row));
-    while (r > 1 && DenseLayout(r, T).bytes > kDenseMaxBytes) --r;
-    return r;
+    int64_t lo = 1, hi = std::max<int64_t>(S, 1);  // largest r whose layout fits
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (FewLayout(mid, T, ksel).bytes <= kFewMaxBytes) lo = mid; else hi = mid - 1;
+    }
+    return lo;
 }
 
 // Screening (IDX_SCREEN) on the streaming path: needs two head blocks.
@@ -161,7 +166,7 @@ struct StreamLayout {
 int64_t workspace_need(const indexer_config &cfg, int64_t S, int64_t T, int H, int64_t ksel,
                        int64_t pmax)
 {
-    if (use_dense(cfg, S, T)) return DenseLayout(dense_rows(S, T), T).bytes;
+    if (use_few(cfg, S, T, ksel)) return FewLayout(few_rows(S, T, ksel), T, ksel).bytes;
     return StreamLayout(rows_per_launch(cfg, S, capacity(ksel, T)), capacity(ksel, pmax), T,
                         use_screen(cfg, H)).bytes;
 }
@@ -194,7 +199,7 @@ int indexer_create(const indexer_config *cfg, int device, indexer_t *out)
 {
     if (!cfg || !out || device < 0) return IDX_EINVAL;
     if (!dtype_ok(cfg->dtype)) return IDX_EINVAL;
-    if (cfg->flags & ~(IDX_EXPAND | IDX_TAIL | IDX_SCREEN)) return IDX_EINVAL;
+    if (cfg->flags & ~kAllFlags) return IDX_EINVAL;
     if ((cfg->flags & IDX_TAIL) && !(cfg->flags & IDX_EXPAND)) return IDX_EINVAL;
     if (cfg->query_chunk < 0) return IDX_EINVAL;
     indexer_s *h = new (std::nothrow) indexer_s;
@@ -213,7 +218,7 @@ int indexer_destroy(indexer_t h)
 
 int indexer_output_width(int topk, int m, int flags, int *W)
 {
-    if (!W || topk < 1 || m < 1 || (flags & ~(IDX_EXPAND | IDX_TAIL | IDX_SCREEN)))
+    if (!W || topk < 1 || m < 1 || (flags & ~kAllFlags))
         return IDX_EINVAL;
     if ((flags & IDX_TAIL) && !(flags & IDX_EXPAND)) return IDX_EINVAL;
     if ((flags & IDX_EXPAND) && topk % m) return IDX_EINVAL;
@@ -243,10 +248,10 @@ struct Docs {  // packed-document layout (varlen); on = false: one document
     const int32_t *cu_q = nullptr, *cu_k = nullptr, *cu_tok = nullptr;
     const int64_t *pos0 = nullptr;
     int ndoc = 0;
-    int64_t row_keys = 0;  // keys per dense row of the few-query path
+    int64_t row_keys = 0;  // keys per row of the few-query path
 };
 
-// Keys per dense row for packed documents: the caller's bound on a
+// Keys per few-query row for packed documents: the caller's bound on a
 // document's keys (0: unknown), at most T.
 int64_t doc_row_keys(int64_t max_doc_keys, int64_t T)
 {
@@ -310,23 +315,23 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     const int64_t pmax = causal && !docs.on ? std::min<int64_t>(T, (q_pos0 + S) / m) : T;
     const int64_t cap = capacity(ksel, pmax);
     int64_t rows = rows_per_launch(cfg, S, capacity(ksel, T));
-    const int64_t Tk = docs.on ? docs.row_keys : T;  // scores per dense row
-    bool dense = use_dense(cfg, S, Tk, docs.on ? docs.ndoc : -1);
-    int64_t dense_R = dense ? dense_rows(S, Tk) : 0;  // rows per few-query pass
-    bool screen = !docs.on && !dense && use_screen(cfg, H);
+    const int64_t Tk = docs.on ? docs.row_keys : T;  // keys per few-query row
+    bool few = use_few(cfg, S, Tk, ksel, docs.on ? docs.ndoc : -1);
+    int64_t few_R = few ? few_rows(S, Tk, ksel) : 0;  // rows per few-query pass
+    bool screen = !docs.on && !few && use_screen(cfg, H);
     size_t need =
-        dense     ? (size_t)DenseLayout(dense_R, Tk).bytes
+        few     ? (size_t)FewLayout(few_R, Tk, ksel).bytes
         : docs.on ? (size_t)(rows * cap * (int64_t)sizeof(uint2))
                   : (size_t)workspace_need(cfg, S, T, H, ksel, pmax);
     if (fit_bytes > 0) {
-        if (dense) {
-            dense_R = std::min(dense_R, rows_that_fit(S, fit_bytes, [&](int64_t r) {
-                                   return DenseLayout(r, Tk).bytes;
+        if (few) {
+            few_R = std::min(few_R, rows_that_fit(S, fit_bytes, [&](int64_t r) {
+                                   return FewLayout(r, Tk, ksel).bytes;
                                }));
-            if (dense_R < 1) dense_R = 0, dense = false;
+            if (few_R < 1) few_R = 0, few = false;
         }
-        screen = !docs.on && !dense && use_screen(cfg, H);
-        if (!dense) {
+        screen = !docs.on && !few && use_screen(cfg, H);
+        if (!few) {
             const bool scr = screen;
             rows = std::min(rows, rows_that_fit(S, fit_bytes, [&](int64_t r) {
                                 return StreamLayout(r, cap, T, scr).bytes;
@@ -337,7 +342,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
                 return IDX_EWORKSPACE;
             }
         }
-        need = dense ? (size_t)DenseLayout(dense_R, Tk).bytes
+        need = few ? (size_t)FewLayout(few_R, Tk, ksel).bytes
                      : (size_t)StreamLayout(rows, cap, T, screen).bytes;
     }
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return IDX_EWORKSPACE;
@@ -376,24 +381,35 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
     p.varlen = docs.on;
     const int nb = (H + 31) / 32;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dense) {
-        // Few-query path: all CUs score the rows' key ranges into the dense
-        // workspace, then the selection runs per row (estimate), per
-        // (row, key segment) (candidate filter) and per row (exact cut); in
-        // passes of as many rows as the workspace holds.
-        // equal passes (each at most the R rows the workspace holds)
-        const int64_t R = dense_R;
-        const DenseLayout L(R, Tk);
+    // element type the scoring kernels take: e4m3 on the fp8 MFMA when asked
+    // for (d = 64, 128, unscreened), else the handle's dtype
+    const int kdt = cfg.dtype == IDX_FP8_E4M3 && (flags & IDX_FP8_MFMA) && !screen &&
+                            (d == 64 || d == 128)
+                        ? 3 : cfg.dtype;
+    if (few) {
+        // Few-query path, in equal passes of at most the R rows the workspace
+        // holds: all CUs score a sample of each row's keys; one block per
+        // row cuts a threshold estimate from it; all CUs score the rows'
+        // keys again and append only the keys at or above the estimate; one
+        // block per row cuts the exact selection from those candidates and
+        // writes the row, or marks it when they cannot hold the selection;
+        // the streaming kernel then selects the marked rows (a launch whose
+        // blocks return at once when no row of theirs is marked).
+        const int64_t R = few_R;
+        const FewLayout L(R, Tk, ksel);
         const int64_t npass = (S + R - 1) / R;
         const int64_t Rp = npass > 0 ? (S + npass - 1) / npass : R;
         char *base = static_cast<char *>(workspace);
-        p.ws = nullptr;
-        p.scores = reinterpret_cast<float *>(base);
-        p.sstride = L.stride;
+        p.samp = reinterpret_cast<float *>(base);
         p.est = reinterpret_cast<uint32_t *>(base + L.est);
-        p.seg_cnt = reinterpret_cast<int32_t *>(base + L.cnt);
-        p.seg_buf = reinterpret_cast<uint2 *>(base + L.key);
-        p.nseg = (int)L.nseg;
+        p.fq_cnt = reinterpret_cast<uint32_t *>(base + L.cnt);
+        p.status = reinterpret_cast<int32_t *>(base + L.stat);
+        p.fq_dir = reinterpret_cast<uint2 *>(base + L.dir);
+        p.ws = reinterpret_cast<uint2 *>(base + L.cand);
+        p.cap = (int)L.cap;
+        p.nbatch = L.nbatch;
+        p.row_keys = Tk;
+        p.split_keys = round_up(std::max<int64_t>(T, 1), dsai::kFewBatch);
         for (int64_t r0 = 0; r0 < S; r0 += Rp) {
             p.row0 = r0;
             p.nrows = std::min(Rp, S - r0);
@@ -403,19 +419,35 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
             const int64_t tiles = (std::max<int64_t>(pm, 1) + dsai::kKeysPerTile - 1) /
                                   dsai::kKeysPerTile;
             const int64_t want = std::max<int64_t>(1, (kFillBlocks + groups - 1) / groups);
-            const int64_t tiles_per = (tiles + std::min(want, tiles) - 1) / std::min(want, tiles);
+            int64_t tiles_per = (tiles + std::min(want, tiles) - 1) / std::min(want, tiles);
+            tiles_per = round_up(tiles_per, dsai::kFewBatch / dsai::kKeysPerTile);  // whole batches
+            bool supported = true;
+            hipError_t e = dsai::launch_score_rows(kdt, nb, d, docs.on, true, p, st,
+                                                   &supported);
+            if (!supported) return IDX_EUNSUPPORTED;
+            if (e != hipSuccess) return fail_hip(e);
+            e = dsai::launch_few_estimate(p, st);
+            if (e != hipSuccess) return fail_hip(e);
+            // one or two rows, or packed documents (each row its own key
+            // window): the rows kernel; else query groups x key ranges
             p.split_keys = tiles_per * dsai::kKeysPerTile;
             p.nsplit = (int)((tiles + tiles_per - 1) / tiles_per);
-            bool supported = true;
-            // packed documents: every row its own key window, one row per slab
-            hipError_t e =
-                p.nrows <= kRowsKernelMax || docs.on
-                    ? dsai::launch_score_rows(cfg.dtype, nb, d, docs.on, p, st, &supported)
-                    : dsai::launch_score_select(cfg.dtype, nb, d, true, false, false, p, st,
+            e = p.nrows <= kRowsKernelMax || docs.on
+                    ? dsai::launch_score_rows(kdt, nb, d, docs.on, false, p, st, &supported)
+                    : dsai::launch_score_select(kdt, nb, d, true, false, false, p, st,
                                                 &supported);
             if (!supported) return IDX_EUNSUPPORTED;
             if (e != hipSuccess) return fail_hip(e);
-            e = dsai::launch_select_dense(p, st);
+            e = dsai::launch_few_finish(p, st);
+            if (e != hipSuccess) return fail_hip(e);
+            // repair: the marked rows through the streaming selection
+            dsai::ScoreSelectParams pr = p;
+            pr.repair = p.status;
+            pr.nsplit = 1;
+            pr.split_keys = round_up(std::max<int64_t>(T, 1), dsai::kFewBatch);
+            e = dsai::launch_score_select(kdt, nb, d, false, docs.on, false, pr, st,
+                                          &supported);
+            if (!supported) return IDX_EUNSUPPORTED;
             if (e != hipSuccess) return fail_hip(e);
         }
         return IDX_OK;
@@ -445,7 +477,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
             if (!supported) return IDX_EUNSUPPORTED;
             if (e != hipSuccess) return fail_hip(e);
         }
-        e = dsai::launch_score_select(cfg.dtype, nb, d, false, docs.on, screen, p, st, &supported);
+        e = dsai::launch_score_select(kdt, nb, d, false, docs.on, screen, p, st, &supported);
         if (!supported) return IDX_EUNSUPPORTED;
         if (e != hipSuccess) return fail_hip(e);
     }
@@ -506,7 +538,7 @@ int indexer_workspace_bytes_varlen(indexer_t h, int64_t S, int64_t T, int H, int
     const int64_t stream_bytes = rows_per_launch(h->cfg, S, capacity(ksel, T)) *
                                  capacity(ksel, T) * 8;
     const int64_t Tk = doc_row_keys(max_doc_keys, T);
-    *bytes = (size_t)(use_dense(h->cfg, S, Tk, ndoc) ? DenseLayout(dense_rows(S, Tk), Tk).bytes
+    *bytes = (size_t)(use_few(h->cfg, S, Tk, ksel, ndoc) ? FewLayout(few_rows(S, Tk, ksel), Tk, ksel).bytes
                                                       : stream_bytes);
     return IDX_OK;
 }

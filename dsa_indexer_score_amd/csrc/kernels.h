@@ -29,12 +29,31 @@ struct ScoreSelectParams {
     float *sel_score;       // [S, W] or null
     uint2 *ws;              // candidate buffers, [nrows, cap] of (score bits, key)
     int cap;                // candidate slots per query
-    // Dense mode (few queries): scores of each row's visible keys are written
-    // to scores[row * sstride + key] instead of being selected in the kernel.
-    float *scores;
-    int64_t sstride;
+    // Few-query mode (decode, small batches): the rows' keys are split over
+    // all CUs; every key is scored once and only the (score bits, key) pairs
+    // at or above the row's threshold estimate are appended to the row's
+    // candidates ws[row * cap ...], one contiguous run per batch of kFewBatch
+    // keys: batch b goes to sub-list b % kFewSub (kFewSubCap slots at
+    // (b % kFewSub) * kFewSubCap), reserved with one atomic on that
+    // sub-list's count fq_cnt[row * kFewSub + b % kFewSub] -- so concurrent
+    // appends of one row spread over kFewSub counters; fq_dir[row * nbatch +
+    // b] = (offset in the sub-list, count) of batch b.
+    // samp[row * kSampleKeys ...] holds the exact scores of a key sample from
+    // which est[row] is estimated; status[row] = 1 leaves the row to the
+    // streaming kernel (repair).  row_keys bounds the keys of a row (packed
+    // documents: the caller's max_doc_keys); nbatch = its batches.
+    float *samp;
+    uint32_t *est;
+    uint32_t *fq_cnt;
+    uint2 *fq_dir;
+    int32_t *status;
+    int64_t row_keys;
+    int64_t nbatch;
+    // Streaming kernel: when non-null, only rows with repair[row] != 0 are
+    // scored and written (the few-query path's rows whose estimate failed).
+    const int32_t *repair;
     int nsplit;             // key ranges per query group; grid = groups * nsplit
-    int64_t split_keys;     // keys per range, a multiple of kKeysPerTile
+    int64_t split_keys;     // keys per range, a multiple of kFewBatch
     // Packed documents (varlen): rows [cu_q[i], cu_q[i+1]) are document i,
     // whose keys are k[cu_k[i], cu_k[i+1]); pos0[i] (or 0) is the position of
     // its first row within the document; expanded outputs are cu_tok[i] +
@@ -45,14 +64,6 @@ struct ScoreSelectParams {
     const int32_t *cu_tok;
     int ndoc;
     int varlen;             // 1: rows are packed documents (the fields above)
-    // Few-query selection scratch (dense mode): per-row threshold estimate,
-    // per (row, segment of dense_segment_keys() keys) candidate counts and
-    // candidates as (score bits, key) (nseg segments per row,
-    // dense_segment_keys() slots each).
-    uint32_t *est;
-    int32_t *seg_cnt;
-    uint2 *seg_buf;
-    int nseg;
     // Screening (DoSA certificates), per row of the launch: head order with
     // the kept heads first [nrows, 64] (-1 = no head), weights w * q_scale in
     // that order [nrows, 64], folded bound weights of the kept heads
@@ -67,10 +78,17 @@ struct ScoreSelectParams {
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
 constexpr int kKeysPerTile = 128;     // keys staged in LDS per step
 constexpr int kSelGroup = 64;         // keys appended per selection step (one per lane)
+constexpr int kFewBatch = 256;        // few-query: keys per candidate run (directory entry)
+constexpr int kSampleKeys = 8192;     // few-query: keys in a row's estimate sample
+constexpr int kFewCap = 8192;         // few-query: candidates the exact cut holds in LDS
+constexpr int kFewSub = 32;           // few-query: candidate sub-lists per row (batch b: b % 32)
+constexpr int kFewSubCap = 1024;      // few-query: entries per sub-list
 
-// dtype codes match enum idx_dtype; dense = write scores (p.scores) instead
+// dtype codes match enum idx_dtype, plus 3 = e4m3 on the fp8 MFMA (d = 64,
+// 128; not screened); few = few-query mode (blocks over
+// (query group, key range), candidates appended as described above) instead
 // of selecting; varlen = rows and keys are packed documents (p.cu_q ...)
-hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen, bool screen,
+hipError_t launch_score_select(int dtype, int nb, int d, bool few, bool varlen, bool screen,
                                const ScoreSelectParams &p, hipStream_t stream, bool *supported);
 
 // DoSA certificates of rows [p.row0, p.row0 + p.nrows) into p.cert_* (one
@@ -80,18 +98,21 @@ hipError_t launch_certificates(int dtype, int d, const ScoreSelectParams &p, hip
 hipError_t launch_key_norms(int dtype, int d, const ScoreSelectParams &p, hipStream_t stream,
                             bool *supported);
 
-// Dense scores of one or two rows (p.scores, as the dense mode of
-// launch_score_select writes them, bit for bit), every CU streaming its own
-// slice of the keys; varlen: any number of packed-document rows, one per
-// slab, each row's scores over its own key window.
-hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, const ScoreSelectParams &p,
-                             hipStream_t stream, bool *supported);
+// Few-query scoring with q in registers and keys straight from memory,
+// every CU streaming its own slice of the keys: sample = the exact scores of
+// each row's key sample (p.samp); otherwise one or two rows (or, varlen, any
+// number of packed-document rows, one per slab, each over its own key
+// window) scored and filtered into candidates as the few-query mode of
+// launch_score_select does, bit for bit.
+hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, bool sample,
+                             const ScoreSelectParams &p, hipStream_t stream, bool *supported);
 
-// Exact top-k of each row's dense scores and its canonical output row:
-// threshold estimate per row, candidate filter per (row, key chunk), exact
-// cut and output per row.
-hipError_t launch_select_dense(const ScoreSelectParams &p, hipStream_t stream);
-int dense_segment_keys();
+// Few-query selection: the threshold estimate of each row from its sample
+// (and the zeroing of its candidate count), before the filtering scoring
+// launch; the exact cut and canonical output row of each row from its
+// candidates (or status = 1 for the repair launch), after it.
+hipError_t launch_few_estimate(const ScoreSelectParams &p, hipStream_t stream);
+hipError_t launch_few_finish(const ScoreSelectParams &p, hipStream_t stream);
 
 // Scratch of the no-allocation entry point: a static device array of
 // noalloc_scratch_bytes() bytes per GPU; noalloc_scratch gives its device

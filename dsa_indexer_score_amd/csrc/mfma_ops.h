@@ -2,9 +2,9 @@
 //
 // Query rows are the A operand (32 heads per block of rows), key rows the B
 // operand (32 keys per block of columns), the d axis the contraction; the
-// three element types feed v_mfma_f32_32x32x16_bf16 (bf16, and OCP e4m3
-// widened exactly to bf16) or v_mfma_f32_32x32x2_f32 (fp32) with fp32
-// accumulation.  Every kernel that uses these operands with the same
+// element types feed v_mfma_f32_32x32x16_bf16 (bf16, and OCP e4m3 widened
+// exactly to bf16), v_mfma_f32_32x32x2_f32 (fp32) with fp32 accumulation, or,
+// when asked for, v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 as it is).  Every kernel that uses these operands with the same
 // instruction order gets bit-identical dot products.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -14,6 +14,7 @@ namespace dsai {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
@@ -40,6 +41,8 @@ __device__ inline void raw_row(const char *row, int hh, uint4 (&raw)[O::RAW])
 template <int D> struct Op<1, D> {  // bf16
     using A = bf16x8;
     static constexpr int ES = 2, KS = D / 16, NCH = D * 2 / 16, GCH = NCH, RAW = KS;
+    static constexpr int CPK = 1;  // 16-byte LDS chunks per operand
+    __device__ static A from_chunks(const uint4 *c) { return __builtin_bit_cast(A, c[0]); }
     __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
     {
         tile[r * NCH + (gch ^ swz)] = v;
@@ -80,6 +83,7 @@ template <int D> struct Op<1, D> {  // bf16
 template <int D> struct Op<2, D> : Op<1, D> {
     using A = bf16x8;
     static constexpr int ES = 1, KS = D / 16, NCH = D * 2 / 16, GCH = D / 16, RAW = KS / 2;
+    static constexpr int CPK = 1;
     template <bool HI> __device__ static uint32_t widen2(uint32_t w)
     {
         auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
@@ -122,9 +126,63 @@ template <int D> struct Op<2, D> : Op<1, D> {
     }
 };
 
+// OCP e4m3 codes contracted as they are on the gfx950 scaled f8f6f4 MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, both formats e4m3, both block scales
+// 2^0), 64 products per instruction.  A lane supplies 32 codes of its row
+// (A) or key (B): the contiguous half d in [hh*D/2, hh*D/2 + D/2) split into
+// KS = D/64 operands, the same slot -> d map for A and B.  Each operand is
+// two 16-byte chunks; keys stay e4m3 in LDS (half the bytes of a widened
+// tile).  The instruction's internal accumulation is narrower than fp32
+// (its products are summed at reduced precision before the fp32 add), so
+// this instance is used only when the caller asks for it.
+template <int D> struct Op<3, D> {
+    static_assert(D % 64 == 0, "one operand covers 32 codes of each lane half");
+    using A = i32x8;
+    static constexpr int ES = 1, KS = D / 64, NCH = D / 16, GCH = NCH, RAW = 2 * KS;
+    static constexpr int CPK = 2;
+    __device__ static A from_chunks(const uint4 *c)
+    {
+        return A{(int)c[0].x, (int)c[0].y, (int)c[0].z, (int)c[0].w,
+                 (int)c[1].x, (int)c[1].y, (int)c[1].z, (int)c[1].w};
+    }
+    __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
+    {
+        tile[r * NCH + (gch ^ swz)] = v;
+    }
+    __device__ static void load_a(const char *row, int hh, A (&a)[KS])
+    {
+        const uint4 *p = reinterpret_cast<const uint4 *>(row + hh * (D / 2));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = from_chunks(p + 2 * ks);
+    }
+    __device__ static void load_b(const uint4 *tile, int r, int hh, int swz, A (&b)[KS])
+    {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load_b_one(tile, r, hh, swz, ks, b[ks]);
+    }
+    __device__ static void load_b_one(const uint4 *tile, int r, int hh, int swz, int ks, A &b)
+    {
+        const uint4 c[2] = {tile[r * NCH + ((hh * 2 * KS + 2 * ks) ^ swz)],
+                            tile[r * NCH + ((hh * 2 * KS + 2 * ks + 1) ^ swz)]};
+        b = from_chunks(c);
+    }
+    __device__ static void from_raw(const uint4 (&raw)[RAW], A (&a)[KS])
+    {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = from_chunks(raw + 2 * ks);
+    }
+    __device__ static f32x16 mma(A a, A b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    }
+    __device__ static A zero() { return A{0, 0, 0, 0, 0, 0, 0, 0}; }
+};
+
 template <int D> struct Op<0, D> {  // fp32
     using A = float;
     static constexpr int ES = 4, KS = D / 2, NCH = D * 4 / 16, GCH = NCH, RAW = KS / 4;
+    static constexpr int CPK = 0;  // operands are single floats (no chunk loads)
+    __device__ static A from_chunks(const uint4 *) { return 0.f; }  // not used
     __device__ static void store_chunk(uint4 *tile, int r, int gch, uint4 v, int swz)
     {
         tile[r * NCH + (gch ^ swz)] = v;

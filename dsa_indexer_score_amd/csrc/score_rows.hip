@@ -1,14 +1,22 @@
-// score_rows: dense scoring of one or two query rows (decode) for gfx950,
-// and of packed-document rows (batched decode: each row its own keys).
+// score_rows: few-query scoring (decode, small batches, batched decode over
+// packed documents) for gfx950.
 //
-// Writes, for every key j visible to row t,
+// Computes, for the keys j visible to row t,
 //     s_tj = sum_h w[t,h] * ReLU(q[t,h,:] . k[j,:])
-// (DoSA: Dots Sparse Attention, summary page, "Prerequisites") into the row's
-// dense score array, which the few-query selection then cuts exactly.  The
-// dot products use the same MFMA operands and instruction order as the fused
-// streaming kernel, and the signed-ReLU head sum the same fma order (head
-// block by head block, accumulator element by element, then the two lane
-// halves, then k_scale), so every score is bit-identical to the one the
+// (DoSA: Dots Sparse Attention, summary page, "Prerequisites") in one of two
+// modes:
+//  * sample: the exact scores of a fixed sample of the row's keys (64
+//    consecutive keys in each of kSampleKeys / 64 places spread over the
+//    row), from which the row's threshold estimate is cut;
+//  * filter: every visible key, keeping only the (score, key) pairs at or
+//    above the row's estimate -- appended to the row's candidate list one
+//    run of kFewBatch keys at a time, with the run's directory entry -- so no
+//    score array is ever written (the DoSA summary's sparse write-back: only
+//    scores that reach the threshold leave the registers).
+// The dot products use the same MFMA operands and instruction order as the
+// fused streaming kernel, and the signed-ReLU head sum the same fma order
+// (head block by head block, accumulator element by element, then the two
+// lane halves, then k_scale), so every score is bit-identical to the one the
 // streaming selection sees.
 //
 // Why a kernel of its own: the streaming kernel's block shares each LDS key
@@ -36,13 +44,18 @@ constexpr int kRowsThreads = kRowsWaves * 64;
 constexpr int kTargetWaves = 1024;
 constexpr int kTargetWavesDocs = 2048;
 
-template <int DT, int NB, int D, int SQ, bool VARLEN>
+constexpr int kBatchGroups = kFewBatch / kSelGroup;     // groups per candidate run
+constexpr int kSampleGroups = kSampleKeys / kSelGroup;  // groups per row sample
+
+template <int DT, int NB, int D, int SQ, bool VARLEN, bool SAMPLE>
 __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectParams p)
 {
     static_assert(!VARLEN || SQ == 1, "packed documents: one row per slab");
+    static_assert(!SAMPLE || SQ == 1, "samples: one row per slab");
     using O = Op<DT, D>;
     using A = typename O::A;
     constexpr int KS = O::KS, ES = O::ES, RAW = O::RAW;
+    constexpr bool kScaled = DT >= 2;  // fp8 codes: per-row scales fold out of the ReLU
     constexpr int64_t ROWB = (int64_t)D * ES;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = lane >> 5, l32 = lane & 31;
@@ -56,20 +69,29 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     for (int i = 0; i < SQ; ++i) {
         const int64_t r = r0 + i;
         if constexpr (VARLEN) {
-            // a window longer than the dense row (the caller's bound on a
+            // a window longer than a row's directory (the caller's bound on a
             // document's keys) is cut to it: every store stays in the row
             const DocWindow dw = r < p.nrows ? doc_window(p, p.row0 + r) : DocWindow{};
-            Pq[i] = dw.P < p.sstride ? dw.P : p.sstride;
+            Pq[i] = dw.P < p.row_keys ? dw.P : p.row_keys;
             klo = dw.klo;
         } else {
             Pq[i] = r < p.nrows ? visible_keys(p.q_pos0 + p.row0 + r, p.T, p.m, p.causal) : 0;
         }
         Pmax = Pq[i] > Pmax ? Pq[i] : Pmax;
     }
-    // the slab's 64-key groups, split evenly over the slab's waves
-    const int64_t ngroups = (Pmax + kSelGroup - 1) / kSelGroup;
+    // sample: rows of at most kFewCap keys need no estimate (all their keys
+    // are candidates); group g starts at key g * spacing
+    int64_t spacing = kSelGroup;
+    if constexpr (SAMPLE) {
+        if (Pmax <= kFewCap) return;
+        spacing = (Pmax - kSelGroup) / (kSampleGroups - 1);
+    }
+    // the slab's 64-key groups, split evenly over the slab's waves in runs
+    // of whole candidate batches
+    const int64_t ngroups = SAMPLE ? kSampleGroups : (Pmax + kSelGroup - 1) / kSelGroup;
     const int64_t nwaves = (int64_t)gridDim.x * kRowsWaves;
-    const int64_t gpw = (ngroups + nwaves - 1) / nwaves;
+    int64_t gpw = (ngroups + nwaves - 1) / nwaves;
+    if (!SAMPLE) gpw = (gpw + kBatchGroups - 1) / kBatchGroups * kBatchGroups;
     const int64_t g0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * gpw;
     if (g0 >= ngroups) return;
     const int64_t g1 = g0 + gpw < ngroups ? g0 + gpw : ngroups;
@@ -100,7 +122,7 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
                 const bool ok = active && h2 < p.H;
                 const int hc = ok ? h2 : 0;
                 float wt = p.w[t * p.w_stride + hc];
-                if (DT == 2) wt *= p.q_scale[t * p.H + hc];
+                if (kScaled) wt *= p.q_scale[t * p.H + hc];
                 wv[i][b][v] = ok ? wt : 0.f;
             }
         }
@@ -118,14 +140,23 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     auto load_group = [&](int64_t g, uint4 (&dst)[2][RAW], float &sc) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int64_t key = klo + g * kSelGroup + 32 * c + l32;
+            const int64_t key = klo + g * spacing + 32 * c + l32;
             raw_row<O, D>(kbytes + (key < p.T ? key : p.T - 1) * ROWB, hh, dst[c]);
         }
-        if (DT == 2) {
-            const int64_t key = klo + g * kSelGroup + lane;
+        if (kScaled) {
+            const int64_t key = klo + g * spacing + lane;
             sc = p.k_scale[key < p.T ? key : p.T - 1];
         }
     };
+    // filter: the rows' estimates, and the scores of the current batch
+    uint32_t est[SQ];
+    float bsc[SQ][kBatchGroups];
+#pragma unroll
+    for (int i = 0; i < SQ; ++i) {
+        est[i] = SAMPLE || r0 + i >= p.nrows ? 0u : p.est[r0 + i];
+#pragma unroll
+        for (int x = 0; x < kBatchGroups; ++x) bsc[i][x] = 0.f;
+    }
 
 #pragma unroll
     for (int a = 0; a < AHEAD; ++a)
@@ -153,7 +184,7 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
                 part[i][c] = e;
             }
         }
-        const int64_t key = g * kSelGroup + lane;  // the key whose score this lane finishes
+        const int gb = (int)(g % kBatchGroups);  // group within its candidate batch
 #pragma unroll
         for (int i = 0; i < SQ; ++i) {
             // lanes < 32 own keys 0..31 of the group, lanes >= 32 keys 32..63:
@@ -162,8 +193,34 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
                                                              __float_as_uint(part[i][1]), false,
                                                              false);
             float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (DT == 2) s *= ksc[0];
-            if (key < Pq[i]) p.scores[(r0 + i) * p.sstride + key] = s;
+            if (kScaled) s *= ksc[0];
+            if constexpr (SAMPLE) {
+                p.samp[(r0 + i) * kSampleKeys + g * kSelGroup + lane] = s;
+            } else {
+#pragma unroll
+                for (int x = 0; x < kBatchGroups; ++x)
+                    if (x == gb) bsc[i][x] = s;
+            }
+        }
+        // the batch is complete: its survivors go to the rows' candidate lists
+        if (!SAMPLE && (gb == kBatchGroups - 1 || g + 1 == g1)) {
+            const int64_t b = g / kBatchGroups;
+#pragma unroll
+            for (int i = 0; i < SQ; ++i) {
+                const int64_t r = r0 + i;
+                if (r >= p.nrows) continue;
+                // a batch ends early only where the slab's keys end (runs are
+                // whole batches): its groups past g are masked off here
+                float sc[kBatchGroups];
+#pragma unroll
+                for (int x = 0; x < kBatchGroups; ++x) sc[x] = x <= gb ? bsc[i][x] : 0.f;
+                const int64_t kend = b * kFewBatch + (gb + 1) * (int64_t)kSelGroup;
+                const int sub = (int)(b % kFewSub);
+                fq_append<kBatchGroups>(sc, b * kFewBatch, Pq[i] < kend ? Pq[i] : kend, est[i],
+                                        p.fq_cnt + r * kFewSub + sub,
+                                        p.ws + r * (int64_t)p.cap + sub * kFewSubCap,
+                                        p.fq_dir + r * p.nbatch + b, lane, kFewSubCap);
+            }
         }
         if (g + 1 < g1) {
 #pragma unroll
@@ -178,13 +235,14 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     }
 }
 
-template <int DT, int NB, int D, int SQ, bool VARLEN>
+template <int DT, int NB, int D, int SQ, bool VARLEN, bool SAMPLE>
 hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
 {
-    // the last row sees the most keys (packed documents: at most a dense row)
+    // the last row sees the most keys (packed documents: at most row_keys)
     const int64_t pmax =
-        VARLEN ? p.sstride : visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
-    const int64_t ngroups = (pmax + kSelGroup - 1) / kSelGroup;
+        VARLEN ? p.row_keys : visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
+    const int64_t ngroups =
+        SAMPLE ? (pmax > kFewCap ? kSampleGroups : 0) : (pmax + kSelGroup - 1) / kSelGroup;
     const int64_t nslab = (p.nrows + SQ - 1) / SQ;
     if (ngroups <= 0 || nslab <= 0) return hipSuccess;
     // about kTargetWaves waves in all, at most one per group of a slab
@@ -192,31 +250,35 @@ hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
     int64_t waves = (target + nslab - 1) / nslab;
     waves = waves < ngroups ? waves : ngroups;
     const int64_t blocks = ((waves + kRowsWaves - 1) / kRowsWaves + 7) / 8 * 8;
-    hipLaunchKernelGGL((score_rows_kernel<DT, NB, D, SQ, VARLEN>),
+    hipLaunchKernelGGL((score_rows_kernel<DT, NB, D, SQ, VARLEN, SAMPLE>),
                        dim3((unsigned)blocks, (unsigned)nslab), dim3(kRowsThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DT, int NB, int D>
-hipError_t launch_sq(const ScoreSelectParams &p, bool varlen, hipStream_t stream)
+hipError_t launch_sq(const ScoreSelectParams &p, bool varlen, bool sample, hipStream_t stream)
 {
-    if (varlen) return launch_rows<DT, NB, D, 1, true>(p, stream);
-    return p.nrows == 1 ? launch_rows<DT, NB, D, 1, false>(p, stream)
-                        : launch_rows<DT, NB, D, 2, false>(p, stream);
+    if (sample)
+        return varlen ? launch_rows<DT, NB, D, 1, true, true>(p, stream)
+                      : launch_rows<DT, NB, D, 1, false, true>(p, stream);
+    if (varlen) return launch_rows<DT, NB, D, 1, true, false>(p, stream);
+    return p.nrows == 1 ? launch_rows<DT, NB, D, 1, false, false>(p, stream)
+                        : launch_rows<DT, NB, D, 2, false, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, const ScoreSelectParams &p,
-                             hipStream_t stream, bool *supported)
+hipError_t launch_score_rows(int dtype, int nb, int d, bool varlen, bool sample,
+                             const ScoreSelectParams &p, hipStream_t stream, bool *supported)
 {
     *supported = true;
 #define DSAI_CASE(DT, NB, D) \
-    if (dtype == DT && nb == NB && d == D) return launch_sq<DT, NB, D>(p, varlen, stream);
+    if (dtype == DT && nb == NB && d == D) return launch_sq<DT, NB, D>(p, varlen, sample, stream);
     DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
     DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
     DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)
     DSAI_CASE(2, 2, 32) DSAI_CASE(2, 2, 64) DSAI_CASE(2, 2, 128)
+    DSAI_CASE(3, 1, 64) DSAI_CASE(3, 1, 128) DSAI_CASE(3, 2, 64) DSAI_CASE(3, 2, 128)
     DSAI_CASE(0, 1, 32) DSAI_CASE(0, 1, 64)
     DSAI_CASE(0, 2, 32) DSAI_CASE(0, 2, 64)
 #undef DSAI_CASE

@@ -81,13 +81,15 @@ namespace {
 
 constexpr int kThreads = kQueriesPerBlock * 64;
 
-template <int DT, int NB, int D, bool DENSE, bool VARLEN, bool SCREEN>
+template <int DT, int NB, int D, bool FEW, bool VARLEN, bool SCREEN>
 __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectParams p)
 {
-    static_assert(!SCREEN || (NB == 2 && !DENSE && !VARLEN), "screening: two head blocks");
+    static_assert(!SCREEN || (NB == 2 && !FEW && !VARLEN && DT != 3),
+                  "screening: two head blocks, fp32-accumulated products");
     using O = Op<DT, D>;
     using A = typename O::A;
-    constexpr int KS = O::KS, NCH = O::NCH, GCH = O::GCH, ES = O::ES;
+    constexpr int KS = O::KS, NCH = O::NCH, GCH = O::GCH, ES = O::ES, CPK = O::CPK;
+    constexpr bool kScaled = DT >= 2;  // fp8 codes: per-row scales fold out of the ReLU
     constexpr int TILE_CH = kKeysPerTile * NCH;     // LDS 16-B chunks per tile
     constexpr int GTILE_CH = kKeysPerTile * GCH;    // global 16-B chunks per tile
     constexpr int CPT = (GTILE_CH + kThreads - 1) / kThreads;
@@ -107,12 +109,15 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = lane >> 5, l32 = lane & 31;
     const int64_t ngroups = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock;
-    // dense mode: block = (query group, key range); streaming: one range
-    const int64_t gi = DENSE ? (int64_t)blockIdx.x / p.nsplit : (int64_t)blockIdx.x;
-    const int sp = DENSE ? (int)((int64_t)blockIdx.x - gi * p.nsplit) : 0;
+    // few-query mode: block = (query group, key range); streaming: one range
+    const int64_t gi = FEW ? (int64_t)blockIdx.x / p.nsplit : (int64_t)blockIdx.x;
+    const int sp = FEW ? (int)((int64_t)blockIdx.x - gi * p.nsplit) : 0;
     const int64_t grp = ngroups - 1 - gi;  // heaviest rows first
     const int64_t qrow = grp * kQueriesPerBlock + wave;
-    const bool active = qrow < p.nrows;
+    // repair launch (few-query rows whose estimate failed): only those rows
+    // are scored and written; a block with none of them returns at once
+    const bool active = qrow < p.nrows && (!p.repair || p.repair[qrow] != 0);
+    if (!FEW && p.repair && !__syncthreads_or(active)) return;
     const int64_t t = p.row0 + qrow;
     // This row's key window [klo, klo + Pq) and the token position of its
     // key 0 (tok0, expanded outputs).  One document: every key from 0, the
@@ -150,8 +155,8 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         int64_t last = grp * kQueriesPerBlock + kQueriesPerBlock - 1;
         if (last > p.nrows - 1) last = p.nrows - 1;
         const int64_t Pblk = visible_keys(p.q_pos0 + p.row0 + last, p.T, p.m, p.causal);
-        kbeg = DENSE ? (int64_t)sp * p.split_keys : 0;
-        kend = DENSE && kbeg + p.split_keys < Pblk ? kbeg + p.split_keys : Pblk;
+        kbeg = FEW ? (int64_t)sp * p.split_keys : 0;
+        kend = FEW && kbeg + p.split_keys < Pblk ? kbeg + p.split_keys : Pblk;
         Pmax = Pblk;
     }
     // The end of an output row after its `body` selected entries: the tail
@@ -172,7 +177,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // asked for: every visible key is selected whatever its score, so the
     // block loads nothing, scores nothing and writes its rows' visible keys
     // in key order (block-uniform, after the last barrier of such a block).
-    if (!DENSE && !p.sel_score && Pmax <= p.ksel) {
+    if (!FEW && !p.sel_score && Pmax <= p.ksel) {
         if (active) {
             const int mexp = p.expand ? p.m : 1;
             const int64_t obase = VARLEN && p.expand ? tok0 - klo * p.m : 0;
@@ -188,7 +193,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + kKeysPerTile - 1) / kKeysPerTile) : 0;
 
     uint32_t *hist = hist_all[wave];
-    if (!DENSE) hist_clear(hist, lane);
+    if (!FEW) hist_clear(hist, lane);
 
     // q fragments and folded head weights of this wave's query; every load
     // is issued from a clamped, valid address and masked afterwards, so the
@@ -218,7 +223,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                 wv[b][v] = active ? p.cert_w[crow * 64 + h2] : 0.f;
             } else {
                 float wt = p.w[tq * p.w_stride + hc];
-                if (DT == 2) wt *= p.q_scale[tq * p.H + hc];
+                if (kScaled) wt *= p.q_scale[tq * p.H + hc];
                 wv[b][v] = ok ? wt : 0.f;
             }
         }
@@ -234,7 +239,12 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         emu = active ? p.cert_e[crow] : 0.f;
     }
 
-    uint2 *buf = p.ws + (active && !DENSE ? qrow : 0) * (int64_t)p.cap;
+    uint2 *buf = p.ws + (active ? qrow : 0) * (int64_t)p.cap;
+    // few-query mode: the row's estimate and the scores of the current
+    // candidate batch (two tiles)
+    const uint32_t west = FEW && active ? p.est[qrow] : 0u;
+    float bsc[2];
+    bsc[0] = bsc[1] = 0.f;
     int cnt = 0;
     uint32_t tau = 0;        // pass iff code >= tau
     float tau_f = -__builtin_inff();  // the same test on the float score
@@ -275,7 +285,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                 }
             }
         }
-        if (DT == 2 && threadIdx.x < kKeysPerTile) {
+        if (kScaled && threadIdx.x < kKeysPerTile) {
             const int64_t key = j0 + threadIdx.x;
             ksc = key < p.T ? p.k_scale[key] : 0.f;
         }
@@ -293,7 +303,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                 O::store_chunk(ktile[slot], r, id % GCH, stage[c], r & SWZ);
             }
         }
-        if (DT == 2 && threadIdx.x < kKeysPerTile) kscale_tile[slot][threadIdx.x] = ksc;
+        if (kScaled && threadIdx.x < kKeysPerTile) kscale_tile[slot][threadIdx.x] = ksc;
         if (SCREEN && threadIdx.x < kKeysPerTile) knorm_tile[slot][threadIdx.x] = kn;
     };
 
@@ -307,10 +317,20 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // l32 & SWZ for every column block, so the byte offsets of its KS chunks
     // are fixed for the whole launch; a column block adds a constant.
     constexpr bool kBOff = DT != 0 && SWZ < 32;
-    uint32_t boff[KS];
+    constexpr int NOFF = kBOff ? KS * CPK : 1;
+    uint32_t boff[NOFF];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        boff[ks] = (uint32_t)((l32 * NCH + ((hh * KS + ks) ^ (l32 & SWZ))) * 16);
+    for (int c = 0; c < NOFF; ++c)
+        boff[c] = (uint32_t)((l32 * NCH + ((hh * KS * CPK + c) ^ (l32 & SWZ))) * 16);
+    // B operand ks of column block cb from the staged tile at those offsets
+    auto lds_b = [&](const char *tbytes, int cb, int ks) __attribute__((always_inline)) {
+        uint4 ch[CPK > 0 ? CPK : 1];
+#pragma unroll
+        for (int c = 0; c < CPK; ++c)
+            ch[c] = *reinterpret_cast<const uint4 *>(tbytes + cb * 32 * NCH * 16 +
+                                                     boff[ks * CPK + c]);
+        return O::from_chunks(ch);
+    };
 
     // Selection of one tile's scores (NG groups of 64 keys, one key per lane).
     constexpr int NCB = kKeysPerTile / 32;  // 32-key column blocks per tile
@@ -358,13 +378,28 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         }
     };
     auto select_tile = [&](const float (&sg)[NG], int64_t j0) {
-        if constexpr (DENSE) {
-            float *srow = p.scores + qrow * p.sstride;
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int64_t key = j0 + g * kSelGroup + lane;
-                if (key < Pq) srow[key] = sg[g];
+        if constexpr (FEW) {
+            // the first tile of a batch waits for the second; the batch is
+            // appended after its last tile this row reaches in this range
+            static_assert(2 * NG * kSelGroup == kFewBatch, "two tiles per candidate batch");
+            const bool second = (j0 / kKeysPerTile) & 1;
+            const bool last = second || j0 + kKeysPerTile >= Pq || j0 + kKeysPerTile >= kend;
+            if (!last) {
+                bsc[0] = sg[0];
+                bsc[1] = sg[1];
+                return;
             }
+            const int64_t b = j0 / kFewBatch;
+            float sc[2 * NG];
+            sc[0] = second ? bsc[0] : sg[0];
+            sc[1] = second ? bsc[1] : sg[1];
+            sc[2] = second ? sg[0] : 0.f;
+            sc[3] = second ? sg[1] : 0.f;
+            const int64_t kv = b * kFewBatch + (second ? 2 : 1) * kKeysPerTile;
+            const int sub = (int)(b % kFewSub);
+            fq_append<2 * NG>(sc, b * kFewBatch, Pq < kv ? Pq : kv, west,
+                              p.fq_cnt + qrow * kFewSub + sub, buf + sub * kFewSubCap,
+                              p.fq_dir + qrow * p.nbatch + b, lane, kFewSubCap);
             return;
         }
         const bool full = j0 >= klo && j0 + kKeysPerTile <= khi;
@@ -393,8 +428,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         if constexpr (kBOff) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                bfr[ks] = __builtin_bit_cast(
-                    A, *reinterpret_cast<const uint4 *>(tbytes + boff[ks]));
+                bfr[ks] = lds_b(tbytes, 0, ks);
         } else {
             O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
         }
@@ -411,9 +445,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                 if (s < NCB) acc = O::mma(qa[0][ks], bfr[ks], acc);
                 if (loads) {
                     if constexpr (kBOff) {
-                        bfr[ks] = __builtin_bit_cast(
-                            A, *reinterpret_cast<const uint4 *>(
-                                   tbytes + (s + 1) * 32 * NCH * 16 + boff[ks]));
+                        bfr[ks] = lds_b(tbytes, s + 1, ks);
                     } else {
                         const int r = (s + 1) * 32 + l32;
                         O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
@@ -451,7 +483,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                                                              false, false);
             const int kl = g * kSelGroup + lane;
             float U = __uint_as_float(sw[0]) + __uint_as_float(sw[1]) + emu * knorm_tile[cur][kl];
-            if (DT == 2) U *= kscale_tile[cur][kl];
+            if (kScaled) U *= kscale_tile[cur][kl];
             const int64_t key = j0 + kl;
             const bool surv = (full || (key >= klo && key < khi)) && U >= tau_f;
             const uint64_t m = __ballot(surv);
@@ -501,7 +533,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                                                              __float_as_uint(pc[1]), false, false);
             const int klane = hh ? kl[1] : kl[0];
             float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (DT == 2) sc *= kscale_tile[cur][klane];
+            if (kScaled) sc *= kscale_tile[cur][klane];
             consider(sc, j0 + klane, sb + lane < ns);
         }
         if (sb < ns) {  // at most 32 survivors left: one gathered block
@@ -520,7 +552,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(e),
                                                              __float_as_uint(e), false, false);
             float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (DT == 2) sc *= kscale_tile[cur][kl];
+            if (kScaled) sc *= kscale_tile[cur][kl];
             consider(sc, j0 + kl, lane < 32 && i < ns);
         }
         wave_sync_mem();  // the next tile's survivor list reuses sl and p0
@@ -530,7 +562,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // opposite ends of a tile: waves 0-3 right after their MFMA/epilogue work,
     // waves 4-7 one tile later, before their MFMAs -- so one wave's branchy
     // selection code always has the other wave's MFMAs to overlap with.
-    const bool lagged = !DENSE && !SCREEN && wave >= kQueriesPerBlock / 2;
+    const bool lagged = !FEW && !SCREEN && wave >= kQueriesPerBlock / 2;
     float pend[NG];
     int64_t pend_j0 = -1;
 
@@ -562,8 +594,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             if constexpr (kBOff) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    bfr[ks] = __builtin_bit_cast(
-                        A, *reinterpret_cast<const uint4 *>(tbytes + boff[ks]));
+                    bfr[ks] = lds_b(tbytes, 0, ks);
             } else {
                 O::load_b(ktile[cur], l32, hh, l32 & SWZ, bfr);
             }
@@ -583,9 +614,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                     if (s < NS) acc = O::mma(qa[b][ks], bfr[ks], acc);
                     if (loads) {
                         if constexpr (kBOff) {
-                            bfr[ks] = __builtin_bit_cast(
-                                A, *reinterpret_cast<const uint4 *>(
-                                       tbytes + (cb + 1) * 32 * NCH * 16 + boff[ks]));
+                            bfr[ks] = lds_b(tbytes, cb + 1, ks);
                         } else {
                             const int r = (cb + 1) * 32 + l32;
                             O::load_b_one(ktile[cur], r, hh, r & SWZ, ks, bfr[ks]);
@@ -614,7 +643,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
                                                                  __float_as_uint(part[2 * g + 1]),
                                                                  false, false);
                 sg[g] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                if (DT == 2) sg[g] *= kscale_tile[cur][g * kSelGroup + lane];
+                if (kScaled) sg[g] *= kscale_tile[cur][g * kSelGroup + lane];
             }
             if (lagged) {
 #pragma unroll
@@ -629,7 +658,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     }
     if (pend_j0 >= 0) select_tile(pend, pend_j0);
 
-    if (!active || DENSE) return;
+    if (!active || FEW) return;
 
     // ---- exact final selection, written straight into the output row ----
     // The K tiles are idle after the last barrier: each wave borrows a slice
@@ -673,23 +702,23 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     end_row(wcnt * mexp, srow);
 }
 
-template <int DT, int NB, int D, bool DENSE, bool VARLEN, bool SCREEN>
+template <int DT, int NB, int D, bool FEW, bool VARLEN, bool SCREEN>
 hipError_t launch_one(const ScoreSelectParams &p, hipStream_t stream)
 {
     const int64_t blocks = (p.nrows + kQueriesPerBlock - 1) / kQueriesPerBlock * p.nsplit;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, DENSE, VARLEN, SCREEN>),
+    hipLaunchKernelGGL((score_select_kernel<DT, NB, D, FEW, VARLEN, SCREEN>),
                        dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int DT, int NB, int D>
-hipError_t launch_mode(bool dense, bool varlen, bool screen, const ScoreSelectParams &p,
+hipError_t launch_mode(bool few, bool varlen, bool screen, const ScoreSelectParams &p,
                        hipStream_t stream)
 {
     if (varlen) return launch_one<DT, NB, D, false, true, false>(p, stream);
-    if (dense) return launch_one<DT, NB, D, true, false, false>(p, stream);
-    if constexpr (NB == 2) {
+    if (few) return launch_one<DT, NB, D, true, false, false>(p, stream);
+    if constexpr (NB == 2 && DT != 3) {
         if (screen) return launch_one<DT, NB, D, false, false, true>(p, stream);
     }
     return launch_one<DT, NB, D, false, false, false>(p, stream);
@@ -697,22 +726,23 @@ hipError_t launch_mode(bool dense, bool varlen, bool screen, const ScoreSelectPa
 
 }  // namespace
 
-hipError_t launch_score_select(int dtype, int nb, int d, bool dense, bool varlen, bool screen,
+hipError_t launch_score_select(int dtype, int nb, int d, bool few, bool varlen, bool screen,
                                const ScoreSelectParams &p, hipStream_t stream, bool *supported)
 {
     *supported = true;
     if (p.nsplit < 1 || p.split_keys < kKeysPerTile || p.split_keys % kKeysPerTile ||
-        (varlen && (dense || p.nsplit != 1)) || (screen && (dense || varlen || nb != 2))) {
+        (varlen && (few || p.nsplit != 1)) || (screen && (few || varlen || nb != 2))) {
         *supported = false;
         return hipSuccess;
     }
 #define DSAI_CASE(DT, NB, D) \
     if (dtype == DT && nb == NB && d == D) \
-        return launch_mode<DT, NB, D>(dense, varlen, screen, p, stream);
+        return launch_mode<DT, NB, D>(few, varlen, screen, p, stream);
     DSAI_CASE(1, 1, 32) DSAI_CASE(1, 1, 64) DSAI_CASE(1, 1, 128)
     DSAI_CASE(1, 2, 32) DSAI_CASE(1, 2, 64) DSAI_CASE(1, 2, 128)
     DSAI_CASE(2, 1, 32) DSAI_CASE(2, 1, 64) DSAI_CASE(2, 1, 128)
     DSAI_CASE(2, 2, 32) DSAI_CASE(2, 2, 64) DSAI_CASE(2, 2, 128)
+    DSAI_CASE(3, 1, 64) DSAI_CASE(3, 1, 128) DSAI_CASE(3, 2, 64) DSAI_CASE(3, 2, 128)
     DSAI_CASE(0, 1, 32) DSAI_CASE(0, 1, 64)
     DSAI_CASE(0, 2, 32) DSAI_CASE(0, 2, 64)
 #undef DSAI_CASE

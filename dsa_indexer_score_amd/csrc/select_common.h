@@ -97,6 +97,42 @@ __device__ __forceinline__ DocWindow doc_window(const Params &p, int64_t t)
 }
 
 
+// Few-query append (one wave, one row): the survivors of one batch of up to
+// kFewBatch keys -- NG groups of 64, key0 + 64 g + lane in the row's local
+// key order, sc[g] the lane's score, visible while below P -- whose order
+// code is at least est.  They go to the candidate sub-list `cand` as one
+// contiguous run in key order, reserved with one atomic on its count *cnt;
+// the batch's directory entry records (offset, count).  Slots from `fewcap`
+// on are counted but not stored (the row then goes to the repair launch).
+template <int NG>
+__device__ __forceinline__ void fq_append(const float (&sc)[NG], int64_t key0, int64_t P,
+                                          uint32_t est, uint32_t *cnt, uint2 *cand,
+                                          uint2 *dir_entry, int lane, int fewcap)
+{
+    uint64_t m[NG];
+    uint32_t before[NG];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const bool pass = key0 + 64 * g + lane < P && ord_code(__float_as_uint(sc[g])) >= est;
+        m[g] = __ballot(pass);
+        before[g] = tot;
+        tot += (uint32_t)__popcll(m[g]);
+    }
+    uint32_t off = 0;
+    if (tot) {
+        if (lane == 0) off = atomicAdd(cnt, tot);
+        off = (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const uint32_t i = off + before[g] + (uint32_t)lane_rank(m[g]);
+            if (((m[g] >> lane) & 1ull) && i < (uint32_t)fewcap)
+                cand[i] = make_uint2(__float_as_uint(sc[g]), (uint32_t)(key0 + 64 * g + lane));
+        }
+    }
+    if (lane == 0) *dir_entry = make_uint2(off, tot);
+}
+
 // ---------------------------------------------------------------------------
 // Selection helpers (one wave, one query).  Codes are cut in three radix
 // levels: the top kB1 = 12 bits (the running histogram), then 10 and 10.

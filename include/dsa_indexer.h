@@ -54,7 +54,16 @@ enum idx_dtype { IDX_F32 = 0, IDX_BF16 = 1, IDX_FP8_E4M3 = 2 };
 enum {
     IDX_EXPAND = 1, /* selected pools expand to their m token positions   */
     IDX_TAIL = 2,   /* append the incomplete pool (needs EXPAND, causal)  */
-    IDX_SCREEN = 4  /* DoSA certificate screening, see below              */
+    IDX_SCREEN = 4, /* DoSA certificate screening, see below              */
+    /* IDX_FP8_E4M3 only: contract the e4m3 codes as they are on the gfx950
+     * fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) instead of widening them
+     * exactly to bf16 for the bf16 MFMA.  Twice the matrix rate, but the
+     * instruction sums its 64 products at reduced internal precision, so
+     * scores differ from the fp32-accumulated ones by more than rounding
+     * (within the fp8 tolerance of the scores the pages' systems compute
+     * on fp8 tensor cores).  d in {64, 128}; ignored for d = 32 and with
+     * IDX_SCREEN (whose bound needs fp32-accumulated products). */
+    IDX_FP8_MFMA = 8
 };
 
 enum {
@@ -67,28 +76,33 @@ enum {
 
 typedef struct {
     int dtype;           /* enum idx_dtype                                     */
-    int flags;           /* IDX_EXPAND | IDX_TAIL | IDX_SCREEN                 */
+    int flags;           /* IDX_EXPAND | IDX_TAIL | IDX_SCREEN | IDX_FP8_MFMA  */
     int64_t query_chunk; /* queries per streaming launch (bounds the workspace);
                           * 0 = as many as 4 GiB of candidate buffers hold
                           * (at least 2048); results do not depend on it    */
     /* Few-query path (decode, small batches against a long key set): when
-     * S <= few_query_rows, every visible score of the S rows is written to
-     * the workspace by all CUs, candidates at or above a per-row threshold
-     * estimate are filtered out by all CUs, and each row is then cut exactly
-     * by one block; otherwise rows are scored and selected in one streaming
+     * S <= few_query_rows, all CUs score a sample of each row's keys (8,192
+     * keys in 128 runs of 64), one block per row cuts a threshold estimate
+     * from it, all CUs score the rows' keys and append only the (score, key)
+     * pairs at or above the estimate to the row's candidate list (the DoSA
+     * summary's sparse write-back: no score array is written), and one block
+     * per row cuts the exact selection from its candidates; a row whose
+     * candidates cannot hold the selection (the estimate too high, or more
+     * than 8,192 candidates) is selected by a streaming launch over the
+     * marked rows.  Otherwise rows are scored and selected in one streaming
      * pass per query chunk.  0 = default: 1024, or 64 for packed documents
      * with more than two rows per document (indexer_score_topk_varlen: S >
      * 2 ndoc), whose rows share key tiles on the streaming path; negative =
-     * never.  Both paths give identical results.  For packed documents the
-     * rows hold max_doc_keys scores instead of T (see the varlen call).  The
-     * dense workspace holds, each part starting
-     * on a 256-byte boundary, the scores (S * T4 * 4 bytes, T4 = T rounded
-     * up to 4), the estimates (S * 4), the candidate counts (S * G * 4,
-     * G = ceil(max(T, 1) / 4096)) and the candidates as (score, key) pairs
-     * (S * G * 4096 * 8), about 12 bytes per (row, key).  It is capped at
-     * 4 GiB: when the S rows need more, the workspace is sized for the R
-     * rows that fit and the rows are taken in ceil(S / R) equal passes (the
-     * path is used while one row fits). */
+     * never.  Both paths give identical results.  The few-query workspace
+     * holds, each part starting on a 256-byte boundary, the samples' scores
+     * (S * 8192 * 4 bytes), the estimates, candidate counts and repair marks
+     * (S * 4 each), a directory of (offset, count) per 256 keys of a row
+     * (S * ceil(Tk / 256) * 8; Tk = T, or max_doc_keys for packed
+     * documents) and the candidate lists (S * cap * 8, cap = max(8192, the
+     * streaming path's slots per row)) -- about 200 KB per row at 262,144
+     * keys.  It is capped at 4 GiB: when the S rows need more, it is sized
+     * for the R rows that fit and the rows are taken in ceil(S / R) equal
+     * passes. */
     int64_t few_query_rows;
 } indexer_config;
 
@@ -111,7 +125,7 @@ int indexer_output_width(int topk, int m, int flags, int *W);
 
 /* Device workspace bytes that indexer_score_topk needs for this problem
  * with this handle: per-query candidate buffers for one query chunk, or the
- * dense score rows of the few-query path.  Host-only; depends on S,
+ * few-query layout (samples, candidate lists, directory).  Host-only; depends on S,
  * query_chunk, few_query_rows, T, m, topk and the flags. */
 int indexer_workspace_bytes(indexer_t h, int64_t S, int64_t T, int H, int d, int m, int topk,
                             size_t *bytes);
@@ -204,9 +218,9 @@ int indexer_score_topk_noalloc(indexer_t h, const void *q, const float *q_scale,
  *           cu_k[i+1] - cu_k[i] (as a maximum sequence length is passed to
  *           varlen attention); 0 = unknown, taken as T; values above T are
  *           taken as T; negative: IDX_EINVAL.  It sizes the few-query
- *           path's dense rows (max_doc_keys scores per row instead of T),
- *           so batched decode over many documents needs far less workspace
- *           and fewer passes; the streaming path does not use it.  A
+ *           path's per-row directory and candidate slots (by max_doc_keys
+ *           keys instead of T), so batched decode over many documents needs
+ *           far less workspace; the streaming path does not use it.  A
  *           document with more keys breaks the precondition: its rows'
  *           selection is then unspecified, but every access stays in bounds.
  *   Output entries: compressed keys as global key indices cu_k[i] + j;
@@ -221,9 +235,10 @@ int indexer_score_topk_noalloc(indexer_t h, const void *q, const float *q_scale,
  * document lacks complete pools gets a tail clipped to the row width.  With
  * IDX_EXPAND the caller keeps every output index below 2^31.  With at most
  * few_query_rows rows (batched decode: one row per sequence) the rows take
- * the few-query path (each row's own key window scored by all CUs into a
- * dense row of max_doc_keys scores, then the per-row exact cut; in equal
- * passes when S rows need more than 4 GiB); otherwise the streaming path.
+ * the few-query path (each row's own key window, at most max_doc_keys keys,
+ * scored by all CUs with only the keys at or above the row's estimate kept,
+ * then the per-row exact cut; in equal passes when S rows need more than
+ * 4 GiB); otherwise the streaming path.
  * With the default few_query_rows that means up to 1024 rows when S <= 2
  * ndoc, else up to 64.  Both give identical results.  Workspace from
  * indexer_workspace_bytes_varlen with the same S, T, ndoc and max_doc_keys.

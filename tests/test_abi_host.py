@@ -60,7 +60,7 @@ def _handle(dtype=_lib.IDX_BF16, flags=0, chunk=0, few=0):
 def test_create_rejects_bad_configs():
     lib = _lib.load()
     h = ctypes.c_void_p()
-    for dtype, flags, chunk, dev in ((7, 0, 0, 0), (1, 8, 0, 0), (1, _lib.IDX_TAIL, 0, 0),
+    for dtype, flags, chunk, dev in ((7, 0, 0, 0), (1, 16, 0, 0), (1, _lib.IDX_TAIL, 0, 0),
                                      (1, 0, -1, 0), (1, 0, 0, -1)):
         cfg = _lib.IndexerConfig(dtype, flags, chunk)
         assert lib.indexer_create(ctypes.byref(cfg), dev, ctypes.byref(h)) == _lib.IDX_EINVAL
@@ -99,32 +99,51 @@ def test_workspace_bytes_automatic_query_chunk():
     lib.indexer_destroy(h)
 
 
-def _dense_bytes(S, T):
-    """The documented few-query layout: scores, estimates, candidate counts
-    and (score, key) candidates, each part 256-byte aligned."""
+def _capacity(ksel, P):
+    """Streaming candidate slots per row (the documented formula)."""
     up = lambda x, a: -(-x // a) * a
-    G = -(-max(T, 1) // 4096)
-    return up(S * up(max(T, 1), 4) * 4, 256) + up(S * 4, 256) + up(S * G * 4, 256) + \
-        S * G * 4096 * 8
+    return min(min(up(10 * ksel + 256, 64), 65472), up(max(P, 0), 64) + 64)
+
+
+def _dense_bytes(S, T, ksel=2048):
+    """The documented few-query layout for S rows of at most T keys: key
+    samples (8192 fp32 per row), estimates, the counts of 32 candidate
+    sub-lists, repair marks, the batch directory (8 bytes per 256 keys) and
+    the candidate sub-lists (max(32 x 1024, streaming capacity) entries of 8
+    bytes), each part 256-byte aligned.  Nothing in it holds a score per
+    key."""
+    up = lambda x, a: -(-x // a) * a
+    nb = -(-max(T, 1) // 256)
+    cap = max(32 * 1024, _capacity(ksel, T))
+    return up(S * 8192 * 4, 256) + up(S * 4, 256) + up(S * 32 * 4, 256) + up(S * 4, 256) + \
+        up(S * nb * 8, 256) + S * cap * 8
 
 
 def test_workspace_bytes_of_the_few_query_path():
-    """At or below few_query_rows (default 1024) the workspace holds the rows'
-    dense scores and the selection's candidate scratch, for as many rows as
-    fit in 4 GiB (the rest are taken in further passes); a negative setting
-    always streams."""
+    """At or below few_query_rows (default 1024) the workspace holds the
+    rows' key samples, candidate sub-lists and batch directory -- a fixed
+    part per row plus 1/32 byte per (row, key), where a score array would be
+    4 bytes -- for as many rows as fit in 4 GiB (the rest are taken in
+    further passes); a negative setting always streams."""
     n = ctypes.c_size_t()
     lib, h = _handle(chunk=16384)
     assert lib.indexer_workspace_bytes(h, 64, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(64, 262144) == 64 * 262144 * 12 + 256 + 64 * 64 * 4
+    assert n.value == _dense_bytes(64, 262144)
+    n4 = ctypes.c_size_t()
+    assert lib.indexer_workspace_bytes(h, 64, 4 * 262144, 64, 128, 4, 2048,
+                                       ctypes.byref(n4)) == 0
+    assert n4.value - n.value == 64 * 3 * 262144 // 256 * 8   # only the directory grows
     assert lib.indexer_workspace_bytes(h, 1, 1001, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(1, 1001) == 4096 + 256 + 256 + 4096 * 8
+    assert n.value == _dense_bytes(1, 1001) == 32768 + 4 * 256 + 32768 * 8
     assert lib.indexer_workspace_bytes(h, 1025, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 1025 * 20736 * 8          # above the default: streaming buffers
     assert lib.indexer_workspace_bytes(h, 1024, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(1024, 262144)   # 3.2 GB: one pass
-    assert lib.indexer_workspace_bytes(h, 64, 2 ** 25, 64, 128, 1, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(10, 2 ** 25)  # 25 GiB for all rows: passes of 10 rows
+    assert n.value == _dense_bytes(1024, 262144)   # 0.2 GB: one pass
+    # 2^31 - 1 keys: the directory alone is 64 MB per row, so 4 GiB holds 63
+    # rows and the 64 rows are taken in two passes of 32
+    assert lib.indexer_workspace_bytes(h, 64, 2 ** 31 - 1, 64, 128, 1, 2048,
+                                       ctypes.byref(n)) == 0
+    assert n.value == _dense_bytes(63, 2 ** 31 - 1)
     lib.indexer_destroy(h)
     lib, h = _handle(few=-1)
     assert lib.indexer_workspace_bytes(h, 1, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
@@ -147,15 +166,12 @@ def test_few_query_passes_property():
     for _ in range(300):
         S, T = rng.randint(1, 3000), rng.choice([rng.randint(1, 5000), rng.randint(1, 1 << 28)])
         assert lib.indexer_workspace_bytes(h, S, T, 8, 64, 1, 64, ctypes.byref(n)) == 0
-        if _dense_bytes(1, T) > 1 << 32:
-            assert n.value < _dense_bytes(1, T)                # streaming buffers
-            continue
         lo, hi = 1, S
         while lo < hi:                                         # largest r with r rows fitting
             mid = (lo + hi + 1) // 2
-            lo, hi = (mid, hi) if _dense_bytes(mid, T) <= 1 << 32 else (lo, mid - 1)
+            lo, hi = (mid, hi) if _dense_bytes(mid, T, 64) <= 1 << 32 else (lo, mid - 1)
         R = lo
-        assert n.value == _dense_bytes(R, T) <= 1 << 32, (S, T)
+        assert n.value == _dense_bytes(R, T, 64) <= 1 << 32, (S, T)
     lib.indexer_destroy(h)
 
 
@@ -183,13 +199,14 @@ def test_workspace_bytes_varlen_follow_the_path():
     assert n.value == 1024 * (4096 + 64) * 8
     assert wb(h, 64, 4096, 1, 1000) == 0       # at most 64 rows: few-query
     assert n.value == _dense_bytes(64, 1000)
-    # 64 decode rows over 64 documents of 262,144 keys: one pass of 64 short
-    # rows with the bound, passes of 21 rows of all 2^24 keys without it
+    # 64 decode rows over 64 documents of 262,144 keys: the bound sizes each
+    # row's directory (and streaming capacity) by 262,144 keys instead of
+    # all 2^24; either way the 64 rows fit in one pass
     T = 64 * 262144
     assert wb(h, 64, T, 64, 262144) == 0
     assert n.value == _dense_bytes(64, 262144)
     assert wb(h, 64, T, 64, 0) == 0
-    assert n.value == _dense_bytes(21, T)
+    assert n.value == _dense_bytes(64, T) > _dense_bytes(64, 262144)
     lib.indexer_destroy(h)
     lib, h = _handle(few=-1)
     assert wb(h, 8, 4096, 8, 0) == 0

@@ -1,5 +1,7 @@
-"""The few-query path (dense scores + candidate filter + exact cut per row)
-against the streaming path and the oracle.
+"""The few-query path (sampled threshold estimate, scoring with sparse
+write-back of the keys that reach it, exact cut per row, repair of the rows
+whose estimate fails by the streaming kernel) against the streaming path and
+the oracle.
 
 Both paths share the scoring arithmetic and implement the same exact
 selection, so on the same inputs they must agree bit for bit (indices,
@@ -149,10 +151,11 @@ def test_few_query_empty_and_single_key():
     assert vl.tolist() == [1, 1, 1, 1] and idx[:, 0].tolist() == [0, 0, 0, 0]
 
 
-def test_few_query_more_than_1024_candidate_segments():
-    """A row of 4.5M keys has more than 1,024 filter segments of 4,096 keys,
+def test_few_query_more_than_1024_candidate_batches():
+    """A row of 4.5M keys has more than 1,024 candidate batches of 256 keys,
     so the cut kernel gathers the candidates in several rounds; ties on
-    repeated keys make the rounds' boundaries matter."""
+    repeated keys make the rounds' boundaries matter (and may overflow the
+    candidate list, which sends the row to the repair launch)."""
     g = torch.Generator().manual_seed(9)
     T, H, d = 4_500_000, 4, 32
     base = torch.randn(4096, d, generator=g)
@@ -165,26 +168,89 @@ def test_few_query_more_than_1024_candidate_segments():
     assert (dense[1] == 300).all()
 
 
-def test_few_query_rows_in_passes():
-    """Eight decode rows over 48M keys need more than the 4 GiB the dense
-    workspace may take, so the rows go in two equal passes (4 + 4; 7 would
-    fit); each row equals the same row scored and cut on its own."""
-    import dsa_indexer_score_amd as dsai
-    g = torch.Generator().manual_seed(21)
-    S, T, H, d = 8, 48_000_000, 4, 32
-    base = (torch.randn(1 << 16, d, generator=g) / d ** 0.5).bfloat16()
-    k = base[torch.randint(0, 1 << 16, (T,), generator=g)].to(DEV)
-    q = (torch.randn(S, H, d, generator=g) / d ** 0.5).bfloat16().to(DEV)
-    w = torch.randn(S, H, generator=g).to(DEV)
-    kw = dict(m=1, topk=700, causal=True, few_query_rows=64, with_scores=True)
-    h = dsai.Indexer(torch.bfloat16, few_query_rows=64, device=DEV)
-    assert 6 * 12 * T < h.workspace_bytes(S, T, H, d, 1, 700) <= 1 << 32   # 7 rows a pass
-    idx, vl, sc = dsai.score_topk(q, w, k, q_pos0=T - S, **kw)
-    torch.cuda.synchronize()
+def _sample_places(P):
+    """Keys of the few-query estimate's sample for a row of P > 8192 keys:
+    64 consecutive keys at each of 128 places g * (P - 64) // 127."""
+    sp = (P - 64) // 127
+    return (np.arange(128)[:, None] * sp + np.arange(64)[None, :]).ravel()
+
+
+def _adversarial_keys(T, P, kind, g):
+    """Column 0 of the keys, read by a query (1, 0, ...) with weight 1, so a
+    key's score is ReLU(k[j, 0]).  'high': the sampled keys score 5..15 and
+    every other key below 5, so the estimate (a high quantile of the sample)
+    leaves fewer candidates than the selection needs; 'overflow': the
+    sampled keys tie at 10 and 3,000 other keys score 20, so more keys than
+    the candidate list holds reach the estimate.  Column 1 is random."""
+    k = torch.zeros(T, 32)
+    k[:, 1] = torch.randn(T, generator=g)
+    places = torch.from_numpy(_sample_places(P))
+    if kind == "high":
+        k[:, 0] = 4.0 + torch.arange(T, dtype=torch.float32) / (4 * T)
+        k[places, 0] = 5.0 + 10.0 * torch.randperm(places.numel(), generator=g).float() / places.numel()
+    else:
+        k[:, 0] = 1.0
+        k[places, 0] = 10.0
+        others = torch.from_numpy(np.setdiff1d(np.arange(T), _sample_places(P)))
+        pick = others[torch.randperm(others.numel(), generator=g)[:3000]]
+        k[pick, 0] = 20.0
+    return k
+
+
+@pytest.mark.parametrize("kind", ["high", "overflow"])
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_few_query_rows_whose_estimate_fails_are_repaired(kind, S):
+    """Rows built so that the sampled estimate fails -- too few candidates
+    reach it, or more than the list holds -- are selected by the repair
+    launch; in a batch, rows reading column 1 (random scores) are cut from
+    their candidates as usual.  Either way the result equals the streaming
+    path's bit for bit, and the adversarial rows keep exactly the keys the
+    construction fixes."""
+    g = torch.Generator().manual_seed(31 + S)
+    T = 65536
+    k = _adversarial_keys(T, T, kind, g)
+    q = torch.zeros(S, 1, 32)
+    adv = [t % 2 == 0 or S == 1 for t in range(S)]
     for t in range(S):
-        i1, v1, s1 = dsai.score_topk(q[t:t + 1].contiguous(), w[t:t + 1].contiguous(), k,
-                                     q_pos0=T - S + t, **kw)
-        torch.cuda.synchronize()
-        assert torch.equal(i1[0], idx[t]) and torch.equal(v1[0], vl[t]), t
-        assert torch.equal(s1[0], sc[t]), t
-    assert (vl == 700).all()
+        q[t, 0, 0 if adv[t] else 1] = 1.0
+    inp = replace(gen.custom(q=q.bfloat16(), k=k.bfloat16(), w=torch.ones(1), topk=2048),
+                  q_pos0=T - 1, causal=False).to(DEV)
+    import dsa_indexer_score_amd as dsai
+    ix = dsai.Indexer(torch.bfloat16, few_query_rows=64, device=DEV)
+    ws = torch.empty(ix.workspace_bytes(S, T, 1, 32, 1, 2048), dtype=torch.uint8, device=DEV)
+    dense = ix.score_topk(inp.q, inp.w, inp.k, topk=2048, causal=False, with_scores=True,
+                          workspace=ws)
+    stream = run(inp, few_query_rows=-1)
+    _assert_identical(dense, stream)
+    # the repair marks, at their documented place in the workspace (after
+    # the samples, estimates and 32 sub-list counts): exactly the
+    # adversarial rows
+    up = lambda x: -(-x // 256) * 256
+    at = up(S * 8192 * 4) + up(S * 4) + up(S * 32 * 4)
+    status = ws[at:at + 4 * S].view(torch.int32).cpu().tolist()
+    assert status == [1 if a else 0 for a in adv], status
+    kb = k.bfloat16().float()[:, 0]
+    want = torch.sort(torch.argsort(-kb, stable=True)[:2048]).values.int()
+    for t in range(S):
+        if adv[t]:
+            assert torch.equal(dense[0][t].cpu(), want), t
+    log(f"  {kind} S={S}: adversarial rows {sum(adv)} of {S}")
+
+
+def test_few_query_rows_in_passes():
+    """The no-allocation entry point sizes few-query passes to its 256 MiB
+    scratch: 1,500 decode rows at a 1M-token context (262,144 keys, about
+    200 KB of candidate lists, directory and sample per row) go in two
+    passes of 750, and equal the workspace call's single pass bit for bit."""
+    import dsa_indexer_score_amd as dsai
+    inp = _decode("c5_csa_1m", 1500, 262144)
+    ix = dsai.Indexer(inp.q.dtype, few_query_rows=4096, device=DEV)
+    kw = dict(m=inp.m, topk=inp.topk, causal=True, q_scale=inp.q_scale, k_scale=inp.k_scale,
+              q_pos0=inp.q_pos0, with_scores=True)
+    per_row = ix.workspace_bytes(1, inp.T, inp.H, inp.d, inp.m, inp.topk)
+    assert 1500 * per_row > 256 << 20 > 750 * per_row
+    ref = ix.score_topk(inp.q, inp.w, inp.k, **kw)
+    got = ix.score_topk_noalloc(inp.q, inp.w, inp.k, **kw)
+    torch.cuda.synchronize()
+    _assert_identical(ref, got)
+    assert (ref[1] == 2048).all()
