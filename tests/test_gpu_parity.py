@@ -85,6 +85,35 @@ def test_full_size_sampled_rows(name):
     assert torch.equal(vl, vl2) and torch.equal(idx, idx2)
 
 
+def test_full_size_query_chunk_sweep_is_bit_identical():
+    """The StreamIndex abstract's chunk sweep at the 256K-query workload's
+    full size: query chunks of 4K, 8K, 16K (the benchmark's) and 32K rows
+    give the same rows bit for bit (rows are independent; only the launch
+    sizes differ)."""
+    inp = gen.generate("c4_csa_256k", device=DEV)
+    ref = run(inp, with_scores=False, query_chunk=16384)
+    for chunk in (4096, 8192, 32768):
+        out = run(inp, with_scores=False, query_chunk=chunk)
+        assert torch.equal(out[1], ref[1]) and torch.equal(out[0], ref[0]), chunk
+
+
+@pytest.mark.parametrize("topk", [512, 1024, 4096])
+def test_full_size_topk_sweep_sampled_rows(topk):
+    """The abstract's top-k sweep at the 256K-query workload's full size (the
+    benchmark's 2048 is covered above): sampled rows against the oracle, and
+    every row's invariants on the device."""
+    inp = gen.generate("c4_csa_256k", topk=topk, device=DEV)
+    idx, vl, sc = run(inp)
+    device_invariants(inp, idx, vl)
+    rows = check.sample_rows(inp.S, m=inp.m, ksel=topk, chunk=inp.query_chunk, seed=inp.seed,
+                             n_uniform=64)
+    hi, hv, hs = rows_to_host(rows, idx, vl, sc)
+    rep = check.compare(inp, rows, hi, hv, hs)
+    log(f"  topk {topk}: rows {rep['rows']}, index-mismatch rows {rep['index_mismatch_rows']}, "
+        f"max score rel err {rep['max_score_rel_err']:.2e}")
+    assert rep["ok"], rep["failures"]
+
+
 def test_automatic_query_chunk_is_bit_identical():
     """query_chunk = 0 takes as many rows per launch as 4 GiB of candidate
     buffers hold (25,888 at the 256K workload): the same rows as the
