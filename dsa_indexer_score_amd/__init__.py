@@ -260,11 +260,14 @@ def score_topk(q, w, k, *, m: int = 1, topk: int, causal: bool = True, expand: b
         q_pos0=q_pos0, with_scores=with_scores, workspace=workspace)
 
 
-def screen_certificates(q: torch.Tensor, w: torch.Tensor, q_scale=None):
+def screen_certificates(q: torch.Tensor, w: torch.Tensor, q_scale=None, k=None, *, m: int = 1,
+                        causal: bool = True, q_pos0: int = 0):
     """The DoSA certificates the screened path builds for each row of q
-    [S, H, d] (33 <= H <= 64): (perm int32 [S, 64], weights [S, 64],
-    bound_weights [S, 32], knorm_coef [S]) on q's device; see
-    indexer_screen_certificates."""
+    [S, H, d] (33 <= H <= 64), with seeds from the keys k [T, d] (none when
+    k is None): (perm int32 [S, 64], weights [S, 64], bound_weights [S, 32],
+    knorm_coef [S], aggregate [S, d], activations int32 [S, 64]) on q's
+    device; see indexer_screen_certificates.  Rows without an aggregate
+    leave their aggregate row zero."""
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [S, H, d] tensor")
     S, H, d = q.shape
@@ -282,16 +285,25 @@ def screen_certificates(q: torch.Tensor, w: torch.Tensor, q_scale=None):
                                 q_scale.dtype != torch.float32 or
                                 not q_scale.is_contiguous() or q_scale.device != q.device):
         raise ValueError("q_scale must be contiguous float32 [S, H] on q's device")
+    T = 0
+    if k is not None:
+        if (k.dim() != 2 or k.shape[1] != d or k.dtype != q.dtype or not k.is_contiguous()
+                or k.device != q.device):
+            raise ValueError("k must be a contiguous [T, d] tensor of q's dtype and device")
+        T = k.shape[0]
     h = _handle(q.dtype, False, False, 0, 0, q.device)
     dev = h.device
     perm = torch.empty((S, 64), dtype=torch.int32, device=dev)
     wv = torch.empty((S, 64), dtype=torch.float32, device=dev)
     wt = torch.empty((S, 32), dtype=torch.float32, device=dev)
     e = torch.empty((S,), dtype=torch.float32, device=dev)
+    agg = torch.zeros((S, d), dtype=torch.float32, device=dev)
+    act = torch.empty((S, 64), dtype=torch.int32, device=dev)
     _lib.check(h._lib.indexer_screen_certificates(
-        h._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, S, H, d, _ptr(perm), _ptr(wv),
-        _ptr(wt), _ptr(e), _stream(dev)), "indexer_screen_certificates")
-    return perm, wv, wt, e
+        h._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, S, H, d, _ptr(k), T, int(m),
+        int(bool(causal)), int(q_pos0), _ptr(perm), _ptr(wv), _ptr(wt), _ptr(e), _ptr(agg),
+        _ptr(act), _stream(dev)), "indexer_screen_certificates")
+    return perm, wv, wt, e, agg, act
 
 
 def pair_overlap(idx: torch.Tensor, valid_len: torch.Tensor) -> torch.Tensor:

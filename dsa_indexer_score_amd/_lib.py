@@ -44,8 +44,8 @@ SIGNATURES = {
     "indexer_pair_overlap": (_I, [_P, _P, _I64, _I, _P, _P]),
     "indexer_pair_regions": (_I, [_P, _P, _I64, _I, _P, _P, _P, _P, _P]),
     "indexer_overlap_summary": (_I, [_P, _P, _I64, ctypes.POINTER(OverlapStats)]),
-    "indexer_screen_certificates": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _P, _P, _P,
-                                         _P]),
+    "indexer_screen_certificates": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _I, _P, _I64, _I, _I,
+                                         _I64, _P, _P, _P, _P, _P, _P, _P]),
     "indexer_strerror": (ctypes.c_char_p, [_I]),
     "indexer_source_hash": (ctypes.c_char_p, []),
 }

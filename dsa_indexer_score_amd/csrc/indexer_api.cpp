@@ -147,9 +147,10 @@ bool use_screen(const indexer_config &cfg, int H)
 // Streaming workspace: the candidate buffers [rows, cap] of (score bits,
 // key), then with screening the certificates of one launch's rows (head
 // order [rows, 64] i32, weights [rows, 64], bound weights [rows, 32], key
-// norm coefficient [rows]) and the key norms [T], each 256-byte aligned.
+// norm coefficient [rows], aggregate row [rows, 128]) and the key norms [T],
+// each 256-byte aligned.
 struct StreamLayout {
-    int64_t perm, w, wt, e, knorm, bytes;
+    int64_t perm, w, wt, e, agg, knorm, bytes;
     StreamLayout(int64_t rows, int64_t cap, int64_t T, bool screen)
     {
         bytes = rows * cap * (int64_t)sizeof(uint2);
@@ -158,7 +159,8 @@ struct StreamLayout {
         w = perm + round_up(rows * 64 * 4, 256);
         wt = w + round_up(rows * 64 * 4, 256);
         e = wt + round_up(rows * 32 * 4, 256);
-        knorm = e + round_up(rows * 4, 256);
+        agg = e + round_up(rows * 4, 256);
+        knorm = agg + round_up(rows * 128 * 4, 256);
         bytes = knorm + std::max<int64_t>(T, 1) * 4;
     }
 };
@@ -460,6 +462,7 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.cert_w = reinterpret_cast<float *>(base + L.w);
         p.cert_wt = reinterpret_cast<float *>(base + L.wt);
         p.cert_e = reinterpret_cast<float *>(base + L.e);
+        p.cert_agg = reinterpret_cast<float *>(base + L.agg);
         p.knorm = reinterpret_cast<float *>(base + L.knorm);
         bool supported = true;
         const hipError_t e = dsai::launch_key_norms(cfg.dtype, d, p, st, &supported);
@@ -666,17 +669,22 @@ const char *indexer_strerror(int code)
 
 extern "C" int indexer_screen_certificates(indexer_t h, const void *q, const float *q_scale,
                                            const float *w, int64_t w_stride_s, int64_t S, int H,
-                                           int d, int32_t *perm, float *weights,
-                                           float *bound_weights, float *knorm_coef, void *stream)
+                                           int d, const void *k, int64_t T, int m, int causal,
+                                           int64_t q_pos0, int32_t *perm, float *weights,
+                                           float *bound_weights, float *knorm_coef,
+                                           float *aggregate, int32_t *activations, void *stream)
 {
-    if (!h || S < 0 || H < 1 || d < 1) return IDX_EINVAL;
+    if (!h || S < 0 || H < 1 || d < 1 || T < 0 || m < 1 || q_pos0 < 0) return IDX_EINVAL;
+    if (causal != 0 && causal != 1) return IDX_EINVAL;
     if (w_stride_s != 0 && w_stride_s < H) return IDX_EINVAL;
     if (!shape_supported(h->cfg.dtype, H, d) || H <= 32 || H > 64) return IDX_EUNSUPPORTED;
     if (S == 0) return IDX_OK;
     const bool fp8 = h->cfg.dtype == IDX_FP8_E4M3;
-    if (!q || !w || !perm || !weights || !bound_weights || !knorm_coef) return IDX_EINVAL;
+    if (!q || !w || !perm || !weights || !bound_weights || !knorm_coef || !aggregate)
+        return IDX_EINVAL;
+    if (T > 0 && !k) return IDX_EINVAL;
     if (fp8 != (q_scale != nullptr)) return IDX_EINVAL;
-    if (!aligned(q, 16) || !aligned(w, 4)) return IDX_EINVAL;
+    if (!aligned(q, 16) || (k && !aligned(k, 16)) || !aligned(w, 4)) return IDX_EINVAL;
     DeviceGuard guard(h->device);
     if (guard.err != hipSuccess) return fail_hip(guard.err);
     dsai::ScoreSelectParams p{};
@@ -684,6 +692,11 @@ extern "C" int indexer_screen_certificates(indexer_t h, const void *q, const flo
     p.q_scale = q_scale;
     p.w = w;
     p.w_stride = w_stride_s;
+    p.k = k;
+    p.T = T;
+    p.m = m;
+    p.causal = causal;
+    p.q_pos0 = q_pos0;
     p.H = H;
     p.row0 = 0;
     p.nrows = S;
@@ -691,6 +704,8 @@ extern "C" int indexer_screen_certificates(indexer_t h, const void *q, const flo
     p.cert_w = weights;
     p.cert_wt = bound_weights;
     p.cert_e = knorm_coef;
+    p.cert_agg = aggregate;
+    p.cert_act = activations;
     bool supported = true;
     const hipError_t e =
         dsai::launch_certificates(h->cfg.dtype, d, p, static_cast<hipStream_t>(stream), &supported);

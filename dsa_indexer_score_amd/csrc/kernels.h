@@ -65,19 +65,23 @@ struct ScoreSelectParams {
     int ndoc;
     int varlen;             // 1: rows are packed documents (the fields above)
     // Screening (DoSA certificates), per row of the launch: head order with
-    // the kept heads first [nrows, 64] (-1 = no head), weights w * q_scale in
+    // the kept heads first [nrows, 64] (-1 = no head, kAggSlot = the
+    // aggregate row, always slot 31 when present), weights w * q_scale in
     // that order [nrows, 64], folded bound weights of the kept heads
     // [nrows, 32], key-norm coefficient [nrows]; key norms ||k_j|| [T].
     int32_t *cert_perm;
     float *cert_w;
     float *cert_wt;
     float *cert_e;
+    float *cert_agg;        // [nrows, d]: the aggregate row a~ (slot kAggSlot of the order)
+    int32_t *cert_act;      // [nrows, 64] or null: seed activation counts (inspection)
     float *knorm;
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves
 constexpr int kKeysPerTile = 128;     // keys staged in LDS per step
 constexpr int kSelGroup = 64;         // keys appended per selection step (one per lane)
+constexpr int kAggSlot = -2;          // screening: head order entry of the aggregate row
 constexpr int kFewBatch = 256;        // few-query: keys per candidate run (directory entry)
 constexpr int kSampleKeys = 8192;     // few-query: keys in a row's estimate sample
 constexpr int kFewCap = 8192;         // few-query: candidates the exact cut holds in LDS

@@ -214,6 +214,24 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) qa[b][ks] = O::zero();
         }
+        if constexpr (SCREEN) {
+            // the certificate's aggregate row: its values are operand values
+            // already (bf16-representable, or fp32), in load_a's slot order
+            if (active && head == kAggSlot) {
+                const float *ag = p.cert_agg + crow * D + hh * (D / 2);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if constexpr (DT == 0) {
+                        qa[b][ks] = ag[ks];
+                    } else {
+                        A v;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = (__bf16)ag[ks * 8 + e];
+                        qa[b][ks] = v;
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int h2 = 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);

@@ -308,37 +308,59 @@ int indexer_overlap_summary(const int32_t *shared, const int32_t *valid_len, int
                             indexer_overlap_stats *out);
 
 /* DoSA certificate screening ("DoSA: Dots Sparse Attention", summary page,
- * "Core method" and "Method steps").  With IDX_SCREEN in the flags, the
- * streaming path (not the few-query or packed-document paths) with
- * 33 <= H <= 64 first builds one certificate per query row: 32 kept heads
- * (all positive heads of the row plus the negative heads of largest
- * |w_h q_scale_h| ||q_h||, or the 32 positive heads of largest w_h
- * q_scale_h ||q_h|| when there are more), each omitted positive head folded
- * onto the kept positive head closest in direction, and a coefficient of
- * ||k|| that holds the residual allowance plus a rounding margin.  Every
- * key's upper bound U = sum_kept w~_h ReLU(q_h . k) + coef ||k|| (times
- * k_scale) is computed from the kept heads alone; a key with U below the
- * row's running Ksel-th score lower bound is not scored further, the others
- * get the remaining heads.  Lossless: the selection equals the unscreened
- * one up to the order in which the 64 head terms are summed (the kept heads
- * come first).  The workspace grows by 644 bytes per row of a launch plus 4
- * per key (indexer_workspace_bytes accounts for it).
+ * "Core method", "Method steps" and "Technical novelty").  With IDX_SCREEN
+ * in the flags, the streaming path (not the few-query or packed-document
+ * paths) with 33 <= H <= 64 first builds one certificate per query row from
+ * its head codes q_h, weights a_h = w_h q_scale_h and a seed set of its
+ * visible keys (256 keys spread evenly over them, or all of them):
+ *  - each head's activation frequency p_h on the seeds (share with
+ *    q_h . k > 0);
+ *  - a head budget r = 31 when H <= 63 (the last row of the kept block then
+ *    holds the aggregate below), else 32: all positive heads plus the
+ *    negative heads of largest |a_h| ||q_h|| min(p_h, 1 - p_h) when at most
+ *    r heads are positive, else the r positive heads of largest
+ *    a_h ||q_h||;
+ *  - each omitted positive head folded onto the kept positive head closest
+ *    in direction, its residual bounded jointly over the omitted heads;
+ *  - the omitted negative heads with p_h >= 1/2 summed into one aggregate
+ *    row a_A = sum |a_h| q_h, whose ReLU(a_A . k) the bound subtracts;
+ *  - a coefficient of ||k|| that holds the residual allowance, the
+ *    aggregate's rounding and a margin for fp32 rounding.
+ * Every key's upper bound U = sum_kept w~_h ReLU(q_h . k) - ReLU(a_A . k)
+ * + coef ||k|| (times k_scale) comes from the kept block alone; a key with
+ * U below the row's running Ksel-th score lower bound is not scored
+ * further, the others get the remaining heads.  Lossless: the selection
+ * equals the unscreened one up to the order in which the head terms are
+ * summed (the kept heads come first).  The workspace grows by 1156 bytes
+ * per row of a launch plus 4 per key (indexer_workspace_bytes accounts for
+ * it).
  *
  * indexer_screen_certificates writes the certificates of S rows as the
  * screened path uses them, for inspection:
  *   q, q_scale, w, w_stride: as for indexer_score_topk (device).
+ *   k, T, m, causal, q_pos0: the keys the seeds come from and the rows'
+ *     visibility, as for indexer_score_topk; k = NULL or T = 0 means no
+ *     seeds: every p_h is taken as 1/2 and there is no aggregate.
  *   perm: device int32 [S, 64], out: head order, kept heads first (by head
- *     index), then the omitted heads (by index), then -1.
+ *     index), then at slot 31 the aggregate (-2) when there is one, then
+ *     the omitted heads (by index), then -1.
  *   weights: device fp32 [S, 64], out: w_h * q_scale_h (w_h for bf16 and
- *     fp32) in that order.
- *   bound_weights: device fp32 [S, 32], out: the kept heads' folded weights.
+ *     fp32) in that order; 0 for the aggregate.
+ *   bound_weights: device fp32 [S, 32], out: the kept heads' folded weights
+ *     (-1 for the aggregate).
  *   knorm_coef: device fp32 [S], out: the coefficient of ||k|| (raw codes).
+ *   aggregate: device fp32 [S, d], out: a_A as the matrix unit reads it
+ *     (rounded to bf16 except for fp32 data); written only for rows that
+ *     have an aggregate.
+ *   activations: device int32 [S, 64] or NULL, out: seed count with
+ *     q_h . k > 0 per head (by head index; 0 past H).
  * Requires 33 <= H <= 64 (else IDX_EUNSUPPORTED).  Asynchronous on `stream`.
  */
 int indexer_screen_certificates(indexer_t h, const void *q, const float *q_scale, const float *w,
-                                int64_t w_stride, int64_t S, int H, int d, int32_t *perm,
+                                int64_t w_stride, int64_t S, int H, int d, const void *k,
+                                int64_t T, int m, int causal, int64_t q_pos0, int32_t *perm,
                                 float *weights, float *bound_weights, float *knorm_coef,
-                                void *stream);
+                                float *aggregate, int32_t *activations, void *stream);
 
 /* Static text for a status code, followed (for IDX_EHIP) by the calling
  * thread's last HIP error.  Never NULL. */

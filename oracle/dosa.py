@@ -55,17 +55,26 @@ def seed_threshold(scores_seed: np.ndarray, K: int) -> float:
     return float(s[K - 1])
 
 
-def certificate(q: np.ndarray, w: np.ndarray, seed_keys: np.ndarray, r: int):
+def certificate(q: np.ndarray, w: np.ndarray, seed_keys: np.ndarray, r: int, p=None):
     """Certificate of one query: q [H, d], w [H] (fp64), seed_keys [n, d].
     Returns dict(kept, w_fold, E, E_joint, aA, A, p) with U(k) = sum_kept
     w_fold [q k]_+ + E_joint ||k|| - [aA k]_+ (E in place of E_joint gives
-    the looser per-head allowance)."""
+    the looser per-head allowance).  p, when given, replaces the activation
+    frequencies measured on the seeds (which must then be non-empty): a
+    sign decided in another precision may differ for a dot product next to
+    zero, and the rest of the construction is then compared on equal
+    footing."""
     q = np.asarray(q, np.float64)
     w = np.asarray(w, np.float64)
     H = q.shape[0]
     X = q @ np.asarray(seed_keys, np.float64).T
     # no seed keys: no activation statistics, every p_h taken as 1/2
-    p = (X > 0).mean(axis=1) if X.shape[1] else np.full(H, 0.5)
+    if p is not None:
+        if not X.shape[1]:
+            raise ValueError("activation frequencies come from a non-empty seed set")
+        p = np.asarray(p, np.float64)
+    else:
+        p = (X > 0).mean(axis=1) if X.shape[1] else np.full(H, 0.5)
     norms = np.linalg.norm(q, axis=1)
     pos = [h for h in range(H) if w[h] > 0]
     neg = [h for h in range(H) if w[h] < 0]

@@ -216,14 +216,15 @@ def test_workspace_bytes_varlen_follow_the_path():
 
 def test_workspace_bytes_with_screening():
     """IDX_SCREEN adds, on the streaming path with 33 <= H <= 64, the
-    certificates of one launch's rows (644 bytes a row in four 256-byte
+    certificates of one launch's rows (1156 bytes a row in five 256-byte
     aligned parts) and 4 bytes per key; H <= 32 cannot screen."""
     up = lambda x, a: -(-x // a) * a
     n = ctypes.c_size_t()
     lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL | _lib.IDX_SCREEN, few=-1)
     S, T, cap = 100, 5000, up(5000, 64) + 64          # cap: every visible key fits
     base = S * cap * 8
-    want = up(base, 256) + 2 * up(S * 256, 256) + up(S * 128, 256) + up(S * 4, 256) + T * 4
+    want = (up(base, 256) + 2 * up(S * 256, 256) + up(S * 128, 256) + up(S * 4, 256)
+            + up(S * 512, 256) + T * 4)
     assert lib.indexer_workspace_bytes(h, S, T, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == want
     assert lib.indexer_workspace_bytes(h, S, T, 32, 128, 4, 2048, ctypes.byref(n)) == 0
@@ -237,23 +238,30 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails
 def test_screen_certificates_validation():
     """indexer_screen_certificates rejects what it cannot build before any
     device call: H outside 33..64 or an unsupported d, missing pointers, a
-    scale that does not match the dtype, misaligned q."""
+    scale that does not match the dtype, misaligned q or k, keys without a
+    pointer, a bad visibility rule."""
     lib, h = _handle()
     E, U = _lib.IDX_EINVAL, _lib.IDX_EUNSUPPORTED
     f = lambda **kw: lib.indexer_screen_certificates(
         h, kw.get("q", FAKE), kw.get("qs", None), kw.get("w", FAKE), kw.get("ws", 0),
-        kw.get("S", 4), kw.get("H", 64), kw.get("d", 128), kw.get("perm", FAKE),
-        kw.get("wv", FAKE), kw.get("wt", FAKE), kw.get("e", FAKE), None)
+        kw.get("S", 4), kw.get("H", 64), kw.get("d", 128), kw.get("k", FAKE),
+        kw.get("T", 16), kw.get("m", 4), kw.get("causal", 1), kw.get("pos0", 0),
+        kw.get("perm", FAKE), kw.get("wv", FAKE), kw.get("wt", FAKE), kw.get("e", FAKE),
+        kw.get("agg", FAKE), kw.get("act", None), None)
     assert f(S=0) == 0
     assert f(H=32) == U and f(H=65) == U and f(d=96) == U
-    assert f(q=None) == E and f(perm=None) == E and f(e=None) == E
+    assert f(q=None) == E and f(perm=None) == E and f(e=None) == E and f(agg=None) == E
     assert f(qs=FAKE) == E                                # scales only for fp8
     assert f(q=ctypes.c_void_p(0x10008)) == E
+    assert f(k=ctypes.c_void_p(0x10008)) == E
+    assert f(k=None) == E                                 # T > 0 keys need a pointer
+    assert f(m=0) == E and f(causal=2) == E and f(pos0=-1) == E and f(T=-1) == E
     assert f(ws=10) == E                                  # w rows would overlap
     lib.indexer_destroy(h)
     lib, h = _handle(dtype=_lib.IDX_FP8_E4M3)
     f8 = lambda **kw: lib.indexer_screen_certificates(h, FAKE, kw.get("qs", None), FAKE, 0, 4, 64,
-                                                      128, FAKE, FAKE, FAKE, FAKE, None)
+                                                      128, None, 0, 1, 1, 0, FAKE, FAKE, FAKE,
+                                                      FAKE, FAKE, None, None)
     assert f8() == E                                      # fp8 needs q_scale
     lib.indexer_destroy(h)
 

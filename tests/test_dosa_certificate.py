@@ -86,6 +86,37 @@ def test_without_seeds_negative_heads_rank_by_weighted_norm():
     assert np.all(dosa.upper_bounds(cert, keys) >= _scores(q, w, keys) - 1e-9)
 
 
+def test_given_activation_frequencies_replace_the_measured_ones():
+    """certificate(..., p=...) takes the activation frequencies as given: the
+    measured ones reproduce the default certificate; moving one omitted
+    negative head across 1/2 moves it into or out of the majority-active set
+    and the aggregate by exactly |w_h| q_h; frequencies without seeds are
+    refused."""
+    rng = np.random.default_rng(21)
+    H, d = 40, 16
+    q = rng.standard_normal((H, d))
+    w = rng.standard_normal(H)
+    seeds = rng.standard_normal((300, d))
+    base = dosa.certificate(q, w, seeds, r=20)
+    same = dosa.certificate(q, w, seeds, r=20, p=base["p"])
+    assert same["kept"] == base["kept"] and same["A"] == base["A"]
+    np.testing.assert_array_equal(same["aA"], base["aA"])
+    omitted = [h for h in range(H)
+               if w[h] < 0 and h not in base["kept"] and base["p"][h] != 0.5]
+    assert omitted
+    h = omitted[0]
+    # p -> 1 - p keeps the priority min(p, 1 - p), so the kept set stays
+    p = base["p"].copy()
+    p[h] = 1 - p[h]
+    moved = dosa.certificate(q, w, seeds, r=20, p=p)
+    assert moved["kept"] == base["kept"]
+    assert (h in moved["A"]) != (h in base["A"])
+    sign = 1.0 if h in moved["A"] else -1.0
+    np.testing.assert_allclose(moved["aA"] - base["aA"], sign * abs(w[h]) * q[h], atol=1e-12)
+    with pytest.raises(ValueError):
+        dosa.certificate(q, w, np.zeros((0, d)), r=20, p=np.full(H, 0.5))
+
+
 def test_seed_threshold_is_a_lower_bound_of_the_kth_score():
     rng = np.random.default_rng(5)
     s = rng.standard_normal(5000)

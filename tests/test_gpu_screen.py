@@ -2,8 +2,9 @@
 
 "DoSA: Dots Sparse Attention" (summary page, "Core method", "Method
 steps"): certificates are checked against the oracle's construction
-(oracle/dosa.py, empty seed set) and against their defining inequality
-U >= s on every key; the screened selection is lossless, so it passes the
+(oracle/dosa.py, with the seed activation counts the GPU measured, or
+an empty seed set) and against their defining inequality U >= s on every
+key; the screened selection is lossless, so it passes the
 oracle's tolerance rule, and on integer-valued inputs (every sum exact in
 any order) it equals the unscreened selection bit for bit.
 """
@@ -25,44 +26,82 @@ def _real(t):
     return t.float().double().cpu().numpy()
 
 
-def _cert_rows(inp, rows):
+def _cert_rows(inp, rows, seeds):
     import dsa_indexer_score_amd as dsai
-    perm, wv, wt, e = dsai.screen_certificates(inp.q, inp.w, inp.q_scale)
+    out = dsai.screen_certificates(inp.q, inp.w, inp.q_scale, inp.k if seeds else None,
+                                   m=inp.m, causal=inp.causal, q_pos0=inp.q_pos0)
     torch.cuda.synchronize()
-    return perm.cpu().numpy()[rows], wv.cpu().numpy()[rows], wt.cpu().numpy()[rows], \
-        e.cpu().numpy()[rows]
+    return [x.cpu().numpy()[rows] for x in out]
 
 
-def _check_certificates(inp, rows, keys_real, kscale):
+def _seed_positions(inp, t):
+    """The seed set the certificate uses: n_s = min(P, 256) of the row's P
+    visible keys, key i P // n_s for i < n_s."""
+    P = min((inp.q_pos0 + t + 1) // inp.m, inp.T) if inp.causal else inp.T
+    ns = min(P, 256)
+    return (np.arange(ns, dtype=np.int64) * P) // max(ns, 1)
+
+
+def _check_certificates(inp, rows, keys_real, kscale, seeds=True):
     """GPU certificates of the given rows against the oracle's and against
-    U >= s on every key (fp64 evaluation of the GPU's numbers)."""
-    perm, wv, wt, e = _cert_rows(inp, rows)
+    U >= s on every key (fp64 evaluation of the GPU's numbers).  Seed
+    activation counts must equal the fp64 counts except for dot products
+    within rounding of zero; the oracle then takes the GPU's counts, so the
+    rest of the construction is compared on equal footing."""
+    perm, wv, wt, e, agg, act = _cert_rows(inp, rows, seeds)
     q = _real(inp.q)
     qs = np.ones((inp.S, inp.H)) if inp.q_scale is None else _real(inp.q_scale)
     w = _real(inp.w)
     w = np.broadcast_to(w, (inp.S, inp.H)) if w.ndim == 1 else w
-    folds = 0
+    stats = dict(folds=0, aggregates=0, agg_heads=0)
+    H = inp.H
     for n, t in enumerate(rows):
-        H = inp.H
-        assert sorted(perm[n][perm[n] >= 0].tolist()) == list(range(H))
         a = w[t] * qs[t]
-        np.testing.assert_allclose(wv[n][:H], a[perm[n][:H]], rtol=1e-6)
         qreal = q[t] * qs[t][:, None]
-        cert = dosa.certificate(qreal, w[t], np.zeros((0, inp.d)), r=32)
-        kept = perm[n][:32]
+        C = np.sum(np.abs(a) * np.linalg.norm(q[t], axis=1))
+        sp = _seed_positions(inp, t) if seeds else np.zeros(0, np.int64)
+        ns = sp.size
+        X = q[t] @ keys_real[sp].T                       # codes: signs ignore the scales
+        cnt = (X > 0).sum(axis=1)
+        near = (np.abs(X) <= 1e-5 * np.linalg.norm(q[t], axis=1)[:, None]
+                * np.linalg.norm(keys_real[sp], axis=1)[None, :]).sum(axis=1)
+        assert np.all(np.abs(act[n][:H] - cnt) <= near), (t, act[n][:H] - cnt)
+        assert np.all(act[n][H:] == 0)
+        has_agg = ns > 0 and H <= 63
+        r = 31 if has_agg else 32
+        cert = dosa.certificate(qreal, w[t], keys_real[sp], r=r,
+                                p=act[n][:H] / ns if ns else None)
+        heads = perm[n][perm[n] >= 0]
+        assert sorted(heads.tolist()) == list(range(H)), t
+        kept = perm[n][:r]
         assert sorted(kept.tolist()) == sorted(cert["kept"]), t
+        assert list(kept) == sorted(kept), t                # by head index
+        assert (perm[n][31] == -2) == has_agg, t
+        np.testing.assert_allclose(wv[n][perm[n] >= 0], a[heads], rtol=1e-6)
         fold_of = dict(zip(cert["kept"], cert["w_fold"]))
         want_wt = np.array([qs[t][j] * fold_of[j] for j in kept])
-        np.testing.assert_allclose(wt[n], want_wt, rtol=2e-5, atol=1e-6 * np.abs(a).max())
-        C = np.sum(np.abs(a) * np.linalg.norm(q[t], axis=1))
-        assert cert["E"] * (1 - 1e-5) <= e[n] <= cert["E"] * (1 + 1e-4) + 1e-3 * C, t
-        folds += cert["E"] > 0
+        np.testing.assert_allclose(wt[n][:r], want_wt, rtol=2e-5, atol=1e-6 * np.abs(a).max())
+        aA = cert["aA"]
+        if has_agg:
+            assert wt[n][31] == -1.0 and wv[n][31] == 0.0, t
+            # a_A rounded to bf16 (fp32 data: fp32 rounding of the sum)
+            rel = 2.0 ** -8 if inp.q.dtype != torch.float32 else 1e-6
+            np.testing.assert_allclose(agg[n], aA, rtol=rel, atol=1e-5 * C)
+            stats["aggregates"] += 1
+            stats["agg_heads"] += len(cert["A"])
+        lo = min(cert["E"], cert["E_joint"])
+        slack = 2.0 ** -8 * np.linalg.norm(aA) + 1e-3 * C
+        assert lo * (1 - 1e-4) - 1e-6 * C <= e[n] <= lo * (1 + 1e-4) + slack, t
+        stats["folds"] += cert["E"] > 0
         # the bound, evaluated in fp64 from the GPU's numbers, covers every key
         s = a @ np.maximum(q[t] @ keys_real.T, 0.0)
-        U = wt[n] @ np.maximum(q[t][kept] @ keys_real.T, 0.0) + \
+        kh = perm[n][:32]
+        U = wt[n][:r] @ np.maximum(q[t][kh[:r]] @ keys_real.T, 0.0) + \
             e[n] * np.linalg.norm(keys_real, axis=1)
+        if has_agg:
+            U -= np.maximum(keys_real @ agg[n], 0.0)
         assert np.all(U * kscale >= s * kscale - 1e-12), t
-    return folds
+    return stats
 
 
 @pytest.mark.parametrize("name", ["c4_csa_256k", "c5_csa_1m", "c3_dsa_token"])
@@ -71,8 +110,10 @@ def test_certificates_match_oracle(name):
     rows = np.arange(0, 64, 3)
     k = _real(inp.k)
     ks = np.ones(inp.T) if inp.k_scale is None else _real(inp.k_scale)
-    folds = _check_certificates(inp, rows, k, ks)
-    log(f"  {name}: {rows.size} rows, {folds} with folded positive heads")
+    st = _check_certificates(inp, rows, k, ks)
+    log(f"  {name}: {rows.size} rows, {st}")
+    st0 = _check_certificates(inp, rows, k, ks, seeds=False)
+    assert st0["aggregates"] == 0
 
 
 def _many_positive(S, H, d, T, dtype, shared, seed):
@@ -101,8 +142,63 @@ def test_certificates_fold_positive_heads(dtype, H, d):
     rows = np.arange(24)
     k = _real(inp.k)
     ks = np.ones(inp.T) if inp.k_scale is None else _real(inp.k_scale)
-    folds = _check_certificates(inp, rows, k, ks)
-    assert folds == rows.size
+    st = _check_certificates(inp, rows, k, ks)
+    assert st["folds"] == rows.size
+    assert st["aggregates"] == (rows.size if H <= 63 else 0)
+    log(f"  {dtype} H={H} d={d}: {st}")
+
+
+def _skewed(S, H, d, T, dtype, seed):
+    """Heads whose activation frequencies sit far from 1/2: keys share a
+    direction u, each head leans towards +u or -u; weights are signed at
+    random (about half negative), so majority-active negative heads exist
+    and the seed statistics decide which negative heads are kept."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    lean = torch.where(torch.rand(S, H, generator=g) < 0.5, -1.0, 1.0)
+    q = (torch.randn(S, H, d, generator=g) / d ** 0.5 + 1.5 * lean[..., None] * u) / 2
+    k = torch.randn(T, d, generator=g) / d ** 0.5 + u
+    w = torch.randn(S, H, generator=g)
+    fp8 = dtype == torch.float8_e4m3fn
+    if fp8:
+        qs = q.abs().amax(-1) / 448 + 1e-12
+        ks = k.abs().amax(-1) / 448 + 1e-12
+        q, k = (q / qs[..., None]).to(dtype), (k / ks[:, None]).to(dtype)
+    else:
+        q, k, qs, ks = q.to(dtype), k.to(dtype), None, None
+    return gen.custom(q=q, k=k, w=w, topk=64, q_scale=qs, k_scale=ks)
+
+
+@pytest.mark.parametrize("dtype,H,d", [(torch.bfloat16, 48, 128), (torch.bfloat16, 63, 64),
+                                       (torch.float8_e4m3fn, 56, 128),
+                                       (torch.float32, 40, 64), (torch.bfloat16, 64, 128)])
+def test_certificates_with_seed_statistics(dtype, H, d):
+    """Skewed activation frequencies: the seed counts, the negative heads
+    kept by |a_h| ||q_h|| min(p_h, 1 - p_h), the aggregate of the
+    majority-active omitted negative heads (H <= 63) and U >= s on every
+    key, against the oracle."""
+    inp = _skewed(20, H, d, 900, dtype, 5 * H + d).to(DEV)
+    rows = np.arange(20)
+    k = _real(inp.k)
+    ks = np.ones(inp.T) if inp.k_scale is None else _real(inp.k_scale)
+    st = _check_certificates(inp, rows, k, ks)
+    log(f"  {dtype} H={H} d={d}: {st}")
+    if H <= 63:
+        assert st["aggregates"] == rows.size and st["agg_heads"] >= rows.size
+
+
+@pytest.mark.parametrize("dtype,H,d", [(torch.bfloat16, 48, 128), (torch.float8_e4m3fn, 56, 64),
+                                       (torch.float32, 40, 32)])
+def test_screened_selection_with_aggregate(dtype, H, d):
+    """Screened selection with the aggregate row in use (skewed activation
+    frequencies, H <= 63): lossless against the oracle's rule."""
+    inp = _skewed(1200, H, d, 1200, dtype, 7 * H + d).to(DEV)
+    idx, vl, sc = run(inp, screen=True)
+    rows = np.arange(0, 1200, 5)
+    rep = check.compare(inp, rows, idx.cpu().numpy()[rows], vl.cpu().numpy()[rows],
+                        sc.cpu().numpy()[rows])
+    assert rep["ok"], rep["failures"][:3]
 
 
 @pytest.mark.parametrize("name,S", [("c4_csa_256k", 3000), ("c3_dsa_token", 2500),
