@@ -142,12 +142,14 @@ def cpu_baseline(inp, budget_s, seed, docs=None):
 
 
 def host_streamed(args, inp, ix, W, dev):
-    """The workload with q (and its scales) in pinned host memory: each query
-    chunk is uploaded, scored at its absolute position (q_pos0), and its
-    index rows downloaded into pinned host memory, one chunk after another
-    on one stream.  Device memory then holds the keys, one chunk of q and of
-    idx, and one chunk's workspace; the peak is reported beside the step
-    time, which includes the PCIe transfers (so it is never the headline)."""
+    """The workload with q (and its scales) and the outputs in pinned host
+    memory: each query chunk is uploaded, scored at its absolute position
+    (q_pos0) and its index rows downloaded.  Two buffers per device array
+    and one copy stream per direction (default priority) let the upload of
+    chunk i+1 and the download of chunk i-1 run while chunk i is scored.
+    Device memory then holds the keys, two chunks of q and of idx, and one
+    chunk's workspace; the peak is reported beside the step time, which
+    includes the PCIe transfers (so it is never the headline)."""
     import torch
     S, chunk = inp.S, inp.query_chunk or inp.S
     q_h = torch.empty(inp.q.shape, dtype=inp.q.dtype, pin_memory=True)
@@ -164,24 +166,49 @@ def host_streamed(args, inp, ix, W, dev):
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats(dev)
     H, d = q_h.shape[1], q_h.shape[2]
-    q_d = torch.empty((chunk, H, d), dtype=q_h.dtype, device=dev)
-    qs_d = None if qs_h is None else torch.empty((chunk, H), dtype=torch.float32, device=dev)
-    idx_d = torch.empty((chunk, W), dtype=torch.int32, device=dev)
-    vl_d = torch.empty((chunk,), dtype=torch.int32, device=dev)
+    q_d = [torch.empty((chunk, H, d), dtype=q_h.dtype, device=dev) for _ in range(2)]
+    qs_d = [None if qs_h is None else torch.empty((chunk, H), dtype=torch.float32, device=dev)
+            for _ in range(2)]
+    idx_d = [torch.empty((chunk, W), dtype=torch.int32, device=dev) for _ in range(2)]
+    vl_d = [torch.empty((chunk,), dtype=torch.int32, device=dev) for _ in range(2)]
     ws = torch.empty((ix.workspace_bytes(chunk, inp.T, H, d, inp.m, inp.topk),), dtype=torch.uint8,
                      device=dev)
+    comp = torch.cuda.current_stream(dev)
+    up, down = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    starts = list(range(0, S, chunk))
+    ev = lambda: [torch.cuda.Event() for _ in range(2)]
+    up_done, comp_done, down_done = ev(), ev(), ev()
+
+    def upload(i):
+        b, r0 = i % 2, starts[i]
+        n = min(chunk, S - r0)
+        with torch.cuda.stream(up):
+            if i >= 2:
+                up.wait_event(comp_done[b])          # chunk i-2 no longer reads q_d[b]
+            q_d[b][:n].copy_(q_h[r0:r0 + n], non_blocking=True)
+            if qs_h is not None:
+                qs_d[b][:n].copy_(qs_h[r0:r0 + n], non_blocking=True)
+            up_done[b].record(up)
 
     def step():
-        for r0 in range(0, S, chunk):
-            n = min(chunk, S - r0)
-            q_d[:n].copy_(q_h[r0:r0 + n], non_blocking=True)
-            if qs_d is not None:
-                qs_d[:n].copy_(qs_h[r0:r0 + n], non_blocking=True)
-            ix.score_topk(q_d[:n], w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
-                          q_scale=None if qs_d is None else qs_d[:n], k_scale=inp.k_scale,
-                          q_pos0=r0, workspace=ws, out=(idx_d[:n], vl_d[:n], None))
-            idx_h[r0:r0 + n].copy_(idx_d[:n], non_blocking=True)
-            vl_h[r0:r0 + n].copy_(vl_d[:n], non_blocking=True)
+        upload(0)
+        for i, r0 in enumerate(starts):
+            b, n = i % 2, min(chunk, S - r0)
+            if i + 1 < len(starts):
+                upload(i + 1)
+            comp.wait_event(up_done[b])
+            if i >= 2:
+                comp.wait_event(down_done[b])        # idx_d[b] of chunk i-2 downloaded
+            ix.score_topk(q_d[b][:n], w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
+                          q_scale=None if qs_h is None else qs_d[b][:n], k_scale=inp.k_scale,
+                          q_pos0=r0, workspace=ws, out=(idx_d[b][:n], vl_d[b][:n], None))
+            comp_done[b].record(comp)
+            with torch.cuda.stream(down):
+                down.wait_event(comp_done[b])
+                idx_h[r0:r0 + n].copy_(idx_d[b][:n], non_blocking=True)
+                vl_h[r0:r0 + n].copy_(vl_d[b][:n], non_blocking=True)
+                down_done[b].record(down)
+        comp.wait_stream(down)
 
     for _ in range(args.warmup):
         step()
@@ -239,6 +266,13 @@ def main():
                          "downloaded: reports peak device bytes and the PCIe-inclusive time")
     ap.add_argument("--fp8-mfma", action="store_true",
                     help="e4m3 workloads: contract the codes on the fp8 MFMA (IDX_FP8_MFMA)")
+    ap.add_argument("--heads", type=int, default=0, metavar="H",
+                    help="override the workload's head count (1..64)")
+    ap.add_argument("--witness", action="store_true",
+                    help="--decode: each row's witnesses are the selection of the row one "
+                         "position earlier (the previous decode step)")
+    ap.add_argument("--rho", type=float, default=None,
+                    help="AR(1) correlation of adjacent queries (default: the workload's)")
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="few-query shape: N query rows at the end of the workload's full "
                          "context (every key visible), timed through the few-query path")
@@ -259,6 +293,8 @@ def main():
     log(f"bench: library {dsai.library_path()}")
     t0 = time.perf_counter()
     over = {"wdist": args.wdist} if args.wdist else {}
+    if args.heads:
+        over["H"] = args.heads
     if args.decode_batch:
         from dataclasses import replace
         full_T = gen.CONFIGS[args.workload]["T"]
@@ -269,8 +305,13 @@ def main():
         from dataclasses import replace
         m = gen.CONFIGS[args.workload]["m"]
         full_T = args.context // m if args.context else gen.CONFIGS[args.workload]["T"]
-        inp = gen.generate(args.workload, S=args.decode, T=full_T, device=dev, **over)
-        inp = replace(inp, q_pos0=full_T * inp.m - args.decode, query_chunk=None)
+        if args.rho is not None:
+            over["rho"] = args.rho
+        # --witness: one more row first; it is selected untimed and its
+        # selection is the next row's witnesses (the previous decode step)
+        S_gen = args.decode + (1 if args.witness else 0)
+        inp = gen.generate(args.workload, S=S_gen, T=full_T, device=dev, **over)
+        inp = replace(inp, q_pos0=full_T * inp.m - S_gen, query_chunk=None)
     else:
         inp = gen.generate(args.workload, S=args.S or None, topk=args.topk or None,
                            device=dev, **over)
@@ -290,6 +331,20 @@ def main():
                       screen=args.screen, fp8_mfma=args.fp8_mfma, device=dev)
     W = dsai.output_width(inp.topk, inp.m, inp.expand, inp.tail)
     ksel = inp.topk // inp.m if inp.expand else inp.topk
+    witness = None
+    if args.witness:
+        if not args.decode:
+            raise SystemExit("--witness applies to --decode")
+        from dataclasses import replace
+        prev_w = inp.w if inp.w.dim() == 1 else inp.w[:-1]
+        witness = ix.score_topk(inp.q[:-1], prev_w, inp.k, m=inp.m, topk=inp.topk,
+                                causal=inp.causal,
+                                q_scale=None if inp.q_scale is None else inp.q_scale[:-1],
+                                k_scale=inp.k_scale, q_pos0=inp.q_pos0)[0]
+        inp = replace(inp, q=inp.q[1:].contiguous(), S=inp.S - 1, q_pos0=inp.q_pos0 + 1,
+                      q_scale=None if inp.q_scale is None else inp.q_scale[1:].contiguous(),
+                      w=inp.w if inp.w.dim() == 1 else inp.w[1:].contiguous())
+        torch.cuda.synchronize()
     docs = None
     if args.varlen:
         # N equal documents; document i owns rows [i*L, (i+1)*L) and its own
@@ -343,7 +398,7 @@ def main():
         else:
             ix.score_topk(inp.q, inp.w, inp.k, m=inp.m, topk=inp.topk, causal=inp.causal,
                           q_scale=inp.q_scale, k_scale=inp.k_scale, q_pos0=inp.q_pos0,
-                          workspace=ws, out=(idx, vl, None))
+                          workspace=ws, out=(idx, vl, None), witness=witness)
 
     if args.graph:
         # The step captured once (score_topk and pair_overlap as two graphs,
@@ -403,8 +458,11 @@ def main():
                   "fp8": "fp8" if args.fp8_mfma and inp.d in (64, 128) and not args.screen
                   else "bf16"}[inp.dtype]
     peak = PEAK_TFLOPS[mfma_dtype]
-    traffic = stored_traffic() if not (args.decode or args.decode_batch or args.varlen or
-                                       args.screen) else None
+    # the committed counters are for the default 256K-query workload only
+    default_run = (args.workload == "c4_csa_256k" and not (
+        args.decode or args.decode_batch or args.varlen or args.screen or args.heads or args.S
+        or args.topk or args.chunk or args.wdist or args.fp8_mfma or args.graph))
+    traffic = stored_traffic() if default_run else None
 
     st = dsai.overlap_summary(shared, vl)
     regions = None
@@ -464,7 +522,8 @@ def main():
                      inp.S * (W + 1) * 4)
         gbs = alg_bytes / score_s / 1e9
         dtraffic = None
-        if args.workload == "c5_csa_1m" and args.decode == 1 and not args.wdist:
+        if (args.workload == "c5_csa_1m" and args.decode == 1 and not args.wdist and
+                not args.witness and args.rho is None):
             dtraffic = stored_traffic(DECODE_PMC_SUMMARY, DECODE_SRCS, "traffic_bytes_per_step")
         roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": gbs / HBM_PEAK_GBS, "traffic": dtraffic,
@@ -489,7 +548,8 @@ def main():
                    "m": inp.m, "topk": inp.topk, "causal": inp.causal, "query_chunk":
                    inp.query_chunk, "launches_per_step": n_launch, "screen": bool(args.screen),
                    "wdist": inp.meta.get("wdist"), "graph": bool(args.graph),
-                   "fp8_mfma": bool(args.fp8_mfma),
+                   "fp8_mfma": bool(args.fp8_mfma), "witness": bool(args.witness),
+                   "rho": args.rho,
                    "parallelism": "none (1 GPU)"},
         "queries_per_s": inp.S / (ms_per_step / 1e3),
         "mfma_frac": achieved_tflops / peak,

@@ -159,19 +159,30 @@ class Indexer:
 
     def score_topk(self, q, w, k, *, m: int = 1, topk: int, causal: bool = True,
                    q_scale=None, k_scale=None, q_pos0: int = 0, with_scores: bool = False,
-                   workspace: Optional[torch.Tensor] = None, out=None):
+                   workspace: Optional[torch.Tensor] = None, out=None, witness=None):
         """q [S,H,d], w [S,H] or [H] (fp32), k [T,d] -> (idx [S,W] int32,
         valid_len [S] int32[, sel_score [S,W] fp32]) on q's device.  out =
-        (idx, valid_len, sel_score or None) writes into the caller's tensors."""
+        (idx, valid_len, sel_score or None) writes into the caller's tensors.
+        witness (int32 [S, n] on q's device, e.g. the rows' idx of an earlier
+        step) goes through indexer_score_topk_witness."""
         S, H, d, T, w_stride = self._inputs(q, w, k, q_scale, k_scale)
         W = output_width(topk, m, self.expand, self.tail)
         idx, valid_len, sel = self._outputs(S, W, with_scores, out)
         workspace = self._workspace(self.workspace_bytes(S, T, H, d, m, topk), workspace)
-        rc = self._lib.indexer_score_topk(
-            self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S, T, H,
-            d, m, topk, int(bool(causal)), int(q_pos0), _ptr(idx), _ptr(valid_len), _ptr(sel),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(self.device))
-        _lib.check(rc, "indexer_score_topk")
+        common = (self._h, _ptr(q), _ptr(q_scale), _ptr(w), w_stride, _ptr(k), _ptr(k_scale), S,
+                  T, H, d, m, topk, int(bool(causal)), int(q_pos0))
+        tail = (_ptr(idx), _ptr(valid_len), _ptr(sel), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(self.device))
+        if witness is None:
+            rc = self._lib.indexer_score_topk(*common, *tail)
+            _lib.check(rc, "indexer_score_topk")
+        else:
+            if (witness.dim() != 2 or witness.shape[0] != S or witness.dtype != torch.int32
+                    or witness.device != self.device or not witness.is_contiguous()):
+                raise ValueError("witness must be a contiguous int32 [S, n] tensor on the device")
+            n = witness.shape[1]
+            rc = self._lib.indexer_score_topk_witness(*common, _ptr(witness), n, n, *tail)
+            _lib.check(rc, "indexer_score_topk_witness")
         return (idx, valid_len, sel) if with_scores else (idx, valid_len)
 
 

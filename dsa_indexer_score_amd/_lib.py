@@ -37,6 +37,8 @@ SIGNATURES = {
                                 _I64, _P, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk_noalloc": (_I, [_P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I, _I, _I,
                                         _I, _I, _I64, _P, _P, _P, _P]),
+    "indexer_score_topk_witness": (_I, [_P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I, _I, _I,
+                                        _I, _I, _I64, _P, _I64, _I, _P, _P, _P, _P, _SZ, _P]),
     "indexer_score_topk_varlen": (_I, [_P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I, _I, _I, _I,
                                        _I, _P, _P, _P, _P, _I, _I64, _P, _P, _P, _P, _SZ, _P]),
     "indexer_workspace_bytes_varlen": (_I, [_P, _I64, _I64, _I, _I, _I, _I, _I, _I64,

@@ -95,7 +95,7 @@ constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
 constexpr int64_t kRowsKernelMax = 2;  // rows scored with q in registers, keys from HBM
 
 // Few-query workspace for R rows of at most Tk keys each: the rows' key
-// samples [R, kSampleKeys] (f32), threshold estimates [R] (u32), candidate
+// sample and witness scores [R, kSampStride] (f32), threshold estimates [R] (u32), candidate
 // sub-list counts [R, kFewSub] (u32), repair marks [R] (i32), the directory
 // of candidate batches [R, nbatch] of (offset, count), and the candidate
 // sub-lists [R, cap] of (score bits, key), each 256-byte aligned.  cap also holds the
@@ -108,7 +108,7 @@ struct FewLayout {
     {
         nbatch = (std::max<int64_t>(Tk, 1) + dsai::kFewBatch - 1) / dsai::kFewBatch;
         cap = std::max<int64_t>(dsai::kFewSub * dsai::kFewSubCap, capacity(ksel, Tk));
-        est = round_up(R * dsai::kSampleKeys * 4, 256);
+        est = round_up(R * dsai::kSampStride * 4, 256);
         cnt = est + round_up(R * 4, 256);
         stat = cnt + round_up(R * dsai::kFewSub * 4, 256);
         dir = stat + round_up(R * 4, 256);
@@ -253,6 +253,12 @@ struct Docs {  // packed-document layout (varlen); on = false: one document
     int64_t row_keys = 0;  // keys per row of the few-query path
 };
 
+struct Witness {  // earlier selections of the rows (few-query path only)
+    const int32_t *ptr = nullptr;
+    int64_t stride = 0;
+    int n = 0;
+};
+
 // Keys per few-query row for packed documents: the caller's bound on a
 // document's keys (0: unknown), at most T.
 int64_t doc_row_keys(int64_t max_doc_keys, int64_t T)
@@ -281,9 +287,12 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
                     int64_t w_stride_s, const void *k, const float *k_scale, int64_t S, int64_t T,
                     int H, int d, int m, int topk, int causal, int64_t q_pos0, const Docs &docs,
                     int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
-                    size_t workspace_bytes, void *stream, int64_t fit_bytes = 0)
+                    size_t workspace_bytes, void *stream, int64_t fit_bytes = 0,
+                    const Witness &wit = Witness{})
 {
     if (!h) return IDX_EINVAL;
+    if (wit.n < 0 || (wit.n > 0 && (!wit.ptr || wit.stride < wit.n || !aligned(wit.ptr, 4))))
+        return IDX_EINVAL;
     const indexer_config &cfg = h->cfg;
     const int flags = cfg.flags;
     const bool expand = flags & IDX_EXPAND, tail = flags & IDX_TAIL;
@@ -412,6 +421,11 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         p.nbatch = L.nbatch;
         p.row_keys = Tk;
         p.split_keys = round_up(std::max<int64_t>(T, 1), dsai::kFewBatch);
+        if (wit.n > 0 && !docs.on) {
+            p.witness = wit.ptr;
+            p.wit_stride = wit.stride;
+            p.nwit = wit.n;
+        }
         for (int64_t r0 = 0; r0 < S; r0 += Rp) {
             p.row0 = r0;
             p.nrows = std::min(Rp, S - r0);
@@ -500,6 +514,22 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
     return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
                            q_pos0, Docs{}, idx, valid_len, sel_score, workspace, workspace_bytes,
                            stream);
+}
+
+int indexer_score_topk_witness(indexer_t h, const void *q, const float *q_scale, const float *w,
+                               int64_t w_stride_s, const void *k, const float *k_scale,
+                               int64_t S, int64_t T, int H, int d, int m, int topk, int causal,
+                               int64_t q_pos0, const int32_t *witness, int64_t witness_stride,
+                               int nwit, int32_t *idx, int32_t *valid_len, float *sel_score,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    Witness wit;
+    wit.ptr = witness;
+    wit.stride = witness_stride;
+    wit.n = nwit;
+    return score_topk_impl(h, q, q_scale, w, w_stride_s, k, k_scale, S, T, H, d, m, topk, causal,
+                           q_pos0, Docs{}, idx, valid_len, sel_score, workspace, workspace_bytes,
+                           stream, 0, wit);
 }
 
 int indexer_score_topk_noalloc(indexer_t h, const void *q, const float *q_scale, const float *w,

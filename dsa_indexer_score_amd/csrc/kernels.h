@@ -38,11 +38,20 @@ struct ScoreSelectParams {
     // sub-list's count fq_cnt[row * kFewSub + b % kFewSub] -- so concurrent
     // appends of one row spread over kFewSub counters; fq_dir[row * nbatch +
     // b] = (offset in the sub-list, count) of batch b.
-    // samp[row * kSampleKeys ...] holds the exact scores of a key sample from
-    // which est[row] is estimated; status[row] = 1 leaves the row to the
-    // streaming kernel (repair).  row_keys bounds the keys of a row (packed
-    // documents: the caller's max_doc_keys); nbatch = its batches.
+    // samp[row * kSampStride ...] holds the exact scores of a key sample
+    // from which est[row] is estimated, then of the row's witness keys;
+    // status[row] = 1 leaves the row to the streaming kernel (repair).
+    // row_keys bounds the keys of a row (packed documents: the caller's
+    // max_doc_keys); nbatch = its batches.
+    // witness (or null): row t's entries at witness + t * wit_stride, the
+    // first nwit (at most kWitnessMax) of them scored: output indices of an
+    // earlier selection (positions when expanding, else keys; -1 = none);
+    // an entry names key e / m when expanding and e % m == 0, else key e,
+    // and counts when that key is visible to the row.
     float *samp;
+    const int32_t *witness;
+    int64_t wit_stride;
+    int nwit;
     uint32_t *est;
     uint32_t *fq_cnt;
     uint2 *fq_dir;
@@ -87,6 +96,8 @@ constexpr int kSampleKeys = 8192;     // few-query: keys in a row's estimate sam
 constexpr int kFewCap = 8192;         // few-query: candidates the exact cut holds in LDS
 constexpr int kFewSub = 32;           // few-query: candidate sub-lists per row (batch b: b % 32)
 constexpr int kFewSubCap = 1024;      // few-query: entries per sub-list
+constexpr int kWitnessMax = 8192;     // few-query: witness entries scored per row
+constexpr int kSampStride = kSampleKeys + kWitnessMax;  // floats per row of samp
 
 // dtype codes match enum idx_dtype, plus 3 = e4m3 on the fp8 MFMA (d = 64,
 // 128; not screened); few = few-query mode (blocks over

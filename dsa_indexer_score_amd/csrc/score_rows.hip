@@ -7,7 +7,10 @@
 // modes:
 //  * sample: the exact scores of a fixed sample of the row's keys (64
 //    consecutive keys in each of kSampleKeys / 64 places spread over the
-//    row), from which the row's threshold estimate is cut;
+//    row), from which the row's threshold estimate is cut, and of the row's
+//    witness keys when the caller gives them (keys of an earlier selection,
+//    whose exact scores bound the threshold from below: DoSA summary,
+//    "Method steps", decode);
 //  * filter: every visible key, keeping only the (score, key) pairs at or
 //    above the row's estimate -- appended to the row's candidate list one
 //    run of kFewBatch keys at a time, with the run's directory entry -- so no
@@ -46,6 +49,21 @@ constexpr int kTargetWavesDocs = 2048;
 
 constexpr int kBatchGroups = kFewBatch / kSelGroup;     // groups per candidate run
 constexpr int kSampleGroups = kSampleKeys / kSelGroup;  // groups per row sample
+
+// Witness entries scored per row, and the key that entry i of row t names
+// (-1: none, or not visible to the row, which sees keys 0 .. P-1).
+__device__ __host__ inline int64_t witness_count(const ScoreSelectParams &p)
+{
+    return p.witness ? (p.nwit < kWitnessMax ? p.nwit : kWitnessMax) : 0;
+}
+__device__ inline int64_t witness_key(const ScoreSelectParams &p, int64_t t, int64_t i, int64_t P)
+{
+    if (i >= witness_count(p)) return -1;
+    const int32_t e = p.witness[t * p.wit_stride + i];
+    if (e < 0 || (p.expand && e % p.m)) return -1;
+    const int64_t key = p.expand ? e / p.m : e;
+    return key < P ? key : -1;
+}
 
 template <int DT, int NB, int D, int SQ, bool VARLEN, bool SAMPLE>
 __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectParams p)
@@ -86,9 +104,10 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
         if (Pmax <= kFewCap) return;
         spacing = (Pmax - kSelGroup) / (kSampleGroups - 1);
     }
-    // the slab's 64-key groups, split evenly over the slab's waves in runs
-    // of whole candidate batches
-    const int64_t ngroups = SAMPLE ? kSampleGroups : (Pmax + kSelGroup - 1) / kSelGroup;
+    // the slab's 64-key groups (sample: then the witness groups), split
+    // evenly over the slab's waves in runs of whole candidate batches
+    const int64_t nwg = SAMPLE && !VARLEN ? (witness_count(p) + kSelGroup - 1) / kSelGroup : 0;
+    const int64_t ngroups = SAMPLE ? kSampleGroups + nwg : (Pmax + kSelGroup - 1) / kSelGroup;
     const int64_t nwaves = (int64_t)gridDim.x * kRowsWaves;
     int64_t gpw = (ngroups + nwaves - 1) / nwaves;
     if (!SAMPLE) gpw = (gpw + kBatchGroups - 1) / kBatchGroups * kBatchGroups;
@@ -137,16 +156,20 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
     constexpr int AHEAD = RAW <= 4 ? 2 : 1;
     uint4 raw[AHEAD + 1][2][RAW];
     float ksc[AHEAD + 1] = {};
+    // witness group g (>= kSampleGroups): entries 64 (g - kSampleGroups) + j
+    const int64_t trow = p.row0 + r0;  // the slab's row (one in sample mode)
+    auto key_of = [&](int64_t g, int j) -> int64_t {
+        if (SAMPLE && g >= kSampleGroups) {
+            const int64_t key = witness_key(p, trow, (g - kSampleGroups) * kSelGroup + j, Pq[0]);
+            return key < 0 ? 0 : key;
+        }
+        const int64_t key = klo + g * spacing + j;
+        return key < p.T ? key : p.T - 1;
+    };
     auto load_group = [&](int64_t g, uint4 (&dst)[2][RAW], float &sc) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int64_t key = klo + g * spacing + 32 * c + l32;
-            raw_row<O, D>(kbytes + (key < p.T ? key : p.T - 1) * ROWB, hh, dst[c]);
-        }
-        if (kScaled) {
-            const int64_t key = klo + g * spacing + lane;
-            sc = p.k_scale[key < p.T ? key : p.T - 1];
-        }
+        for (int c = 0; c < 2; ++c) raw_row<O, D>(kbytes + key_of(g, 32 * c + l32) * ROWB, hh, dst[c]);
+        if (kScaled) sc = p.k_scale[key_of(g, lane)];
     };
     // filter: the rows' estimates, and the scores of the current batch
     uint32_t est[SQ];
@@ -195,7 +218,11 @@ __global__ void __launch_bounds__(kRowsThreads) score_rows_kernel(ScoreSelectPar
             float s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
             if (kScaled) s *= ksc[0];
             if constexpr (SAMPLE) {
-                p.samp[(r0 + i) * kSampleKeys + g * kSelGroup + lane] = s;
+                // witness entries that name no visible key rank below every score
+                if (g >= kSampleGroups &&
+                    witness_key(p, trow, (g - kSampleGroups) * kSelGroup + lane, Pq[0]) < 0)
+                    s = -__builtin_inff();
+                p.samp[(r0 + i) * kSampStride + g * kSelGroup + lane] = s;
             } else {
 #pragma unroll
                 for (int x = 0; x < kBatchGroups; ++x)
@@ -241,8 +268,9 @@ hipError_t launch_rows(const ScoreSelectParams &p, hipStream_t stream)
     // the last row sees the most keys (packed documents: at most row_keys)
     const int64_t pmax =
         VARLEN ? p.row_keys : visible_keys(p.q_pos0 + p.row0 + p.nrows - 1, p.T, p.m, p.causal);
+    const int64_t nwg = SAMPLE && !VARLEN ? (witness_count(p) + kSelGroup - 1) / kSelGroup : 0;
     const int64_t ngroups =
-        SAMPLE ? (pmax > kFewCap ? kSampleGroups : 0) : (pmax + kSelGroup - 1) / kSelGroup;
+        SAMPLE ? (pmax > kFewCap ? kSampleGroups + nwg : 0) : (pmax + kSelGroup - 1) / kSelGroup;
     const int64_t nslab = (p.nrows + SQ - 1) / SQ;
     if (ngroups <= 0 || nslab <= 0) return hipSuccess;
     // about kTargetWaves waves in all, at most one per group of a slab

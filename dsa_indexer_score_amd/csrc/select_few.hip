@@ -96,8 +96,10 @@ __device__ void block_boundary(const uint32_t *hist, int nbins, uint32_t need, u
 // feeds its own share): keep codes > tc plus the first need_eq codes equal
 // to tc in key order (exact), or every code >= tc.  1 <= need <= count.
 // LEVELS = 2 stops after the 22-bit prefix: tc is then the lower edge of the
-// prefix bin holding the need-th code (a lower bound, exact = false).
-template <int LEVELS = 3, class Src>
+// prefix bin holding the need-th code (a lower bound, exact = false).  FULL:
+// no early stop where a bin edge already separates the need best codes; tc
+// is then always the need-th code itself.
+template <int LEVELS = 3, bool FULL = false, class Src>
 __device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32_t *red,
                                 uint32_t *res, uint32_t &tc, bool &exact, uint32_t &need_eq)
 {
@@ -110,7 +112,7 @@ __device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32
     int b1;
     uint32_t a1, h1;
     block_boundary(hist, kBins1, need, red, res, b1, a1, h1);
-    if (a1 + h1 == need) {
+    if (!FULL && a1 + h1 == need) {
         tc = (uint32_t)b1 << kShift1;
         return;
     }
@@ -125,7 +127,7 @@ __device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32
     block_boundary(hist, 1024, need - a1, red, res, b2, a2, h2);
     const uint32_t pre = ((uint32_t)b1 << 10) | (uint32_t)b2;  // top 22 bits
     const uint32_t above = a1 + a2;
-    if (LEVELS == 2 || above + h2 == need) {
+    if (LEVELS == 2 || (!FULL && above + h2 == need)) {
         tc = pre << 10;
         return;
     }
@@ -193,8 +195,16 @@ struct RowView {
 // to a 22-bit prefix: the lower edge of the prefix bin holding it), c about
 // 1.5x the sample's expected share of the selection plus a margin, so that
 // the keys at or above it almost always hold the whole selection and fit the
-// candidate list.  Also zeroes the row's candidate count for the filtering
-// launch that follows.
+// candidate list.  With witness keys (DoSA summary, "Method steps": decode
+// takes keys selected at an earlier step as witnesses), the need-th best of
+// their exact scores is a lower bound of the row's need-th best score -- any
+// need visible keys bound it from below -- so the estimate is raised to it
+// when it is higher: the keys at or above it then hold the selection
+// whenever the witnesses name need distinct visible keys.  (Repeated keys
+// can make it too high; the cut then finds fewer candidates than it needs
+// and the row goes to the repair launch, as for any failed estimate.)
+// Also zeroes the row's candidate count for the filtering launch that
+// follows.
 __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectParams p)
 {
     __shared__ uint32_t hist[kBins1];
@@ -207,8 +217,8 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
     if (rv.n > kCap) {
         const uint64_t c = (3ull * rv.need * kSampleKeys) / (2ull * (uint64_t)rv.n) + 8u;
         est = kNoList;
+        const float *sm = p.samp + (int64_t)blockIdx.x * kSampStride;
         if (c <= (uint64_t)kSampleKeys) {
-            const float *sm = p.samp + (int64_t)blockIdx.x * kSampleKeys;
             for (int s = threadIdx.x; s < kSampleKeys; s += kDenseThreads)
                 sample[s] = ord_code(__float_as_uint(sm[s]));
             __syncthreads();
@@ -219,6 +229,30 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
                     for (int i = threadIdx.x; i < kSampleKeys; i += kDenseThreads) f(sample[i]);
                 },
                 (uint32_t)c, hist, red, res, est, est_exact, est_eq);  // low bits 0: never kNoList
+        }
+        const int nw = p.witness && !p.varlen ? (p.nwit < kWitnessMax ? p.nwit : kWitnessMax) : 0;
+        if (nw > 0) {
+            // the witness scores (entries naming no visible key hold -inf)
+            const uint32_t none = ord_code(__float_as_uint(-__builtin_inff()));
+            __syncthreads();
+            uint32_t nvalid = 0;
+            for (int s = threadIdx.x; s < nw; s += kDenseThreads) {
+                const uint32_t u = ord_code(__float_as_uint(sm[kSampleKeys + s]));
+                sample[s] = u;
+                nvalid += u != none ? 1u : 0u;
+            }
+            uint32_t tot;
+            block_excl_scan(nvalid, red, tot);
+            if (tot >= rv.need) {
+                uint32_t tw, tw_eq;
+                bool tw_exact;
+                block_exact_cut<3, true>(  // the need-th witness code itself
+                    [&](auto &&f) {
+                        for (int i = threadIdx.x; i < nw; i += kDenseThreads) f(sample[i]);
+                    },
+                    rv.need, hist, red, res, tw, tw_exact, tw_eq);
+                if (est == kNoList || tw > est) est = tw;
+            }
         }
     }
     if (threadIdx.x == 0) p.est[blockIdx.x] = est;

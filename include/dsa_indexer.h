@@ -94,15 +94,15 @@ typedef struct {
      * with more than two rows per document (indexer_score_topk_varlen: S >
      * 2 ndoc), whose rows share key tiles on the streaming path; negative =
      * never.  Both paths give identical results.  The few-query workspace
-     * holds, each part starting on a 256-byte boundary, the samples' scores
-     * (S * 8192 * 4 bytes), the estimates, candidate counts and repair marks
-     * (S * 4 each), a directory of (offset, count) per 256 keys of a row
-     * (S * ceil(Tk / 256) * 8; Tk = T, or max_doc_keys for packed
-     * documents) and the candidate lists (S * cap * 8, cap = max(8192, the
-     * streaming path's slots per row)) -- about 200 KB per row at 262,144
-     * keys.  It is capped at 4 GiB: when the S rows need more, it is sized
-     * for the R rows that fit and the rows are taken in ceil(S / R) equal
-     * passes. */
+     * holds, each part starting on a 256-byte boundary, the samples' and
+     * witnesses' scores (S * 16384 * 4 bytes), the estimates (S * 4), the
+     * candidate sub-list counts (S * 32 * 4), the repair marks (S * 4), a
+     * directory of (offset, count) per 256 keys of a row (S * ceil(Tk /
+     * 256) * 8; Tk = T, or max_doc_keys for packed documents) and the
+     * candidate lists (S * cap * 8, cap = max(32768, the streaming path's
+     * slots per row)) -- about 330 KB per row at 262,144 keys.  It is
+     * capped at 4 GiB: when the S rows need more, it is sized for the R
+     * rows that fit and the rows are taken in ceil(S / R) equal passes. */
     int64_t few_query_rows;
 } indexer_config;
 
@@ -171,6 +171,40 @@ int indexer_score_topk(indexer_t h, const void *q, const float *q_scale, const f
                        int64_t T, int H, int d, int m, int topk, int causal, int64_t q_pos0,
                        int32_t *idx, int32_t *valid_len, float *sel_score, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * indexer_score_topk with witness keys for the few-query path ("DoSA: Dots
+ * Sparse Attention", summary page, "Method steps": decode scores every key
+ * and takes keys selected at an earlier step as witnesses for a threshold
+ * that cannot exceed the current one).  Same arguments, results and errors
+ * as indexer_score_topk, plus:
+ *   witness         device int32 [S, witness_stride], in: row t's entries
+ *                   start at witness + t * witness_stride; the first
+ *                   min(nwit, 8192) are used.  Each is an output index as
+ *                   this handle writes them (a token position when
+ *                   IDX_EXPAND is set, else a key index), typically the
+ *                   row's idx of the previous decode step; -1 means none.
+ *                   When expanding, an entry names key e / m if e % m == 0
+ *                   (the first position of a pool) and nothing otherwise, so
+ *                   a whole output row names each of its pools once; an
+ *                   entry naming a key the row does not see is ignored.
+ *   witness_stride  >= nwit (IDX_EINVAL otherwise); nwit >= 0, 0 = none.
+ * Rows taken by the few-query path score their witness keys with the
+ * sample; when the witnesses name at least Ksel visible keys, the Ksel-th
+ * best of their exact scores replaces the sampled estimate if it is higher.
+ * Distinct witnesses make it a lower bound of the row's Ksel-th best score,
+ * so no key of the selection is filtered out; repeated ones can make it
+ * too high, which the exact cut detects (the row then goes to the repair
+ * launch).  The result is the exact selection in every case, identical to
+ * indexer_score_topk's; witnesses change only the work.  The streaming path
+ * (rows beyond the few-query limit) ignores them.
+ */
+int indexer_score_topk_witness(indexer_t h, const void *q, const float *q_scale, const float *w,
+                               int64_t w_stride_s, const void *k, const float *k_scale,
+                               int64_t S, int64_t T, int H, int d, int m, int topk, int causal,
+                               int64_t q_pos0, const int32_t *witness, int64_t witness_stride,
+                               int nwit, int32_t *idx, int32_t *valid_len, float *sel_score,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * indexer_score_topk without a workspace, for callers that cannot allocate

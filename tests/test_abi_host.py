@@ -107,7 +107,7 @@ def _capacity(ksel, P):
 
 def _dense_bytes(S, T, ksel=2048):
     """The documented few-query layout for S rows of at most T keys: key
-    samples (8192 fp32 per row), estimates, the counts of 32 candidate
+    sample and witness scores (16384 fp32 per row), estimates, the counts of 32 candidate
     sub-lists, repair marks, the batch directory (8 bytes per 256 keys) and
     the candidate sub-lists (max(32 x 1024, streaming capacity) entries of 8
     bytes), each part 256-byte aligned.  Nothing in it holds a score per
@@ -115,7 +115,7 @@ def _dense_bytes(S, T, ksel=2048):
     up = lambda x, a: -(-x // a) * a
     nb = -(-max(T, 1) // 256)
     cap = max(32 * 1024, _capacity(ksel, T))
-    return up(S * 8192 * 4, 256) + up(S * 4, 256) + up(S * 32 * 4, 256) + up(S * 4, 256) + \
+    return up(S * 16384 * 4, 256) + up(S * 4, 256) + up(S * 32 * 4, 256) + up(S * 4, 256) + \
         up(S * nb * 8, 256) + S * cap * 8
 
 
@@ -134,7 +134,7 @@ def test_workspace_bytes_of_the_few_query_path():
                                        ctypes.byref(n4)) == 0
     assert n4.value - n.value == 64 * 3 * 262144 // 256 * 8   # only the directory grows
     assert lib.indexer_workspace_bytes(h, 1, 1001, 64, 128, 4, 2048, ctypes.byref(n)) == 0
-    assert n.value == _dense_bytes(1, 1001) == 32768 + 4 * 256 + 32768 * 8
+    assert n.value == _dense_bytes(1, 1001) == 65536 + 4 * 256 + 32768 * 8
     assert lib.indexer_workspace_bytes(h, 1025, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == 1025 * 20736 * 8          # above the default: streaming buffers
     assert lib.indexer_workspace_bytes(h, 1024, 262144, 64, 128, 4, 2048, ctypes.byref(n)) == 0
@@ -306,6 +306,31 @@ def test_score_topk_validation_paths():
     assert _call(lib, h, m=4, topk=6) == E               # topk not a multiple of m
     assert _call(lib, h, m=4, topk=8, causal=0) == E      # tail needs causal
     assert _call(lib, h, m=4, topk=8, S=64, T=15) == E    # tail needs every complete pool
+    lib.indexer_destroy(h)
+
+
+def test_score_topk_witness_validation_paths():
+    """indexer_score_topk_witness validates like indexer_score_topk, plus its
+    witness arguments: a negative count, rows that would overlap (stride
+    below the count), a missing or misaligned pointer.  No witnesses (count
+    0) is a plain call."""
+    lib, h = _handle()
+    E = _lib.IDX_EINVAL
+
+    def f(wit=FAKE, stride=8, n=8, **kw):
+        a = dict(q=FAKE, q_scale=None, w=FAKE, w_stride=0, k=FAKE, k_scale=None, S=16, T=16,
+                 H=64, d=128, m=1, topk=4, causal=1, q_pos0=0, idx=FAKE, vl=FAKE, sel=None,
+                 ws=FAKE, ws_bytes=1 << 40, stream=None)
+        a.update(kw)
+        return lib.indexer_score_topk_witness(
+            h, a["q"], a["q_scale"], a["w"], a["w_stride"], a["k"], a["k_scale"], a["S"],
+            a["T"], a["H"], a["d"], a["m"], a["topk"], a["causal"], a["q_pos0"], wit, stride, n,
+            a["idx"], a["vl"], a["sel"], a["ws"], a["ws_bytes"], a["stream"])
+    assert f(S=0) == 0
+    assert f(n=-1) == E and f(stride=7) == E and f(wit=None) == E
+    assert f(wit=ctypes.c_void_p(0x10002)) == E
+    assert f(q=None) == E and f(S=-1) == E                 # the plain call's checks remain
+    assert f(wit=None, stride=0, n=0, S=0) == 0
     lib.indexer_destroy(h)
 
 

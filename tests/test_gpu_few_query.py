@@ -223,10 +223,10 @@ def test_few_query_rows_whose_estimate_fails_are_repaired(kind, S):
     stream = run(inp, few_query_rows=-1)
     _assert_identical(dense, stream)
     # the repair marks, at their documented place in the workspace (after
-    # the samples, estimates and 32 sub-list counts): exactly the
-    # adversarial rows
+    # the sample and witness scores, estimates and 32 sub-list counts):
+    # exactly the adversarial rows
     up = lambda x: -(-x // 256) * 256
-    at = up(S * 8192 * 4) + up(S * 4) + up(S * 32 * 4)
+    at = up(S * 16384 * 4) + up(S * 4) + up(S * 32 * 4)
     status = ws[at:at + 4 * S].view(torch.int32).cpu().tolist()
     assert status == [1 if a else 0 for a in adv], status
     kb = k.bfloat16().float()[:, 0]

@@ -209,7 +209,7 @@ def generate(name: str, *, S: Optional[int] = None, T: Optional[int] = None,
         q_scale = torch.empty((S, H), dtype=torch.float32, device=device)
         if q is None:
             r0 = 0
-            for chunk in _ar1_chunks(S, H, d, AR1_RHO, gq, device, gen_chunk_rows):
+            for chunk in _ar1_chunks(S, H, d, cfg.get("rho", AR1_RHO), gq, device, gen_chunk_rows):
                 n = chunk.shape[0]
                 q8[r0:r0 + n], q_scale[r0:r0 + n] = quant_e4m3_rows(chunk)
                 r0 += n
@@ -220,7 +220,7 @@ def generate(name: str, *, S: Optional[int] = None, T: Optional[int] = None,
         q = q8
     else:
         if q is None:
-            q = torch.cat(list(_ar1_chunks(S, H, d, AR1_RHO, gq, device, gen_chunk_rows)), 0)
+            q = torch.cat(list(_ar1_chunks(S, H, d, cfg.get("rho", AR1_RHO), gq, device, gen_chunk_rows)), 0)
         if dtype == "bf16":
             q = q.to(torch.bfloat16)
         elif dtype != "f32":
