@@ -206,7 +206,9 @@ __global__ void __launch_bounds__(kWideThreads) pair_overlap_wide_kernel(
 // -1) with the three counts.  Same bitmap windows as above, twice per
 // window: row B's bits classify row A's entries, then row A's bits pick row
 // B's unique entries.  Entries are visited in row order (e = 64 i + lane),
-// so ballot-ranked appends keep every region sorted.
+// so ballot-ranked appends keep every region sorted.  Rows of up to 2304
+// entries are held in registers for all windows; longer rows are read
+// again per pass.
 __global__ void __launch_bounds__(kWaves * 64) pair_regions_kernel(
     const int32_t *idx, const int32_t *valid_len, int64_t npairs, int W, int32_t *shared,
     int32_t *left, int32_t *right, int32_t *counts)
@@ -230,7 +232,68 @@ __global__ void __launch_bounds__(kWaves * 64) pair_regions_kernel(
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = x;
         n += __popcll(m);
     };
-    if (va > 0 || vb > 0) {
+    if ((va > 0 || vb > 0) && va <= 64 * kRegPerLane && vb <= 64 * kRegPerLane) {
+        // both rows in registers (entry 64 i + lane in slot i): each row is
+        // read from memory once, however many windows the pair's range needs
+        const int64_t lo = va == 0 ? b[0] : (vb == 0 ? a[0] : (a[0] < b[0] ? a[0] : b[0]));
+        const int64_t hi = va == 0 ? b[vb - 1]
+                                   : (vb == 0 ? a[va - 1]
+                                              : (a[va - 1] > b[vb - 1] ? a[va - 1] : b[vb - 1]));
+        int32_t ra[kRegPerLane], rb[kRegPerLane];
+#pragma unroll
+        for (int i = 0; i < kRegPerLane; ++i) {
+            const int e = i * 64 + lane;
+            ra[i] = e < va ? a[e] : 0;
+            rb[i] = e < vb ? b[e] : 0;
+        }
+        clear_words(bm, kWindow, lane);
+        wave_sync_lds();
+        for (int64_t w0 = lo; w0 <= hi; w0 += kWindow) {
+            const int64_t nbits = hi - w0 + 1 < kWindow ? hi - w0 + 1 : kWindow;
+            // entries and w0 lie in [0, 2^31): 32-bit offsets, and an entry
+            // below the window wraps to >= 2^31
+            const int32_t w0i = (int32_t)w0;
+            // row B's bits; row A's entries -> shared or left-only
+#pragma unroll
+            for (int i = 0; i < kRegPerLane; ++i) {
+                const uint32_t r = (uint32_t)(rb[i] - w0i);
+                if (i * 64 + lane < vb && r < (uint32_t)kWindow) atomicOr(&bm[r >> 5], 1u << (r & 31));
+            }
+            wave_sync_lds();
+#pragma unroll
+            for (int i = 0; i < kRegPerLane; ++i) {
+                if (i * 64 >= va) break;  // wave-uniform
+                const uint32_t r = (uint32_t)(ra[i] - w0i);
+                const bool in = i * 64 + lane < va && r < (uint32_t)kWindow;
+                if (!__ballot(in)) continue;  // no entry of this slot in the window
+                const bool hit = in && ((bm[r >> 5] >> (r & 31)) & 1u);
+                put(osh, nsh, hit, ra[i]);
+                put(ol, nl, in && !hit, ra[i]);
+            }
+            wave_sync_lds();
+            clear_words(bm, nbits, lane);
+            wave_sync_lds();
+            // row A's bits; row B's entries -> right-only
+#pragma unroll
+            for (int i = 0; i < kRegPerLane; ++i) {
+                const uint32_t r = (uint32_t)(ra[i] - w0i);
+                if (i * 64 + lane < va && r < (uint32_t)kWindow) atomicOr(&bm[r >> 5], 1u << (r & 31));
+            }
+            wave_sync_lds();
+#pragma unroll
+            for (int i = 0; i < kRegPerLane; ++i) {
+                if (i * 64 >= vb) break;  // wave-uniform
+                const uint32_t r = (uint32_t)(rb[i] - w0i);
+                const bool in = i * 64 + lane < vb && r < (uint32_t)kWindow;
+                if (!__ballot(in)) continue;
+                const bool hit = in && ((bm[r >> 5] >> (r & 31)) & 1u);
+                put(orr, nr, in && !hit, rb[i]);
+            }
+            wave_sync_lds();
+            clear_words(bm, nbits, lane);
+            wave_sync_lds();
+        }
+    } else if (va > 0 || vb > 0) {
         const int64_t lo = va == 0 ? b[0] : (vb == 0 ? a[0] : (a[0] < b[0] ? a[0] : b[0]));
         const int64_t hi = va == 0 ? b[vb - 1]
                                    : (vb == 0 ? a[va - 1]

@@ -374,6 +374,32 @@ def test_pair_overlap_wide_ranges_and_ragged_rows(W):
     assert np.array_equal(shared4.cpu().numpy(), np.tile(want[:150], 4))
 
 
+@pytest.mark.parametrize("W", [2051, 2304, 2305])
+def test_pair_regions_skewed_pairs(W):
+    """Pairs that load one lane of the merge kernel with most of the other
+    row (a dense block of B inside one chunk of a sparse A), equal rows,
+    disjoint rows, one empty row, and rows exactly as wide as the merge
+    kernel takes (2304) and one wider (the windowed kernel): exact against
+    the oracle."""
+    import dsa_indexer_score_amd as dsai
+    n = min(W, 2200)
+    A = np.arange(n, dtype=np.int64) * 1000                     # sparse, ascending
+    B = 333_333 + np.arange(n, dtype=np.int64)                 # dense block inside one chunk
+    B = np.unique(np.concatenate([B[: n - 3], A[[5, 900, n - 1]]]))[:n]
+    pairs = [(A, B), (A, A), (A, A + 1), (A, np.zeros(0, np.int64)),
+             (np.zeros(0, np.int64), B), (np.arange(W), np.arange(1, W + 1))]
+    idx = np.full((2 * len(pairs), W), -1, np.int32)
+    vl = np.zeros(2 * len(pairs), np.int32)
+    for p_, (x, y) in enumerate(pairs):
+        x, y = x[:W], y[:W]
+        idx[2 * p_, :x.size], vl[2 * p_] = x, x.size
+        idx[2 * p_ + 1, :y.size], vl[2 * p_ + 1] = y, y.size
+    got = dsai.pair_regions(torch.from_numpy(idx).to(DEV), torch.from_numpy(vl).to(DEV))
+    want = orc.pair_regions(idx, vl)
+    for g, w_ in zip(got, want):
+        assert np.array_equal(g.cpu().numpy(), w_)
+
+
 @pytest.mark.parametrize("W", [2051, 5000])
 def test_pair_regions_match_oracle(W):
     """The three-region q-cluster split (shared / left-only / right-only with
