@@ -376,11 +376,11 @@ def test_pair_overlap_wide_ranges_and_ragged_rows(W):
 
 @pytest.mark.parametrize("W", [2051, 2304, 2305])
 def test_pair_regions_skewed_pairs(W):
-    """Pairs that load one lane of the merge kernel with most of the other
-    row (a dense block of B inside one chunk of a sparse A), equal rows,
-    disjoint rows, one empty row, and rows exactly as wide as the merge
-    kernel takes (2304) and one wider (the windowed kernel): exact against
-    the oracle."""
+    """Skewed pairs -- a dense block of row B inside a short stretch of a
+    sparse row A spanning 2.2M positions (34 bitmap windows, most holding
+    entries of one row only), equal rows, rows shifted by one, an empty
+    row -- at widths on both sides of the register path's limit (2304
+    entries per row): exact against the oracle."""
     import dsa_indexer_score_amd as dsai
     n = min(W, 2200)
     A = np.arange(n, dtype=np.int64) * 1000                     # sparse, ascending
