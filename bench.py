@@ -464,6 +464,12 @@ def main():
         or args.topk or args.chunk or args.wdist or args.fp8_mfma or args.graph))
     traffic = stored_traffic() if default_run else None
 
+    screen_stats = None
+    if args.screen and not docs and not args.decode:
+        # the last call's counts, at the start of its workspace
+        tested, passed = ws[:16].view(torch.int64).cpu().tolist()
+        screen_stats = {"keys_tested": tested, "keys_passed": passed,
+                        "survival": passed / tested if tested else None}
     st = dsai.overlap_summary(shared, vl)
     regions = None
     if args.regions:
@@ -559,6 +565,7 @@ def main():
         "roofline": roofline,
         "overlap": {k: st[k] for k in ("mean_overlap", "median_overlap", "mean_jaccard")},
         **({"pair_regions": regions} if regions else {}),
+        **({"screen_stats": screen_stats} if screen_stats else {}),
     }
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle for ~{args.cpu_budget:.0f} s")

@@ -145,16 +145,19 @@ bool use_screen(const indexer_config &cfg, int H)
 }
 
 // Streaming workspace: the candidate buffers [rows, cap] of (score bits,
-// key), then with screening the certificates of one launch's rows (head
-// order [rows, 64] i32, weights [rows, 64], bound weights [rows, 32], key
-// norm coefficient [rows], aggregate row [rows, 128]) and the key norms [T],
-// each 256-byte aligned.
+// key); with screening, the call's statistics (two u64: keys tested against
+// the bound, keys that passed) first, then the candidate buffers, the
+// certificates of one launch's rows (head order [rows, 64] i32, weights
+// [rows, 64], bound weights [rows, 32], key norm coefficient [rows],
+// aggregate row [rows, 128]) and the key norms [T], each 256-byte aligned.
 struct StreamLayout {
-    int64_t perm, w, wt, e, agg, knorm, bytes;
+    int64_t cand = 0, perm, w, wt, e, agg, knorm, bytes;
     StreamLayout(int64_t rows, int64_t cap, int64_t T, bool screen)
     {
         bytes = rows * cap * (int64_t)sizeof(uint2);
         if (!screen) return;
+        cand = 256;  // the call's screening statistics come first
+        bytes += cand;
         perm = round_up(bytes, 256);
         w = perm + round_up(rows * 64 * 4, 256);
         wt = w + round_up(rows * 64 * 4, 256);
@@ -472,6 +475,8 @@ int score_topk_impl(indexer_t h, const void *q, const float *q_scale, const floa
         // DoSA screening: key norms once, certificates per launch
         const StreamLayout L(rows, cap, T, true);
         char *base = static_cast<char *>(workspace);
+        p.scr_stats = reinterpret_cast<unsigned long long *>(base);
+        p.ws = reinterpret_cast<uint2 *>(base + L.cand);
         p.cert_perm = reinterpret_cast<int32_t *>(base + L.perm);
         p.cert_w = reinterpret_cast<float *>(base + L.w);
         p.cert_wt = reinterpret_cast<float *>(base + L.wt);

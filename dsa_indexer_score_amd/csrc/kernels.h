@@ -85,6 +85,9 @@ struct ScoreSelectParams {
     float *cert_agg;        // [nrows, d]: the aggregate row a~ (slot kAggSlot of the order)
     int32_t *cert_act;      // [nrows, 64] or null: seed activation counts (inspection)
     float *knorm;
+    // screening statistics of the call (or null): keys tested against the
+    // bound and keys that passed it; zeroed by the key-norm launch
+    unsigned long long *scr_stats;
 };
 
 constexpr int kQueriesPerBlock = 8;   // one query per wave, 8 waves

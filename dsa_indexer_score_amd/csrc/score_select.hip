@@ -438,6 +438,9 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
     // from the staged tile at the survivor's row), and continue the exact
     // sum from their block-0 partial in the same order as an unscreened
     // tile, so a survivor's score does not depend on the screen.
+    // screening statistics of this wave's row: keys tested against the
+    // bound, keys that passed it
+    uint32_t scr_tested = 0, scr_passed = 0;
     auto screen_tile = [&](int cur, int64_t j0) __attribute__((always_inline)) {
         constexpr int EPK = (16 + KS - 1) / KS;
         float part[NCB], ub[NCB];
@@ -503,8 +506,11 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
             float U = __uint_as_float(sw[0]) + __uint_as_float(sw[1]) + emu * knorm_tile[cur][kl];
             if (kScaled) U *= kscale_tile[cur][kl];
             const int64_t key = j0 + kl;
-            const bool surv = (full || (key >= klo && key < khi)) && U >= tau_f;
+            const bool vis = full || (key >= klo && key < khi);
+            const bool surv = vis && U >= tau_f;
             const uint64_t m = __ballot(surv);
+            scr_tested += __popcll(__ballot(vis));
+            scr_passed += __popcll(m);
             if (surv) sl[ns + lane_rank(m)] = (uint16_t)kl;
             ns += __popcll(m);
         }
@@ -675,6 +681,10 @@ __global__ void __launch_bounds__(kThreads, 1) score_select_kernel(ScoreSelectPa
         __syncthreads();
     }
     if (pend_j0 >= 0) select_tile(pend, pend_j0);
+    if (SCREEN && p.scr_stats && lane == 0 && scr_tested) {
+        atomicAdd(p.scr_stats, (unsigned long long)scr_tested);
+        atomicAdd(p.scr_stats + 1, (unsigned long long)scr_passed);
+    }
 
     if (!active || FEW) return;
 

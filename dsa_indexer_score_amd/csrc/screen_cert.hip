@@ -297,7 +297,8 @@ __global__ void __launch_bounds__(64) certificate_kernel(ScoreSelectParams p)
     if (lane == 0) p.cert_e[r] = (Euse + delta + mu) * (1.f + 0x1p-20f);
 }
 
-// ||k_j|| of the raw key codes (fp32), one thread per key.
+// ||k_j|| of the raw key codes (fp32), one thread per key; the first
+// launch of a screened call, so it also zeroes the call's statistics.
 template <int DT, int D>
 __global__ void __launch_bounds__(256) key_norms_kernel(ScoreSelectParams p)
 {
@@ -306,6 +307,7 @@ __global__ void __launch_bounds__(256) key_norms_kernel(ScoreSelectParams p)
     constexpr int KS = O::KS, ES = O::ES;
     constexpr int EPA = sizeof(A) / sizeof(float) == 4 ? 8 : 1;
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p.scr_stats && j < 2) p.scr_stats[j] = 0;  // the call's screening statistics
     if (j >= p.T) return;
     const char *row = static_cast<const char *>(p.k) + j * (int64_t)D * ES;
     float s = 0.f;

@@ -366,8 +366,11 @@ int indexer_overlap_summary(const int32_t *shared, const int32_t *valid_len, int
  * further, the others get the remaining heads.  Lossless: the selection
  * equals the unscreened one up to the order in which the head terms are
  * summed (the kept heads come first).  The workspace grows by 1156 bytes
- * per row of a launch plus 4 per key (indexer_workspace_bytes accounts for
- * it).
+ * per row of a launch, 4 per key and 256 (indexer_workspace_bytes accounts
+ * for it).  After a screened call (ordered on its stream) the workspace's
+ * first 16 bytes hold two uint64 counts for the call: keys tested against
+ * a bound, and keys whose bound reached the row's running threshold (and
+ * got the remaining heads); the rest of the workspace stays undefined.
  *
  * indexer_screen_certificates writes the certificates of S rows as the
  * screened path uses them, for inspection:

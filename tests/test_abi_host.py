@@ -216,14 +216,15 @@ def test_workspace_bytes_varlen_follow_the_path():
 
 def test_workspace_bytes_with_screening():
     """IDX_SCREEN adds, on the streaming path with 33 <= H <= 64, the
-    certificates of one launch's rows (1156 bytes a row in five 256-byte
-    aligned parts) and 4 bytes per key; H <= 32 cannot screen."""
+    call's statistics (256 bytes, first), the certificates of one launch's
+    rows (1156 bytes a row in five 256-byte aligned parts) and 4 bytes per
+    key; H <= 32 cannot screen."""
     up = lambda x, a: -(-x // a) * a
     n = ctypes.c_size_t()
     lib, h = _handle(flags=_lib.IDX_EXPAND | _lib.IDX_TAIL | _lib.IDX_SCREEN, few=-1)
     S, T, cap = 100, 5000, up(5000, 64) + 64          # cap: every visible key fits
     base = S * cap * 8
-    want = (up(base, 256) + 2 * up(S * 256, 256) + up(S * 128, 256) + up(S * 4, 256)
+    want = (up(256 + base, 256) + 2 * up(S * 256, 256) + up(S * 128, 256) + up(S * 4, 256)
             + up(S * 512, 256) + T * 4)
     assert lib.indexer_workspace_bytes(h, S, T, 64, 128, 4, 2048, ctypes.byref(n)) == 0
     assert n.value == want

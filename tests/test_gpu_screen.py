@@ -300,3 +300,36 @@ def test_screened_full_size_sampled_rows():
     rep = check.compare(inp, rows, hi, hv, hs)
     log(f"  rows {rep['rows']}, index-mismatch rows {rep['index_mismatch_rows']}")
     assert rep["ok"], rep["failures"][:3]
+
+
+@pytest.mark.parametrize("name,S,heads", [("c4_csa_256k", 2500, None), ("c4_csa_256k", 2500, 48)])
+def test_screening_statistics(name, S, heads):
+    """The call's statistics in the workspace's first 16 bytes: every
+    visible key of every row is tested once, and every key of the final
+    selection (at least the first Ksel of each row) passes."""
+    import dsa_indexer_score_amd as dsai
+    over = {} if heads is None else {"H": heads}
+    inp = gen.generate(name, S=S, topk=512, **over).to(DEV)
+    ix = dsai.Indexer(inp.q.dtype, expand=inp.expand, tail=inp.tail, query_chunk=1024,
+                      few_query_rows=-1, screen=True, device=DEV)
+    ws = torch.empty(ix.workspace_bytes(inp.S, inp.T, inp.H, inp.d, inp.m, inp.topk),
+                     dtype=torch.uint8, device=DEV)
+    kw = dict(m=inp.m, topk=inp.topk, causal=inp.causal, q_scale=inp.q_scale,
+              k_scale=inp.k_scale, q_pos0=inp.q_pos0, with_scores=True, workspace=ws)
+    out = ix.score_topk(inp.q, inp.w, inp.k, **kw)
+    torch.cuda.synchronize()
+    tested, passed = ws[:16].view(torch.int64).cpu().tolist()
+    pos = np.arange(inp.S) + inp.q_pos0
+    P = np.minimum((pos + 1) // inp.m, inp.T)
+    ksel = inp.topk // inp.m if inp.expand else inp.topk
+    assert tested == int(P.sum())
+    assert int(np.minimum(P, ksel).sum()) <= passed <= tested
+    log(f"  {name} H={inp.H}: {passed}/{tested} keys passed the bound ({passed / tested:.3f})")
+    # a second call starts from zero
+    ix.score_topk(inp.q, inp.w, inp.k, **kw)
+    torch.cuda.synchronize()
+    assert ws[:16].view(torch.int64).cpu().tolist() == [tested, passed]
+    rows = np.arange(0, S, 11)
+    rep = check.compare(inp, rows, out[0].cpu().numpy()[rows], out[1].cpu().numpy()[rows],
+                        out[2].cpu().numpy()[rows])
+    assert rep["ok"], rep["failures"][:3]
