@@ -286,12 +286,13 @@ def test_screened_chunked_launches_and_modes():
         assert rep["ok"], (causal, rep["failures"][:3])
 
 
-def test_screened_full_size_sampled_rows():
-    """The 256K workload at full size in its benchmark launch configuration
-    (16 query chunks), screened: sampled rows against the oracle's rule,
-    every row against the device invariants."""
+@pytest.mark.parametrize("name", ["c4_csa_256k", "c3_dsa_token"])
+def test_screened_full_size_sampled_rows(name):
+    """The 256K-query (bf16) and 128K-token (fp8) workloads at full size in
+    their benchmark launch configurations, screened: sampled rows against
+    the oracle's rule, every row against the device invariants."""
     from gpu_util import device_invariants, rows_to_host
-    inp = gen.generate("c4_csa_256k", device=DEV)
+    inp = gen.generate(name, device=DEV)
     idx, vl, sc = run(inp, screen=True)
     device_invariants(inp, idx, vl)
     rows = check.sample_rows(inp.S, m=inp.m, ksel=inp.topk, chunk=inp.query_chunk,
