@@ -39,7 +39,7 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_select_c4_csa_256k_pmc.md")
 # the one-row decode step of the 1M-token workload (few-query path)
 DECODE_SRCS = [os.path.join(ROOT, "dsa_indexer_score_amd", "csrc", f) for f in
                ("score_rows.hip", "select_few.hip", "score_select.hip", "mfma_ops.h",
-                "select_common.h", "kernels.h")]
+                "select_common.h", "block_cut.h", "kernels.h")]
 DECODE_PMC_SUMMARY = os.path.join(ROOT, "profiles", "few_query_decode_c5_csa_1m_pmc.md")
 
 

@@ -30,6 +30,7 @@
 //  3. ordered output: a block-wide prefix count of entries above c and of
 //     entries equal to c (packed into one 32-bit scan) gives each kept key
 //     its output slot, so ties go to the lowest keys.
+#include "block_cut.h"
 #include "kernels.h"
 #include "select_common.h"
 
@@ -38,112 +39,6 @@ namespace {
 
 constexpr int kDenseThreads = 1024;
 constexpr int kDenseWaves = kDenseThreads / 64;
-
-// Exclusive prefix sum over the block's NW waves of threads (thread order)
-// and its total.
-template <int NW = kDenseWaves>
-__device__ uint32_t block_excl_scan(uint32_t x, uint32_t *red, uint32_t &total)
-{
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint32_t incl = wave_incl_scan(x);
-    if (lane == 63) red[wave] = incl;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        const uint32_t v = red[i];
-        off += i < wave ? v : 0u;
-        tot += v;
-    }
-    __syncthreads();
-    total = tot;
-    return off + incl - x;
-}
-
-// Bin b of hist[0, nbins) with (count above b) < need <= (count above b) +
-// hist[b], for 1 <= need <= total.  Thread i owns nbins/1024 consecutive bins
-// counted down from the top, so a prefix over threads is a suffix over bins.
-__device__ void block_boundary(const uint32_t *hist, int nbins, uint32_t need, uint32_t *red,
-                               uint32_t *res, int &b, uint32_t &above, uint32_t &hb)
-{
-    const int per = nbins / kDenseThreads;
-    const int top = nbins - 1 - (int)threadIdx.x * per;
-    uint32_t s = 0;
-    for (int i = 0; i < per; ++i) s += hist[top - i];
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan(s, red, tot);
-    if (ex < need && ex + s >= need) {  // exactly one thread
-        uint32_t acc = ex;
-        for (int i = 0; i < per; ++i) {
-            const uint32_t h = hist[top - i];
-            if (acc + h >= need) {
-                res[0] = (uint32_t)(top - i);
-                res[1] = acc;
-                res[2] = h;
-                break;
-            }
-            acc += h;
-        }
-    }
-    __syncthreads();
-    b = (int)res[0];
-    above = res[1];
-    hb = res[2];
-    __syncthreads();
-}
-
-// Exact cut keeping `need` of the codes that src(f) feeds to f (each thread
-// feeds its own share): keep codes > tc plus the first need_eq codes equal
-// to tc in key order (exact), or every code >= tc.  1 <= need <= count.
-// LEVELS = 2 stops after the 22-bit prefix: tc is then the lower edge of the
-// prefix bin holding the need-th code (a lower bound, exact = false).  FULL:
-// no early stop where a bin edge already separates the need best codes; tc
-// is then always the need-th code itself.
-template <int LEVELS = 3, bool FULL = false, class Src>
-__device__ void block_exact_cut(Src &&src, uint32_t need, uint32_t *hist, uint32_t *red,
-                                uint32_t *res, uint32_t &tc, bool &exact, uint32_t &need_eq)
-{
-    exact = false;
-    need_eq = 0;
-    for (int i = threadIdx.x; i < kBins1; i += kDenseThreads) hist[i] = 0;
-    __syncthreads();
-    src([&](uint32_t u) { atomicAdd(&hist[u >> kShift1], 1u); });
-    __syncthreads();
-    int b1;
-    uint32_t a1, h1;
-    block_boundary(hist, kBins1, need, red, res, b1, a1, h1);
-    if (!FULL && a1 + h1 == need) {
-        tc = (uint32_t)b1 << kShift1;
-        return;
-    }
-    for (int i = threadIdx.x; i < 1024; i += kDenseThreads) hist[i] = 0;
-    __syncthreads();
-    src([&](uint32_t u) {
-        if ((u >> kShift1) == (uint32_t)b1) atomicAdd(&hist[(u >> 10) & 1023u], 1u);
-    });
-    __syncthreads();
-    int b2;
-    uint32_t a2, h2;
-    block_boundary(hist, 1024, need - a1, red, res, b2, a2, h2);
-    const uint32_t pre = ((uint32_t)b1 << 10) | (uint32_t)b2;  // top 22 bits
-    const uint32_t above = a1 + a2;
-    if (LEVELS == 2 || (!FULL && above + h2 == need)) {
-        tc = pre << 10;
-        return;
-    }
-    for (int i = threadIdx.x; i < 1024; i += kDenseThreads) hist[i] = 0;
-    __syncthreads();
-    src([&](uint32_t u) {
-        if ((u >> 10) == pre) atomicAdd(&hist[u & 1023u], 1u);
-    });
-    __syncthreads();
-    int b3;
-    uint32_t a3, h3;
-    block_boundary(hist, 1024, need - above, red, res, b3, a3, h3);
-    tc = (pre << 10) | (uint32_t)b3;
-    exact = true;
-    need_eq = need - above - a3;
-}
 
 // Output slots of one thread's consecutive entries under a cut: counts of
 // entries above / equal to the cut before this thread (block-wide, plus the
@@ -159,8 +54,6 @@ struct CutCounter {
 
 constexpr int kCap = kFewCap;         // candidate list (LDS)
 constexpr int kSampleBlock = 64;      // consecutive keys per sample place
-constexpr uint32_t kAllKeys = 0u;     // estimate: every key is a candidate
-constexpr uint32_t kNoList = 0xFFFFFFFFu;  // estimate: leave the row to the repair launch
 static_assert(kSampleKeys % kSampleBlock == 0 && kCap % kDenseThreads == 0, "layout");
 
 // One few-query row: its visible keys are local keys 0 .. n-1 (key klo + j
@@ -190,21 +83,17 @@ struct RowView {
     }
 };
 
-// Threshold estimate of each row: the c-th best code of its sample
-// (kSampleKeys exact scores from 128 places of 64 keys spread over the row;
-// to a 22-bit prefix: the lower edge of the prefix bin holding it), c about
-// 1.5x the sample's expected share of the selection plus a margin, so that
-// the keys at or above it almost always hold the whole selection and fit the
-// candidate list.  With witness keys (DoSA summary, "Method steps": decode
-// takes keys selected at an earlier step as witnesses), the need-th best of
-// their exact scores is a lower bound of the row's need-th best score -- any
-// need visible keys bound it from below -- so the estimate is raised to it
-// when it is higher: the keys at or above it then hold the selection
-// whenever the witnesses name need distinct visible keys.  (Repeated keys
-// can make it too high; the cut then finds fewer candidates than it needs
-// and the row goes to the repair launch, as for any failed estimate.)
-// Also zeroes the row's candidate count for the filtering launch that
-// follows.
+// Threshold estimate of each row (sample_estimate), when the filtering
+// launch does not compute it itself.  With witness keys (DoSA summary,
+// "Method steps": decode takes keys selected at an earlier step as
+// witnesses), the need-th best of their exact scores is a lower bound of
+// the row's need-th best score -- any need visible keys bound it from below
+// -- so the estimate is raised to it when it is higher: the keys at or
+// above it then hold the selection whenever the witnesses name need
+// distinct visible keys.  (Repeated keys can make it too high; the cut then
+// finds fewer candidates than it needs and the row goes to the repair
+// launch, as for any failed estimate.)  Also zeroes the row's candidate
+// counts for the filtering launch that follows.
 __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectParams p)
 {
     __shared__ uint32_t hist[kBins1];
@@ -213,46 +102,39 @@ __global__ void __launch_bounds__(kDenseThreads) estimate_kernel(ScoreSelectPara
     __shared__ uint32_t res[3];
     const RowView rv(p, blockIdx.x);
     if (threadIdx.x < kFewSub) p.fq_cnt[blockIdx.x * kFewSub + threadIdx.x] = 0;
-    uint32_t est = kAllKeys;
+    const float *sm = p.samp + (int64_t)blockIdx.x * kSampStride;
     if (rv.n > kCap) {
-        const uint64_t c = (3ull * rv.need * kSampleKeys) / (2ull * (uint64_t)rv.n) + 8u;
-        est = kNoList;
-        const float *sm = p.samp + (int64_t)blockIdx.x * kSampStride;
-        if (c <= (uint64_t)kSampleKeys) {
-            for (int s = threadIdx.x; s < kSampleKeys; s += kDenseThreads)
-                sample[s] = ord_code(__float_as_uint(sm[s]));
-            __syncthreads();
-            uint32_t est_eq;
-            bool est_exact;
-            block_exact_cut<2>(  // a lower bound of the c-th code is all it needs
-                [&](auto &&f) {
-                    for (int i = threadIdx.x; i < kSampleKeys; i += kDenseThreads) f(sample[i]);
-                },
-                (uint32_t)c, hist, red, res, est, est_exact, est_eq);  // low bits 0: never kNoList
+        for (int s = threadIdx.x; s < kSampleKeys; s += kDenseThreads)
+            sample[s] = ord_code(__float_as_uint(sm[s]));
+        __syncthreads();
+    }
+    uint32_t est = sample_estimate<kDenseThreads>(
+        [&](auto &&f) {
+            for (int i = threadIdx.x; i < kSampleKeys; i += kDenseThreads) f(sample[i]);
+        },
+        rv.n, rv.need, hist, red, res);
+    const int nw = p.witness && !p.varlen ? (p.nwit < kWitnessMax ? p.nwit : kWitnessMax) : 0;
+    if (rv.n > kCap && nw > 0) {
+        // the witness scores (entries naming no visible key hold -inf)
+        const uint32_t none = ord_code(__float_as_uint(-__builtin_inff()));
+        __syncthreads();
+        uint32_t nvalid = 0;
+        for (int s = threadIdx.x; s < nw; s += kDenseThreads) {
+            const uint32_t u = ord_code(__float_as_uint(sm[kSampleKeys + s]));
+            sample[s] = u;
+            nvalid += u != none ? 1u : 0u;
         }
-        const int nw = p.witness && !p.varlen ? (p.nwit < kWitnessMax ? p.nwit : kWitnessMax) : 0;
-        if (nw > 0) {
-            // the witness scores (entries naming no visible key hold -inf)
-            const uint32_t none = ord_code(__float_as_uint(-__builtin_inff()));
-            __syncthreads();
-            uint32_t nvalid = 0;
-            for (int s = threadIdx.x; s < nw; s += kDenseThreads) {
-                const uint32_t u = ord_code(__float_as_uint(sm[kSampleKeys + s]));
-                sample[s] = u;
-                nvalid += u != none ? 1u : 0u;
-            }
-            uint32_t tot;
-            block_excl_scan(nvalid, red, tot);
-            if (tot >= rv.need) {
-                uint32_t tw, tw_eq;
-                bool tw_exact;
-                block_exact_cut<3, true>(  // the need-th witness code itself
-                    [&](auto &&f) {
-                        for (int i = threadIdx.x; i < nw; i += kDenseThreads) f(sample[i]);
-                    },
-                    rv.need, hist, red, res, tw, tw_exact, tw_eq);
-                if (est == kNoList || tw > est) est = tw;
-            }
+        uint32_t tot;
+        block_excl_scan<kDenseThreads>(nvalid, red, tot);
+        if (tot >= rv.need) {
+            uint32_t tw, tw_eq;
+            bool tw_exact;
+            block_exact_cut<kDenseThreads, 3, true>(  // the need-th witness code itself
+                [&](auto &&f) {
+                    for (int i = threadIdx.x; i < nw; i += kDenseThreads) f(sample[i]);
+                },
+                rv.need, hist, red, res, tw, tw_exact, tw_eq);
+            if (est == kNoList || tw > est) est = tw;
         }
     }
     if (threadIdx.x == 0) p.est[blockIdx.x] = est;
@@ -316,7 +198,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
                                      : (sg < nbat ? dir[sg] : make_uint2(0u, 0u));  // (offset, count)
             const uint32_t at = (uint32_t)(sg % kFewSub) * kFewSubCap + de.x;  // run start
             uint32_t tot;
-            const uint32_t off = block_excl_scan(de.y, red, tot);
+            const uint32_t off = block_excl_scan<kDenseThreads>(de.y, red, tot);
             // the list slots of the batch's run name it as their owner, and
             // the batch records the shift from list slot to buffer position
             for (uint32_t i = 0; i < de.y; ++i) owner[done + off + i] = (uint16_t)threadIdx.x;
@@ -350,7 +232,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
     cc.exact = false;
     cc.need_eq = 0;
     if ((uint32_t)ncand > need)
-        block_exact_cut(
+        block_exact_cut<kDenseThreads>(
             [&](auto &&f) {
                 for (int i = threadIdx.x; i < ncand; i += kDenseThreads) f(ord_code(cbits[i]));
             },
@@ -366,7 +248,7 @@ __global__ void __launch_bounds__(kDenseThreads) finish_kernel(ScoreSelectParams
         neq += cc.eq(valid, u) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan(ngt | (neq << 16), red, tot);
+    const uint32_t ex = block_excl_scan<kDenseThreads>(ngt | (neq << 16), red, tot);
     uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
 #pragma unroll
     for (int i = 0; i < kPerC; ++i) {
