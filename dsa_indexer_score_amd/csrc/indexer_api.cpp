@@ -91,7 +91,7 @@ constexpr int64_t kFewRowsDefault = 1024;
 // are at most two rows per document (batched decode).
 constexpr int64_t kFewRowsDocsDefault = 64;
 constexpr int64_t kFewMaxBytes = int64_t(1) << 32;
-constexpr int64_t kFillBlocks = 512;  // two scoring blocks per CU
+constexpr int64_t kFillBlocks = 256;  // one scoring block per CU (measured best)
 constexpr int64_t kRowsKernelMax = 2;  // rows scored with q in registers, keys from HBM
 
 // Few-query workspace for R rows of at most Tk keys each: the rows' key
