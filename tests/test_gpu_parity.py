@@ -85,6 +85,19 @@ def test_full_size_sampled_rows(name):
     assert torch.equal(vl, vl2) and torch.equal(idx, idx2)
 
 
+def test_c2_every_row_at_full_size():
+    """The 32K-token pooled workload (expansion and tail, 2,051-slot rows)
+    at full size: every one of its 32,768 rows against the oracle, not a
+    sample (about 4.3e9 triples of fp64 oracle work)."""
+    inp = gen.generate("c2_glm_pooled", device=DEV)
+    idx, vl, sc = run(inp)
+    rows = np.arange(inp.S)
+    rep = check.compare(inp, rows, idx.cpu().numpy(), vl.cpu().numpy(), sc.cpu().numpy())
+    log(f"  rows {rep['rows']}, index-mismatch rows {rep['index_mismatch_rows']}, "
+        f"max score rel err {rep['max_score_rel_err']:.2e}")
+    assert rep["ok"], rep["failures"][:3]
+
+
 def test_full_size_query_chunk_sweep_is_bit_identical():
     """The StreamIndex abstract's chunk sweep at the 256K-query workload's
     full size: query chunks of 4K, 8K, 16K (the benchmark's) and 32K rows
