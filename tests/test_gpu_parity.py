@@ -70,7 +70,7 @@ def test_full_size_sampled_rows(name):
     idx, vl, sc = run(inp)
     device_invariants(inp, idx, vl)
     ksel = inp.topk // inp.m if inp.expand else inp.topk
-    n_uniform = 96 if inp.S >= 1 << 20 else 160
+    n_uniform = 320 if inp.S >= 1 << 20 else 640
     rows = check.sample_rows(inp.S, m=inp.m, ksel=ksel, chunk=inp.query_chunk, seed=inp.seed,
                              n_uniform=n_uniform)
     hi, hv, hs = rows_to_host(rows, idx, vl, sc)
