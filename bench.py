@@ -104,6 +104,41 @@ def stored_traffic(summary=PMC_SUMMARY, srcs=None, key="traffic_bytes_per_launch
     return float(val.group(1))
 
 
+def gemm_context(dev, n=16384, reps=10):
+    """The vendor library's dense bf16 GEMM (torch.matmul, hipBLASLt) on this
+    GPU, as a measured reference for the bf16 dense peak: n x n x n on
+    normally distributed operands (the data the indexer contracts) and on
+    zeros. The matrix units draw more power on random operands, so the
+    clock, and with it the attainable fraction of the nominal peak, depends
+    on the data."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(7)
+    out = {"op": "torch.matmul bf16 (hipBLASLt)", "shape": f"{n}x{n}x{n}"}
+    for name in ("random_normal", "zeros"):
+        if name == "zeros":
+            a = torch.zeros(n, n, dtype=torch.bfloat16, device=dev)
+            b = torch.zeros(n, n, dtype=torch.bfloat16, device=dev)
+        else:
+            a = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+            b = torch.randn(n, n, generator=g, device=dev).to(torch.bfloat16)
+        c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / ms / 1e9
+        out[f"{name}_tflops"] = tf
+        out[f"{name}_frac_of_bf16_peak"] = tf / PEAK_TFLOPS["bf16"]
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, budget_s, seed, docs=None):
     """The oracle on seeded uniform rows of the same workload, for about
     budget_s seconds of host time; a rate, so no extrapolation is needed.
@@ -237,6 +272,8 @@ def main():
     ap.add_argument("--workload", default="c4_csa_256k")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-context", action="store_true",
+                    help="skip timing the vendor bf16 GEMM beside the prefill kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
     ap.add_argument("--varlen", type=int, default=0, metavar="N",
@@ -567,6 +604,10 @@ def main():
         **({"pair_regions": regions} if regions else {}),
         **({"screen_stats": screen_stats} if screen_stats else {}),
     }
+    if not (args.no_gemm_context or args.decode or args.decode_batch or args.host_streamed):
+        result["gemm_context"] = gemm_context(dev)
+        log(f"bench: vendor bf16 GEMM {result['gemm_context']['random_normal_tflops']:.0f} "
+            f"TFLOP/s on normal operands, {result['gemm_context']['zeros_tflops']:.0f} on zeros")
     if not args.no_cpu_baseline:
         log(f"bench: timing the CPU oracle for ~{args.cpu_budget:.0f} s")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, inp.seed, docs)
