@@ -242,6 +242,32 @@ def test_topk_larger_than_visible_and_topk_one():
         device_invariants(inp, out[0], out[1])
 
 
+@pytest.mark.parametrize("causal,q_pos0", [(True, 15988), (False, 0)])
+def test_largest_supported_topk_on_both_paths(causal, q_pos0):
+    """topk = 16,000, the largest Ksel the library takes (its 16-bit
+    histogram counters bound a candidate buffer below 65,536 entries):
+    causal rows that see from 15,989 to 16,012 keys (fewer than, exactly and
+    more than Ksel), and non-causal rows that see all 40,000 keys.  Every row
+    against the oracle, on the streaming path and on the few-query path --
+    whose cut list holds 8,192 candidates, so these rows reach the result
+    through its repair launch -- and the two paths bit for bit."""
+    g = torch.Generator().manual_seed(16000)
+    S, H, d, T = 24, 8, 64, 40000
+    q = (torch.randn(S, H, d, generator=g) / d ** 0.5).bfloat16()
+    k = (torch.randn(T, d, generator=g) / d ** 0.5).bfloat16()
+    w = torch.randn(H, generator=g)
+    inp = gen.custom(q=q, k=k, w=w, topk=16000, causal=causal, q_pos0=q_pos0).to(DEV)
+    stream = run(inp)
+    few = run(inp, few_query_rows=64)
+    for x, y in zip(stream, few):
+        assert torch.equal(x, y)
+    _compare_all(inp, stream)
+    device_invariants(inp, stream[0], stream[1])
+    vl = stream[1].cpu()
+    want = torch.clamp(torch.arange(S) + q_pos0 + 1, max=16000) if causal else torch.full((S,), 16000)
+    assert torch.equal(vl, want.int())
+
+
 @pytest.mark.parametrize("expand,tail,causal,q_pos0,T", [
     (False, False, True, 0, None),       # first 2048 pools' rows taken whole
     (True, True, True, 6001, None),      # blocks straddle the Ksel edge
