@@ -34,3 +34,32 @@ def test_scored_pairs_at_the_csa_prefill_shape():
     sc = bench.scored_pairs(262144, 65536, 4, True, 2048)
     assert vis - sc == sum(min(65536, (t + 1) // 4) for t in range(8195))
     assert 0.998 < sc / vis < 0.9991
+
+
+def test_gemm_context_reports_both_operand_kinds(monkeypatch):
+    """The vendor-GEMM reference figure: n^3 matmuls timed on normal
+    operands and on zeros, each as TFLOP/s (2 n^3 flop per call) and as a
+    fraction of the bf16 dense peak.  Timed here on the CPU with a clock in
+    place of the device events (the arithmetic, not the GPU)."""
+    import time
+    import torch
+
+    class _Event:
+        def __init__(self, enable_timing=True):
+            self.t = 0.0
+
+        def record(self, *args):
+            self.t = time.perf_counter()
+
+        def elapsed_time(self, other):
+            return (other.t - self.t) * 1e3
+
+    monkeypatch.setattr(torch.cuda, "Event", _Event)
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a: None)
+    monkeypatch.setattr(torch.cuda, "empty_cache", lambda *a: None)
+    ctx = bench.gemm_context("cpu", n=128, reps=2)
+    assert ctx["shape"] == "128x128x128"
+    for kind in ("random_normal", "zeros"):
+        tf = ctx[f"{kind}_tflops"]
+        assert tf > 0
+        assert abs(ctx[f"{kind}_frac_of_bf16_peak"] - tf / bench.PEAK_TFLOPS["bf16"]) < 1e-12
