@@ -168,6 +168,27 @@ def test_repeated_witnesses_are_caught_and_repaired(name, T):
     assert np.all(est1 > est0) and np.all(stat == 1) and np.all(tot1 < ksel)
 
 
+def test_witness_entries_past_8192_are_not_read():
+    """Only the first 8,192 entries of a row's witnesses are scored: with
+    those all -1 and the row's own selection after them, the estimate stays
+    the sampled one (with the selection within the first 8,192 it would
+    become the exact Ksel-th code)."""
+    inp = _rows(_pair("c5_csa_1m", 2, 262144), 1, 3)
+    ix = _indexer(inp)
+    plain, est0, tot0, _ = _call(ix, inp)
+    sel = plain[0]
+    W = sel.shape[1]
+    late = torch.full((inp.S, 8192 + W), -1, dtype=torch.int32, device=DEV)
+    late[:, 8192:] = sel
+    wout, est1, tot1, _ = _call(ix, inp, witness=late.contiguous())
+    _same(plain, wout)
+    assert np.array_equal(est1, est0) and np.array_equal(tot1, tot0)
+    early = late.clone()
+    early[:, :W] = sel
+    _, est2, _, _ = _call(ix, inp, witness=early.contiguous())
+    assert np.all(est2 > est0)
+
+
 def test_streaming_path_ignores_witnesses():
     """Rows beyond the few-query limit stream; the witnesses change nothing."""
     inp = _rows(_pair("c4_csa_256k", 40, 4096), 1, 41)
